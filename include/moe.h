@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of libmoe: one sparse mixture-of-experts layer with 2-bit (and
+ * 3-bit / bf16) block-quantized experts, for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (pages cited by title and section):
+ *   - route each token to the 10 largest of 512 router logits, plus one always-on
+ *     shared expert ("Strata Runs 125B Qwen3.8-Flash-Next on a 12GB Gaming GPU at
+ *     Up to 94 Tokens/s", section "What it is"; "Strata: a 125B AI model on your
+ *     gaming PC", model spec table, rows "Experts" and "Hidden dimension");
+ *   - run every selected expert's FFN from quantized weights (the Q2_0 2-bit build
+ *     of the first page's section "The numbers, measured by the author") and sum
+ *     the results weighted by the gates;
+ *   - compute only the experts resident in a GPU cache and list the others as
+ *     misses (first page, section "How a 125B model fits in 12 GB");
+ *   - take decode batches of 1 + 3 MTP draft tokens and prompt chunks of up to
+ *     8,192 tokens ("Strata Runs a 125-Billion-Parameter Qwen Model on a 12 GB
+ *     Gaming GPU at up to 93 Tokens per Second", speculative decoding and
+ *     chunked prompt reading).
+ * The pages leave the router function, gate normalisation, FFN type and weight
+ * layout open.  This library's reading: softmax router, top-k by logit with ties
+ * to the lower expert index, gates = softmax renormalised over the k selected,
+ * SwiGLU experts (h = SiLU(W_gate x) * (W_up x), y = W_down h) without biases,
+ * shared expert added with weight 1, fp32 layer output.
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
+ *     owned by the caller; structs (moe_layer_t, moe_bank_t) live in host memory
+ *     and are read during the call only.  bf16 / fp16 values travel as uint16_t
+ *     bit patterns.  Row-major unless stated.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue kernels and
+ *     return without synchronising; they allocate nothing and call no memset, so
+ *     they can be captured into a HIP graph.
+ *   - Errors: arguments are validated on the host before any launch; a failed
+ *     check returns MOE_EINVAL / MOE_EUNSUPPORTED / MOE_EWORKSPACE and enqueues
+ *     nothing.  A launch failure returns MOE_EHIP.  Nothing is thrown.
+ *   - Workspace: ``ws`` is caller-owned device memory of at least
+ *     moe_workspace_bytes() bytes, 256-byte aligned.  Its first
+ *     MOE_WS_CONTROL_BYTES hold counters that must be zero before the first call
+ *     (allocate it zero-filled, or call moe_workspace_clear once); every call
+ *     leaves them zero again.  Calls that share a workspace must not overlap.
+ *   - Results are deterministic: no floating-point atomics; every sum has a
+ *     fixed order, so re-running a call gives bit-identical outputs.
+ *
+ * Weight layouts (this library's own definition; the pages give none).
+ * A matrix W has N rows (outputs) and K columns (inputs), N % 64 == 0 and
+ * K % 128 == 0, cut into tiles of 64 rows x 64 columns numbered
+ * t = (n / 64) * (K / 64) + k / 64.
+ *   MOE_FMT_Q2  code c in 0..3, weight = s * (c - 2), s = fp16 scale of the
+ *               row's 32-column block.  Code byte t*1024 + (n%64)*16 + (k%64)/4,
+ *               bits 2*(k%4)..+1.  Scale index ((n/64)*(K/128) + (k/32)/4)*256
+ *               + (n%64)*4 + (k/32)%4.  1,536,000 bytes per 2560x640 expert.
+ *   MOE_FMT_Q3  c = lo + 4*hi in 0..7, weight = s * (c - 4).  ``lo`` has the Q2
+ *               code layout; ``hi`` holds 8 bytes per (tile, row) at byte
+ *               t*512 + (n%64)*8: writing k%64 = 16*w + j (w 0..3, j 0..15), the
+ *               bit is number 32*(w/2) + 8*(w%2) + (j%8) + 16*(j/8) of that
+ *               little-endian 64-bit word.  Scales as Q2.
+ *   MOE_FMT_BF16 element (n, k) at ((n/64)*(K/8) + k/8)*512 + (n%64)*8 + k%8.
+ * Each expert has W13 = [2I x H] (rows 0..I-1 gate, I..2I-1 up) and
+ * W2 = [H x I] (down); a bank stores its experts back to back, expert-major.
+ * The router weight is plain row-major bf16 [E x H].
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* null pointer, non-positive size, k > E, bad shape */
+  MOE_EUNSUPPORTED = -2,  /* format or shape this build has no kernel for */
+  MOE_EWORKSPACE = -3,    /* workspace missing, misaligned or too small */
+  MOE_EHIP = -4           /* a HIP launch reported an error */
+};
+
+enum { MOE_FMT_NONE = -1, MOE_FMT_BF16 = 0, MOE_FMT_Q2 = 1, MOE_FMT_Q3 = 2 };
+
+/* Bytes at the start of every workspace reserved for zero-initialised counters. */
+#define MOE_WS_CONTROL_BYTES 65536
+
+/* A bank of n_experts experts in one format (device pointers, caller-owned). */
+typedef struct moe_bank {
+  int32_t fmt;                /* MOE_FMT_*; MOE_FMT_NONE = no bank */
+  int32_t n_experts;
+  int32_t hidden;             /* H */
+  int32_t inter;              /* I */
+  const void* w13;            /* Q2 codes / Q3 lo plane / bf16 values, n_experts * [2I x H] */
+  const void* w13_hi;         /* Q3 hi plane, else NULL */
+  const uint16_t* w13_scale;  /* fp16 block scales (Q2/Q3), else NULL */
+  const void* w2;             /* same for the down projection, n_experts * [H x I] */
+  const void* w2_hi;
+  const uint16_t* w2_scale;
+} moe_bank_t;
+
+/* One MoE layer. */
+typedef struct moe_layer {
+  int32_t hidden;             /* H, multiple of 128 */
+  int32_t n_experts;          /* E routed experts, <= 1023 */
+  int32_t top_k;              /* k, 1 <= k <= min(E, 32) */
+  int32_t inter;              /* I, multiple of 128 */
+  const uint16_t* w_router;   /* bf16 [E x H] row-major */
+  const float* router_bias;   /* fp32 [E] added to the logits, or NULL */
+  moe_bank_t routed;          /* n_experts == E */
+  moe_bank_t shared;          /* n_experts == 1, or fmt == MOE_FMT_NONE for no shared expert */
+} moe_layer_t;
+
+/* Workspace bytes needed by every call below for a layer of this shape and up
+ * to T tokens (including MOE_WS_CONTROL_BYTES).  Returns 0 for invalid shapes. */
+size_t moe_workspace_bytes(const moe_layer_t* L, int32_t T);
+
+/* Zero the workspace's control region with a kernel (no memset), on ``stream``. */
+int moe_workspace_clear(void* ws, size_t ws_bytes, void* stream);
+
+/* Router: logits l[t,e] = sum_h x[t,h] Wr[e,h] (+ b[e]) in fp32 from bf16
+ * inputs; topk_ids[t, 0..k-1] = the k largest logits in descending order, ties to
+ * the lower expert index; topk_gates[t,i] = exp(l_i - l_0) / sum_j exp(l_j - l_0)
+ * over the selected (= the softmax over all E renormalised over the k);
+ * margin[t] = l_(k) - l_(k+1) (the gap below the last selected logit; +inf if
+ * k == E), so callers can flag near-ties.
+ * x bf16 [T x H]; topk_ids int32 [T x k]; topk_gates fp32 [T x k]; margin fp32 [T] or NULL. */
+int moe_route(const moe_layer_t* L, const uint16_t* x, int32_t T,
+              int32_t* topk_ids, float* topk_gates, float* margin,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Permutation of the routed entries r = t*k + i (and, if with_shared, the shared
+ * entries r = T*k + t, as group E) by expert: a stable counting sort.
+ * offsets int32 [E + 2]: offsets[g] = first sorted position of group g,
+ * offsets[E + 1] = total entries; sorted_rows int32 [n]: the entry at each sorted
+ * position, ascending r inside a group; row_to_sorted int32 [n]: the inverse.
+ * n = T*k (+ T).  Expert ids must lie in [0, E). */
+int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t with_shared,
+                int32_t* offsets, int32_t* sorted_rows, int32_t* row_to_sorted,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs over a permutation: for every sorted position p holding entry r of
+ * group g (token t = r / k for r < T*k, t = r - T*k for the shared group E),
+ * y_sorted[p] = W_down,g ( SiLU(W_gate,g x[t]) * (W_up,g x[t]) ), fp32 [n x H].
+ * The routed bank serves groups 0..E-1, the shared bank group E.  The bank
+ * format picks the kernel (2-bit, 3-bit or bf16); groups with few tokens use
+ * the dequant-GEMV kernels, groups with many tokens the MFMA grouped GEMM. */
+int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T,
+                      const int32_t* offsets, const int32_t* sorted_rows, float* y_sorted,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Gate-weighted combine in a fixed order:
+ * out[t] = sum_{i=0..k-1} g[t,i] y_sorted[row_to_sorted[t*k+i]]
+ *          (+ y_sorted[row_to_sorted[T*k+t]] if with_shared) (+ residual[t]);
+ * out fp32 [T x H]; out_bf16 (optional) = out rounded to bf16, nearest-even. */
+int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* topk_gates,
+                int32_t T, int32_t k, int32_t H, int32_t with_shared, const uint16_t* residual,
+                float* out, uint16_t* out_bf16, void* stream);
+
+/* The whole layer: route, permute, expert FFNs, shared expert, combine, as one call.
+ * out fp32 [T x H] = MoE(x) (+ residual); out_bf16, topk_ids, topk_gates, margin
+ * optional (NULL = not returned). */
+int moe_layer_forward(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
+                      float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates,
+                      float* margin, void* ws, size_t ws_bytes, void* stream);
+
+/* A stack of n_layers layers joined by residual adds (48 layers in the model, first
+ * page, section "What it is"): x_{l+1} = bf16(x_l + MoE_l(x_l)).  x0 bf16 [T x H];
+ * x_out bf16 [T x H] = x_{n_layers}; out_last (optional) fp32 [T x H] = the last
+ * layer's fp32 x + MoE(x).  ``layers`` is a host array of n_layers layer structs. */
+int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_t* x0, int32_t T,
+                      uint16_t* x_out, float* out_last, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert-cache mode (first page, section "How a 125B model fits in 12 GB"; the
+ * aireport.net page: an adaptive GPU cache of the most used experts, the others
+ * computed elsewhere).  slot_of int32 [n_layers x E]: cache slot of expert e of
+ * layer l, or -1; slot_pool: a bank whose expert s is the weights of slot s.
+ * Routing uses L's router; gates are renormalised over all k selected experts.
+ * out fp32 [T x H] = sum over selected experts WITH a slot of g * FFN + shared
+ * expert; miss_rows int32 [T*k] receives the entries r = t*k + i whose expert has
+ * no slot, ascending, and n_miss (device int32) their count. */
+int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers,
+                             const int32_t* slot_of, const moe_bank_t* slot_pool,
+                             const uint16_t* x, int32_t T, float* out,
+                             int32_t* topk_ids, float* topk_gates,
+                             int32_t* miss_rows, int32_t* n_miss,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,174 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function here forwards to the C ABI with device pointers taken from torch
+tensors and the current HIP stream; all computation happens in the library's
+kernels.  There is no fallback: if libmoe.so is missing, ``lib()`` raises.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+FMT_NONE, FMT_BF16, FMT_Q2, FMT_Q3 = -1, 0, 1, 2
+FMT_BY_NAME = {"bf16": FMT_BF16, "q2": FMT_Q2, "q3": FMT_Q3}
+WS_CONTROL_BYTES = 65536
+
+# Every function the header declares, with (restype, argtypes).
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+class Bank(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("w13", _vp), ("w13_hi", _vp), ("w13_scale", _vp),
+        ("w2", _vp), ("w2_hi", _vp), ("w2_scale", _vp),
+    ]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("w_router", _vp), ("router_bias", _vp),
+        ("routed", Bank), ("shared", Bank),
+    ]
+
+
+_SIGS = {
+    "moe_workspace_bytes": (_sz, [ctypes.POINTER(Layer), _i32]),
+    "moe_workspace_clear": (ctypes.c_int, [_vp, _sz, _vp]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(Layer), _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_permute": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_q2": (ctypes.c_int, [ctypes.POINTER(Layer), _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _sz, _vp]),
+    "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_layer_forward_cached": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank), _vp,
+                                                _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_LIB = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_expert_ffn_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def declared_functions():
+    return sorted(_SIGS)
+
+
+def strerror(code):
+    return lib().moe_strerror(int(code)).decode()
+
+
+def _check(fn, rc):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def ptr(t):
+    """Device address of a tensor, or None for None."""
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------- structs
+
+def make_bank(fmt, n_experts, hidden, inter, w13=None, w13_hi=None, w13_scale=None, w2=None, w2_hi=None,
+              w2_scale=None):
+    f = FMT_BY_NAME[fmt] if isinstance(fmt, str) else fmt
+    return Bank(f, n_experts, hidden, inter, ptr(w13), ptr(w13_hi), ptr(w13_scale), ptr(w2), ptr(w2_hi),
+                ptr(w2_scale))
+
+
+def no_bank():
+    return Bank(FMT_NONE, 0, 0, 0, None, None, None, None, None, None)
+
+
+def make_layer(hidden, n_experts, top_k, inter, w_router, router_bias, routed, shared=None):
+    return Layer(hidden, n_experts, top_k, inter, ptr(w_router), ptr(router_bias), routed,
+                 shared if shared is not None else no_bank())
+
+
+# ---------------------------------------------------------------- calls
+
+def workspace_bytes(layer, T):
+    return int(lib().moe_workspace_bytes(ctypes.byref(layer), int(T)))
+
+
+def workspace_clear(ws, stream=None):
+    _check("moe_workspace_clear", lib().moe_workspace_clear(ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def route(layer, x, T, topk_ids, topk_gates, margin, ws, stream=None):
+    _check("moe_route", lib().moe_route(ctypes.byref(layer), ptr(x), int(T), ptr(topk_ids), ptr(topk_gates),
+                                        ptr(margin), ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def permute(topk_ids, T, k, E, with_shared, offsets, sorted_rows, row_to_sorted, ws, stream=None):
+    _check("moe_permute", lib().moe_permute(ptr(topk_ids), int(T), int(k), int(E), int(bool(with_shared)),
+                                            ptr(offsets), ptr(sorted_rows), ptr(row_to_sorted), ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def expert_ffn_q2(layer, x, T, offsets, sorted_rows, y_sorted, ws, stream=None):
+    _check("moe_expert_ffn_q2", lib().moe_expert_ffn_q2(ctypes.byref(layer), ptr(x), int(T), ptr(offsets),
+                                                        ptr(sorted_rows), ptr(y_sorted), ptr(ws),
+                                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def combine(y_sorted, row_to_sorted, topk_gates, T, k, H, with_shared, residual, out, out_bf16=None, stream=None):
+    _check("moe_combine", lib().moe_combine(ptr(y_sorted), ptr(row_to_sorted), ptr(topk_gates), int(T), int(k),
+                                            int(H), int(bool(with_shared)), ptr(residual), ptr(out), ptr(out_bf16),
+                                            _stream(stream)))
+
+
+def layer_forward(layer, x, T, out, ws, residual=None, out_bf16=None, topk_ids=None, topk_gates=None, margin=None,
+                  stream=None):
+    _check("moe_layer_forward", lib().moe_layer_forward(
+        ctypes.byref(layer), ptr(x), int(T), ptr(residual), ptr(out), ptr(out_bf16), ptr(topk_ids),
+        ptr(topk_gates), ptr(margin), ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def stack_forward(layers, x0, T, x_out, ws, out_last=None, stream=None):
+    arr = (Layer * len(layers))(*layers)
+    _check("moe_stack_forward", lib().moe_stack_forward(arr, len(layers), ptr(x0), int(T), ptr(x_out),
+                                                        ptr(out_last), ptr(ws), ws.numel() * ws.element_size(),
+                                                        _stream(stream)))
+
+
+def layer_forward_cached(layer, layer_idx, n_layers, slot_of, slot_pool, x, T, out, topk_ids, topk_gates,
+                         miss_rows, n_miss, ws, stream=None):
+    _check("moe_layer_forward_cached", lib().moe_layer_forward_cached(
+        ctypes.byref(layer), int(layer_idx), int(n_layers), ptr(slot_of), ctypes.byref(slot_pool), ptr(x), int(T),
+        ptr(out), ptr(topk_ids), ptr(topk_gates), ptr(miss_rows), ptr(n_miss), ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,0 +1,334 @@
+// C ABI of libmoe: host-side validation, workspace layout and kernel dispatch.
+// Every argument check runs before the first HIP call, so invalid calls return
+// an error code without touching the device.
+#include <string.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool fmt_ok(int f) { return f == MOE_FMT_BF16 || f == MOE_FMT_Q2 || f == MOE_FMT_Q3; }
+
+int check_bank(const moe_bank_t& b, int n_experts_min, int H, int I) {
+  if (!fmt_ok(b.fmt)) return MOE_EUNSUPPORTED;
+  if (b.n_experts < n_experts_min || b.hidden != H || b.inter != I) return MOE_EINVAL;
+  if (!b.w13 || !b.w2) return MOE_EINVAL;
+  if (b.fmt != MOE_FMT_BF16 && (!b.w13_scale || !b.w2_scale)) return MOE_EINVAL;
+  if (b.fmt == MOE_FMT_Q3 && (!b.w13_hi || !b.w2_hi)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int check_shape(const moe_layer_t* L) {
+  if (!L) return MOE_EINVAL;
+  if (L->hidden <= 0 || L->inter <= 0 || L->hidden % 128 || L->inter % 128) return MOE_EINVAL;
+  if (L->n_experts < 1 || L->n_experts > 1023) return MOE_EINVAL;
+  if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > 32) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int check_layer(const moe_layer_t* L) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (!L->w_router) return MOE_EINVAL;
+  rc = check_bank(L->routed, L->n_experts, L->hidden, L->inter);
+  if (rc) return rc;
+  if (L->routed.n_experts != L->n_experts) return MOE_EINVAL;
+  if (L->shared.fmt != MOE_FMT_NONE) {
+    rc = check_bank(L->shared, 1, L->hidden, L->inter);
+    if (rc) return rc;
+    if (L->shared.fmt != L->routed.fmt) return MOE_EUNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+bool has_shared(const moe_layer_t* L) { return L->shared.fmt != MOE_FMT_NONE; }
+
+// Workspace layout of every call for a layer shape and up to T tokens.
+struct Layout {
+  size_t logits, ids, gates, margin;
+  size_t counts, base, offsets, sorted_rows, row_to_sorted, active, n_active;
+  size_t xtab_pairs, xtab_init, xf32;
+  size_t h, htab_pairs, htab_init, y;
+  size_t out_f32, xa, xb;     // stack ping-pong buffers
+  size_t miss_flag;
+  size_t total;
+};
+
+Layout make_layout(const moe_layer_t* L, int64_t T) {
+  const int64_t E = L->n_experts, k = L->top_k, H = L->hidden, I = L->inter;
+  const int64_t n = T * k + T;   // room for the shared group
+  const int64_t nc = permute_chunks((int)n);
+  const int planes = L->routed.fmt == MOE_FMT_Q3 ? 2 : 1;
+  const bool dense = L->routed.fmt == MOE_FMT_BF16;
+  Layout o;
+  size_t p = MOE_WS_CONTROL_BYTES;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p = align_up(p + bytes);
+    return at;
+  };
+  o.logits = take(T * E * 4);
+  o.ids = take(T * k * 4);
+  o.gates = take(T * k * 4);
+  o.margin = take(T * 4);
+  o.counts = take(nc * (E + 2) * 4);
+  o.base = take(nc * (E + 2) * 4);
+  o.offsets = take((E + 2) * 4);
+  o.sorted_rows = take(n * 4);
+  o.row_to_sorted = take(n * 4);
+  o.active = take((E + 1) * 4);
+  o.n_active = take(4);
+  o.xtab_pairs = take(dense ? 0 : T * (H / 32) * planes * 16 * 4);
+  o.xtab_init = take(dense ? 0 : T * (H / 32) * 4);
+  o.xf32 = take(dense ? T * H * 4 : 0);
+  o.h = take(n * I * 4);
+  o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
+  o.htab_init = take(dense ? 0 : n * (I / 32) * 4);
+  o.y = take(n * H * 4);
+  o.out_f32 = take(T * H * 4);
+  o.xa = take(T * H * 2);
+  o.xb = take(T * H * 2);
+  o.miss_flag = take(T * k * 4);
+  o.total = p;
+  return o;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(void* ws, size_t ws_bytes, const Layout& lay) {
+  if (!ws) return MOE_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
+  if (ws_bytes < lay.total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    hipError_t e_ = (expr);             \
+    if (e_ != hipSuccess) return MOE_EHIP; \
+  } while (0)
+
+// ---- steps shared by the public calls (arguments already validated) ----
+
+int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float* gates, float* margin, void* ws,
+             const Layout& lay, hipStream_t s) {
+  float* logits = at<float>(ws, lay.logits);
+  MOE_TRY(launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s));
+  MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
+  return MOE_OK;
+}
+
+int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef& perm, int n_entries,
+                  float* y_sorted, void* ws, const Layout& lay, hipStream_t s,
+                  const moe_bank_t* routed_override = nullptr) {
+  const moe_bank_t& rb = routed_override ? *routed_override : L->routed;
+  const int H = L->hidden, I = L->inter, E = L->n_experts;
+  const int max_groups = std::min(E + 1, n_entries);
+  const MatRef r13 = mat_w13(rb), r2 = mat_w2(rb);
+  const MatRef s13 = has_shared(L) ? mat_w13(L->shared) : MatRef(), s2 = has_shared(L) ? mat_w2(L->shared) : MatRef();
+  float* h = at<float>(ws, lay.h);
+  if (rb.fmt == MOE_FMT_BF16) {
+    float* xf = at<float>(ws, lay.xf32);
+    MOE_TRY(launch_bf16_rows_to_f32(x, T, H, xf, s));
+    MOE_TRY(launch_gemv_dense(GemvKind::GateUp, r13, s13, 2 * I, H, I, perm, max_groups, xf, h, s));
+    MOE_TRY(launch_gemv_dense(GemvKind::Down, r2, s2, H, I, I, perm, max_groups, h, y_sorted, s));
+    return MOE_OK;
+  }
+  const bool q3 = rb.fmt == MOE_FMT_Q3;
+  TableRef xt;
+  xt.pairs = at<uint32_t>(ws, lay.xtab_pairs);
+  xt.init = at<float>(ws, lay.xtab_init);
+  xt.sets = q3 ? 2 : 1;
+  MOE_TRY(launch_prep_table_bf16(x, T, H, q3, const_cast<uint32_t*>(xt.pairs), const_cast<float*>(xt.init), s));
+  MOE_TRY(launch_gemv_quant(GemvKind::GateUp, rb.fmt, r13, s13, 2 * I, H, I, perm, max_groups, xt, h, s));
+  TableRef ht;
+  ht.pairs = at<uint32_t>(ws, lay.htab_pairs);
+  ht.init = at<float>(ws, lay.htab_init);
+  ht.sets = (q3 ? 2 : 1) * 2;
+  MOE_TRY(launch_prep_table_f32(h, n_entries, I, q3, const_cast<uint32_t*>(ht.pairs), const_cast<float*>(ht.init),
+                                s));
+  MOE_TRY(launch_gemv_quant(GemvKind::Down, rb.fmt, r2, s2, H, I, I, perm, max_groups, ht, y_sorted, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported format or shape";
+    case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_layer_t* L, int32_t T) {
+  if (check_shape(L) || T <= 0) return 0;
+  if (!fmt_ok(L->routed.fmt)) return 0;
+  return make_layout(L, T).total;
+}
+
+int moe_workspace_clear(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < MOE_WS_CONTROL_BYTES || reinterpret_cast<uintptr_t>(ws) % kAlign) return MOE_EWORKSPACE;
+  return hip_rc(launch_workspace_clear(ws, MOE_WS_CONTROL_BYTES, (hipStream_t)stream));
+}
+
+int moe_route(const moe_layer_t* L, const uint16_t* x, int32_t T, int32_t* topk_ids, float* topk_gates,
+              float* margin, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (!L->w_router || !x || !topk_ids || !topk_gates || T <= 0) return MOE_EINVAL;
+  if (!fmt_ok(L->routed.fmt)) return MOE_EUNSUPPORTED;
+  const Layout lay = make_layout(L, T);
+  if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
+  return do_route(L, x, T, topk_ids, topk_gates, margin, ws, lay, (hipStream_t)stream);
+}
+
+int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t with_shared, int32_t* offsets,
+                int32_t* sorted_rows, int32_t* row_to_sorted, void* ws, size_t ws_bytes, void* stream) {
+  if (!topk_ids || !offsets || !sorted_rows || !row_to_sorted) return MOE_EINVAL;
+  if (T <= 0 || E < 1 || E > 1023 || k < 1 || k > E) return MOE_EINVAL;
+  if ((int64_t)T * (k + 1) > (int64_t)1 << 30) return MOE_EINVAL;
+  const int n = T * k + (with_shared ? T : 0);
+  const int nc = permute_chunks(n);
+  const size_t need = MOE_WS_CONTROL_BYTES + align_up((size_t)nc * (E + 2) * 4) * 2 + align_up((size_t)(E + 1) * 4) +
+                      align_up(4);
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign || ws_bytes < need) return MOE_EWORKSPACE;
+  size_t p = MOE_WS_CONTROL_BYTES;
+  int32_t* counts = at<int32_t>(ws, p);
+  p += align_up((size_t)nc * (E + 2) * 4);
+  int32_t* base = at<int32_t>(ws, p);
+  p += align_up((size_t)nc * (E + 2) * 4);
+  int32_t* active = at<int32_t>(ws, p);
+  p += align_up((size_t)(E + 1) * 4);
+  int32_t* n_active = at<int32_t>(ws, p);
+  return hip_rc(launch_permute(topk_ids, T, k, E, with_shared ? 1 : 0, offsets, sorted_rows, row_to_sorted, active,
+                               n_active, counts, base, (hipStream_t)stream));
+}
+
+int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T, const int32_t* offsets,
+                      const int32_t* sorted_rows, float* y_sorted, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!x || !offsets || !sorted_rows || !y_sorted || T <= 0) return MOE_EINVAL;
+  const Layout lay = make_layout(L, T);
+  if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  PermRef perm;
+  perm.offsets = offsets;
+  perm.sorted_rows = sorted_rows;
+  perm.active = at<int32_t>(ws, lay.active);
+  perm.n_active = at<int32_t>(ws, lay.n_active);
+  perm.T = T;
+  perm.k = L->top_k;
+  perm.E = L->n_experts;
+  MOE_TRY(launch_active_from_offsets(offsets, L->n_experts, const_cast<int32_t*>(perm.active),
+                                     const_cast<int32_t*>(perm.n_active), s));
+  const int n = T * L->top_k + (has_shared(L) ? T : 0);
+  return do_expert_ffn(L, x, T, perm, n, y_sorted, ws, lay, s);
+}
+
+int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* topk_gates, int32_t T, int32_t k,
+                int32_t H, int32_t with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                void* stream) {
+  if (!y_sorted || !row_to_sorted || !topk_gates || !out) return MOE_EINVAL;
+  if (T <= 0 || k < 1 || H <= 0 || H % 4) return MOE_EINVAL;
+  return hip_rc(launch_combine(y_sorted, row_to_sorted, topk_gates, T, k, H, with_shared ? 1 : 0, residual, out,
+                               out_bf16, (hipStream_t)stream));
+}
+
+static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
+                              float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
+                              void* ws, const Layout& lay, hipStream_t s) {
+  const int k = L->top_k, E = L->n_experts;
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
+  float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
+  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
+  if (rc) return rc;
+  const int with_shared = has_shared(L) ? 1 : 0;
+  const int n = T * k + (with_shared ? T : 0);
+  int32_t* offsets = at<int32_t>(ws, lay.offsets);
+  int32_t* srt = at<int32_t>(ws, lay.sorted_rows);
+  int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
+  int32_t* active = at<int32_t>(ws, lay.active);
+  int32_t* n_active = at<int32_t>(ws, lay.n_active);
+  MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, active, n_active, at<int32_t>(ws, lay.counts),
+                         at<int32_t>(ws, lay.base), s));
+  PermRef perm;
+  perm.offsets = offsets;
+  perm.sorted_rows = srt;
+  perm.active = active;
+  perm.n_active = n_active;
+  perm.T = T;
+  perm.k = k;
+  perm.E = E;
+  float* y = at<float>(ws, lay.y);
+  rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s);
+  if (rc) return rc;
+  MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual, float* out,
+                      uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!x || !out || T <= 0) return MOE_EINVAL;
+  const Layout lay = make_layout(L, T);
+  if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
+  return layer_forward_impl(L, x, T, residual, out, out_bf16, topk_ids, topk_gates, margin, ws, lay,
+                            (hipStream_t)stream);
+}
+
+int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_t* x0, int32_t T, uint16_t* x_out,
+                      float* out_last, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || n_layers < 1 || !x0 || !x_out || T <= 0) return MOE_EINVAL;
+  int rc;
+  size_t need = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = check_layer(&layers[l]))) return rc;
+    if (layers[l].hidden != layers[0].hidden) return MOE_EINVAL;
+    need = std::max(need, make_layout(&layers[l], T).total);
+  }
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign || ws_bytes < need) return MOE_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* cur = x0;
+  for (int l = 0; l < n_layers; ++l) {
+    const Layout lay = make_layout(&layers[l], T);
+    uint16_t* nxt = (l == n_layers - 1) ? x_out : at<uint16_t>(ws, (l % 2) ? lay.xb : lay.xa);
+    float* of = (l == n_layers - 1 && out_last) ? out_last : at<float>(ws, lay.out_f32);
+    rc = layer_forward_impl(&layers[l], cur, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s);
+    if (rc) return rc;
+    cur = nxt;
+  }
+  return MOE_OK;
+}
+
+int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers, const int32_t* slot_of,
+                             const moe_bank_t* slot_pool, const uint16_t* x, int32_t T, float* out,
+                             int32_t* topk_ids, float* topk_gates, int32_t* miss_rows, int32_t* n_miss, void* ws,
+                             size_t ws_bytes, void* stream) {
+  (void)L; (void)layer_idx; (void)n_layers; (void)slot_of; (void)slot_pool; (void)x; (void)T; (void)out;
+  (void)topk_ids; (void)topk_gates; (void)miss_rows; (void)n_miss; (void)ws; (void)ws_bytes; (void)stream;
+  return MOE_EUNSUPPORTED;
+}
+
+}  // extern "C"

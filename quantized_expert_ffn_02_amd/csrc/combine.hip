@@ -1,0 +1,78 @@
+// Gate-weighted combine of the expert outputs plus the shared expert, in a
+// fixed order (no atomics), with an optional residual add and bf16 copy.
+// The shared expert is added with weight 1 for every token (page "Strata Runs
+// 125B Qwen3.8-Flash-Next on a 12GB Gaming GPU", section "What it is": one
+// shared expert fires per token).  A fixed summation order makes the output
+// the same on every run, the property the pages report for the engine's
+// releases (page "Strata: a 125B AI model on your gaming PC", section "What is
+// new in Strata 0.1.45": byte-identical answers).
+#include "device.h"
+#include "internal.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_sorted,
+                                                 const int32_t* __restrict__ row_to_sorted,
+                                                 const float* __restrict__ gates, int T, int k, int H,
+                                                 int with_shared, const uint16_t* __restrict__ residual,
+                                                 float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+  const int t = blockIdx.y;
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;   // index of 4 consecutive outputs
+  if (q * 4 >= H) return;
+  const size_t H4 = H / 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < k; ++i) {
+    const float g = gates[(size_t)t * k + i];
+    const size_t p = (size_t)row_to_sorted[(size_t)t * k + i];
+    const float4 y = reinterpret_cast<const float4*>(y_sorted)[p * H4 + q];
+    acc.x = fmaf(g, y.x, acc.x);
+    acc.y = fmaf(g, y.y, acc.y);
+    acc.z = fmaf(g, y.z, acc.z);
+    acc.w = fmaf(g, y.w, acc.w);
+  }
+  if (with_shared) {
+    const size_t p = (size_t)row_to_sorted[(size_t)T * k + t];
+    const float4 y = reinterpret_cast<const float4*>(y_sorted)[p * H4 + q];
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
+  }
+  if (residual) {
+    const uint2 r = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[q];
+    acc.x += bf16_to_f32(r.x & 0xFFFFu);
+    acc.y += bf16_to_f32(r.x >> 16);
+    acc.z += bf16_to_f32(r.y & 0xFFFFu);
+    acc.w += bf16_to_f32(r.y >> 16);
+  }
+  reinterpret_cast<float4*>(out)[(size_t)t * H4 + q] = acc;
+  if (out_bf16) {
+    uint2 o;
+    o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    reinterpret_cast<uint2*>(out_bf16 + (size_t)t * H)[q] = o;
+  }
+}
+
+hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
+                          int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                          hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared,
+                     residual, out, out_bf16);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, (uint32_t*)ws, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

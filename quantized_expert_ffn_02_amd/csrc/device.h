@@ -1,0 +1,132 @@
+// Device helpers for the gfx950 kernels: bf16/fp16 conversions, the packed
+// bf16 dot product, wave64 reductions, and the 2-bit block dot product used by
+// every dequant-GEMV kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+
+#define MOE_WAVE 64
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN keeps a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float fp16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi over packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(moe_bf16x2, a),
+                                         __builtin_bit_cast(moe_bf16x2, b), acc, false);
+}
+
+// A constant held in a VGPR, so that (x & m) | magic can be one v_and_or_b32
+// (gfx9 VOP3 encodings take no literal operand).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// 2-bit block dot product ("magic pair" form).
+//
+// A 32-weight block is two u32 words of 16 codes each (weight j of a word at
+// bits 2j..2j+1).  For pair index j in 0..7 the word holds weight j in its low
+// half and weight j + 8 in its high half.  Three code positions of each half
+// (bits 0-1, 2-3, 4-5) lie inside a bf16 significand; OR-ing the exponent of
+// 128.0 onto them gives the bf16 pair (128 + c_j * 2^p, 128 + c_{j+8} * 2^p)
+// with no conversion instruction.  The activation pair table holds
+// (x_j * 2^-p, x_{j+8} * 2^-p) (exact: scaling by a power of two), so one
+// dot2 yields x*c plus the constant 128 * 2^-p * x, and the per-block init
+// value  -(sum_k (128 * 2^-p(k) + 2) * x_k)  removes both that constant and
+// the code offset 2.  Result: sum_k x_k * (c_k - 2) over the block.
+//
+//   pair j : 0 1 2 | 3 4 5 | 6 7
+//   shift  : 0 0 0 | 6 6 6 | 12 12
+//   p      : 0 2 4 | 0 2 4 | 0 2
+// ---------------------------------------------------------------------------
+struct Q2Masks {
+  uint32_t m0, m1, m2, magic;
+};
+
+__device__ __forceinline__ Q2Masks q2_masks() {
+  Q2Masks m;
+  m.m0 = vgpr_const(0x00030003u);
+  m.m1 = vgpr_const(0x000C000Cu);
+  m.m2 = vgpr_const(0x00300030u);
+  m.magic = vgpr_const(0x43004300u);
+  return m;
+}
+
+// acc + sum over the 16 weights of word w of x * c (plus the magic constant
+// term), with xp the 8 activation pairs of this word.
+__device__ __forceinline__ float q2_word_dot(uint32_t w, const uint32_t* __restrict__ xp, float acc,
+                                             const Q2Masks& M) {
+  const uint32_t a = w, b = w >> 6, c = w >> 12;
+  acc = dot2_bf16((a & M.m0) | M.magic, xp[0], acc);
+  acc = dot2_bf16((a & M.m1) | M.magic, xp[1], acc);
+  acc = dot2_bf16((a & M.m2) | M.magic, xp[2], acc);
+  acc = dot2_bf16((b & M.m0) | M.magic, xp[3], acc);
+  acc = dot2_bf16((b & M.m1) | M.magic, xp[4], acc);
+  acc = dot2_bf16((b & M.m2) | M.magic, xp[5], acc);
+  acc = dot2_bf16((c & M.m0) | M.magic, xp[6], acc);
+  acc = dot2_bf16((c & M.m1) | M.magic, xp[7], acc);
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// 3-bit block dot product.  Codes c = lo + 4 hi; lo uses the 2-bit form above,
+// hi is a bit plane whose 32-bit word d covers lo-words 2d and 2d+1:
+// bits j / 16 + j (j < 8) hold the hi bits of weights j / j + 8 of word 2d, and
+// bits 8 + j / 24 + j those of word 2d + 1.  For word 2d the pair of bit
+// position j (j = 0..6) is used in place (it lies inside a bf16 significand:
+// magic 128, value 128 + hi * 2^j); position 7 is shifted down to 0.  Word
+// 2d + 1 first shifts h right by 8.  The hi pair table holds
+// (4 x_j 2^-q, 4 x_{j+8} 2^-q) with q = j (j < 7) and q = 0 (j = 7), so each dot
+// adds 4 * x * hi plus the constant 512 * 2^-q * x, which the init removes.
+// ---------------------------------------------------------------------------
+struct Q3Masks {
+  uint32_t bit[7];
+  uint32_t magic;
+};
+
+__device__ __forceinline__ Q3Masks q3_masks() {
+  Q3Masks m;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) m.bit[j] = vgpr_const(0x00010001u << j);
+  m.magic = vgpr_const(0x43004300u);
+  return m;
+}
+
+__device__ __forceinline__ float q3_hi_dot(uint32_t h, const uint32_t* __restrict__ xp, float acc,
+                                           const Q3Masks& M) {
+#pragma unroll
+  for (int j = 0; j < 7; ++j) acc = dot2_bf16((h & M.bit[j]) | M.magic, xp[j], acc);
+  acc = dot2_bf16(((h >> 7) & M.bit[0]) | M.magic, xp[7], acc);
+  return acc;
+}

@@ -1,0 +1,102 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// One weight matrix of a bank: [n_experts] x [N rows x K cols].
+struct MatRef {
+  const uint8_t* codes = nullptr;     // Q2 codes / Q3 lo plane / bf16 values (as bytes)
+  const uint8_t* hi = nullptr;        // Q3 hi plane
+  const uint16_t* scales = nullptr;   // fp16 block scales
+  size_t code_stride = 0;             // bytes per expert
+  size_t hi_stride = 0;               // bytes per expert
+  size_t scale_stride = 0;            // scales per expert
+};
+
+inline MatRef mat_w13(const moe_bank_t& b) {
+  MatRef m;
+  const size_t n = (size_t)2 * b.inter * b.hidden;
+  m.codes = (const uint8_t*)b.w13;
+  m.hi = (const uint8_t*)b.w13_hi;
+  m.scales = b.w13_scale;
+  m.code_stride = b.fmt == MOE_FMT_BF16 ? n * 2 : n / 4;
+  m.hi_stride = n / 8;
+  m.scale_stride = n / 32;
+  return m;
+}
+
+inline MatRef mat_w2(const moe_bank_t& b) {
+  MatRef m;
+  const size_t n = (size_t)b.hidden * b.inter;
+  m.codes = (const uint8_t*)b.w2;
+  m.hi = (const uint8_t*)b.w2_hi;
+  m.scales = b.w2_scale;
+  m.code_stride = b.fmt == MOE_FMT_BF16 ? n * 2 : n / 4;
+  m.hi_stride = n / 8;
+  m.scale_stride = n / 32;
+  return m;
+}
+
+// Groups of a permutation: group g < E is routed expert g, group E the shared expert.
+struct PermRef {
+  const int32_t* offsets = nullptr;      // [E + 2]
+  const int32_t* sorted_rows = nullptr;  // [n]
+  const int32_t* active = nullptr;       // non-empty groups, ascending [<= E + 1]
+  const int32_t* n_active = nullptr;     // device scalar
+  int32_t T = 0, k = 0, E = 0;
+};
+
+// Activation table of a quantized GEMV input (see k_prep_table): per row and
+// 32-column block, ``sets`` x 16 packed bf16 pairs and one fp32 init value.
+struct TableRef {
+  const uint32_t* pairs = nullptr;   // [rows][K/32][sets][16]
+  const float* init = nullptr;       // [rows][K/32]
+  int sets = 1;
+};
+
+enum class GemvKind { GateUp, Down };
+
+// ---- launchers (return hipGetLastError()) ----
+hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s);
+
+hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
+                              float* logits, hipStream_t s);
+hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
+                              float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
+                       hipStream_t s);
+
+// permutation: counts/base are [n_chunks][E + 2] int32 scratch; active/n_active outputs
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* active, int32_t* n_active,
+                          int32_t* counts, int32_t* base, hipStream_t s);
+int permute_chunks(int n_entries);
+hipError_t launch_active_from_offsets(const int32_t* offsets, int E, int32_t* active, int32_t* n_active,
+                                      hipStream_t s);
+
+// activation tables
+hipError_t launch_prep_table_bf16(const uint16_t* x, int rows, int K, bool q3, uint32_t* pairs, float* init,
+                                  hipStream_t s);
+hipError_t launch_prep_table_f32(const float* h, int rows, int K, bool q3, uint32_t* pairs, float* init,
+                                 hipStream_t s);
+hipError_t launch_bf16_rows_to_f32(const uint16_t* x, int rows, int K, float* out, hipStream_t s);
+
+// dequant GEMV over the groups of a permutation
+hipError_t launch_gemv_quant(GemvKind kind, int fmt, const MatRef& routed, const MatRef& shared, int N, int K,
+                             int inter, const PermRef& perm, int max_groups, const TableRef& tab, float* out,
+                             hipStream_t s);
+hipError_t launch_gemv_dense(GemvKind kind, const MatRef& routed, const MatRef& shared, int N, int K, int inter,
+                             const PermRef& perm, int max_groups, const float* in_rows, float* out,
+                             hipStream_t s);
+
+hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
+                          int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                          hipStream_t s);
+
+}  // namespace moe

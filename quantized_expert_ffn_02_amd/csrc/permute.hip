@@ -1,0 +1,167 @@
+// Token permutation by expert: a stable counting sort of the routed entries
+// r = t*k + i (and the shared-expert entries r = T*k + t as group E), done as
+// histogram -> prefix sum -> stable scatter, all on the device with integer
+// arithmetic only (so the result is the same on every run).
+//
+// The pages motivate it: per token only 10 of a layer's 512 experts run (page
+// "Strata Runs 125B Qwen3.8-Flash-Next on a 12GB Gaming GPU", section "How a
+// 125B model fits in 12 GB"), and a prompt chunk of up to 8,192 tokens (page
+// "Strata Runs a 125-Billion-Parameter Qwen Model on a 12 GB Gaming GPU ...")
+// has to be grouped by expert before each expert's weights are read once.
+#include "device.h"
+#include "internal.h"
+
+namespace moe {
+
+static constexpr int kChunk = 1024;   // entries per histogram / scatter chunk
+
+int permute_chunks(int n_entries) { return (n_entries + kChunk - 1) / kChunk; }
+
+__device__ __forceinline__ int group_of(const int32_t* __restrict__ ids, int r, int Tk, int E) {
+  return r < Tk ? ids[r] : E;
+}
+
+// Per-chunk histogram over G = E + 1 groups: counts[chunk][g].
+__global__ __launch_bounds__(256) void k_perm_hist(const int32_t* __restrict__ ids, int Tk, int n, int E,
+                                                   int32_t* __restrict__ counts) {
+  __shared__ int h[1024];
+  const int G = E + 1;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) h[g] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * kChunk;
+  const int r1 = min(n, r0 + kChunk);
+  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+    const int g = group_of(ids, r, Tk, E);
+    if ((unsigned)g <= (unsigned)E) atomicAdd(&h[g], 1);   // out-of-range ids are dropped
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x) counts[(size_t)blockIdx.x * G + g] = h[g];
+}
+
+// Exclusive scan of v over the 1024 threads of a block (v = 0 past the end).
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int s = wsum[i];
+    if (i < w) base += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return base + incl - v;
+}
+
+// One block of 1024 threads, thread g = group: totals, offsets, per-chunk bases,
+// and the ascending list of non-empty groups.
+__global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
+                                                    int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  const int G = E + 1;
+  const int g = threadIdx.x;
+  int tot = 0;
+  if (g < G)
+    for (int c = 0; c < n_chunks; ++c) tot += counts[(size_t)c * G + g];
+  int n_all = 0;
+  const int off = block_exclusive_scan_1024(g < G ? tot : 0, &n_all);
+  int n_act = 0;
+  const int apos = block_exclusive_scan_1024(g < G && tot > 0 ? 1 : 0, &n_act);
+  if (g < G) {
+    offsets[g] = off;
+    int run = off;
+    for (int c = 0; c < n_chunks; ++c) {
+      base[(size_t)c * G + g] = run;
+      run += counts[(size_t)c * G + g];
+    }
+    if (tot > 0) active[apos] = g;
+  }
+  if (g == 0) {
+    offsets[G] = n_all;
+    *n_active = n_act;
+  }
+}
+
+// One wave per chunk: entries in ascending r, 64 at a time; the rank of an
+// entry among equal-group entries of its batch comes from ballots over the
+// group's bits, and a per-group running count in LDS carries across batches.
+__global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int Tk, int n, int E,
+                                                     const int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ sorted_rows,
+                                                     int32_t* __restrict__ row_to_sorted) {
+  __shared__ int run[1024];
+  const int G = E + 1;
+  const int lane = threadIdx.x;
+  for (int g = lane; g < G; g += 64) run[g] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * kChunk;
+  const int r1 = min(n, r0 + kChunk);
+  const int32_t* __restrict__ cbase = base + (size_t)blockIdx.x * G;
+  for (int b = r0; b < r1; b += 64) {
+    const int r = b + lane;
+    int g = r < r1 ? group_of(ids, r, Tk, E) : 0;
+    const bool valid = r < r1 && (unsigned)g <= (unsigned)E;
+    if (!valid) g = 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const bool on = (g >> bit) & 1;
+      const uint64_t m = __ballot(on);
+      peers &= on ? m : ~m;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & below);
+    int prior = 0;
+    if (valid) prior = run[g];
+    __syncthreads();
+    if (valid) {
+      const int pos = cbase[g] + prior + rank;
+      sorted_rows[pos] = r;
+      row_to_sorted[r] = pos;
+      const bool last = (peers >> lane) == 1ull;   // highest lane of this group in the batch
+      if (last) run[g] = prior + __popcll(peers);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* active, int32_t* n_active,
+                          int32_t* counts, int32_t* base, hipStream_t s) {
+  const int Tk = T * k;
+  const int n = Tk + (with_shared ? T : 0);
+  const int nc = permute_chunks(n);
+  hipLaunchKernelGGL(k_perm_hist, dim3(nc), dim3(256), 0, s, ids, Tk, n, E, counts);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets, active, n_active);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(nc), dim3(64), 0, s, ids, Tk, n, E, base, sorted_rows, row_to_sorted);
+  return hipGetLastError();
+}
+
+// Non-empty groups of an existing offsets array (for callers that permuted themselves).
+__global__ __launch_bounds__(1024) void k_active_from_offsets(const int32_t* __restrict__ offsets, int E,
+                                                              int32_t* __restrict__ active,
+                                                              int32_t* __restrict__ n_active) {
+  const int G = E + 1;
+  const int g = threadIdx.x;
+  const bool ne = g < G && offsets[g + 1] > offsets[g];
+  int n_act = 0;
+  const int pos = block_exclusive_scan_1024(ne ? 1 : 0, &n_act);
+  if (ne) active[pos] = g;
+  if (g == 0) *n_active = n_act;
+}
+
+hipError_t launch_active_from_offsets(const int32_t* offsets, int E, int32_t* active, int32_t* n_active,
+                                      hipStream_t s) {
+  hipLaunchKernelGGL(k_active_from_offsets, dim3(1), dim3(1024), 0, s, offsets, E, active, n_active);
+  return hipGetLastError();
+}
+
+}  // namespace moe

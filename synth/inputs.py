@@ -23,7 +23,7 @@ counts per expert are the only shape facts used.
 import numpy as np
 
 __all__ = [
-    "stream", "f32_to_bf16_bits", "activations", "router_weight", "zipf_ranks",
+    "stream", "f32_to_bf16_bits", "activation_row", "activations", "router_weight", "zipf_ranks",
     "zipf_bias", "expert_tensors", "bank", "hot_slot_table", "expert_nbytes",
 ]
 
@@ -47,13 +47,17 @@ def f32_to_bf16_bits(a):
     return u.astype(np.uint16)
 
 
+def activation_row(seed, layer, t, H, attempt=0):
+    """bf16 bits [H] of token t, from its own stream (a later attempt is a fresh draw)."""
+    g = stream(seed, "x", layer, t, attempt)
+    return f32_to_bf16_bits(g.standard_normal(H, dtype=np.float32))
+
+
 def activations(seed, layer, T, H, attempts=None):
     """bf16 bits [T, H]; token t is drawn from its own stream (attempt attempts[t])."""
     out = np.empty((T, H), dtype=np.uint16)
     for t in range(T):
-        a = 0 if attempts is None else int(attempts[t])
-        g = stream(seed, "x", layer, t, a)
-        out[t] = f32_to_bf16_bits(g.standard_normal(H, dtype=np.float32))
+        out[t] = activation_row(seed, layer, t, H, 0 if attempts is None else int(attempts[t]))
     return out
 
 

@@ -1,0 +1,97 @@
+"""Test-side construction of the workloads: seeded inputs from ``synth``, with the
+router margin enforced through the oracle's fp64 logits (a token whose gap
+between the k-th and (k+1)-th logit is below 1e-4 is redrawn from a fresh
+sub-stream), and device upload.  Test infrastructure."""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+import synth
+from oracle import formats as OF
+from oracle import layer as OL
+
+MIN_MARGIN = 1e-4
+
+
+@dataclass
+class HostLayer:
+    seed: int
+    layer: int
+    shape: synth.LayerShape
+    wr: np.ndarray
+    bias: Optional[np.ndarray]
+    routed: dict
+    shared: Optional[dict]
+    _fn: dict = field(default_factory=dict)
+
+    @property
+    def H(self):
+        return self.shape.hidden
+
+    @property
+    def I(self):
+        return self.shape.inter
+
+    def expert_fn(self):
+        if "e" not in self._fn:
+            self._fn["e"] = OL.bank_expert_fn(self.shape.fmt, self.routed, self.H, self.I)
+        return self._fn["e"]
+
+    def shared_fn(self):
+        if self.shared is None:
+            return None
+        if "s" not in self._fn:
+            m = OF.expert_matrices(self.shape.fmt, self.shared, self.H, self.I)
+            self._fn["s"] = lambda: m
+        return self._fn["s"]
+
+    def oracle_forward(self, x_bits, residual_bits=None):
+        return OL.layer_forward(x_bits, self.wr, self.shape.top_k, self.expert_fn(), self.shared_fn(),
+                                bias=self.bias, residual_bits=residual_bits)
+
+    def logits(self, x_bits):
+        return OL.router_logits(x_bits, self.wr, self.bias)
+
+
+def host_layer(workload, layer=0, shape=None, router_std=0.02):
+    """All experts of one layer of a workload (name or synth.Workload)."""
+    w = synth.CONFIGS[workload] if isinstance(workload, str) else workload
+    s = shape or w.shape
+    wr = synth.router_weight(w.seed, layer, s.n_experts, s.hidden, std=router_std)
+    bias = synth.zipf_bias(w.seed, layer, s.n_experts, s.zipf) if s.zipf else None
+    routed = synth.bank(w.seed, layer, s.fmt, range(s.n_experts), s.hidden, s.inter)
+    shared = synth.bank(w.seed, layer, s.fmt, [s.n_experts], s.hidden, s.inter) if s.shared else None
+    return HostLayer(w.seed, layer, s, wr, bias, routed, shared)
+
+
+def activations_with_margin(hl, T, x_seed=None, min_margin=MIN_MARGIN, max_rounds=50):
+    """Token rows whose oracle top-k margin is at least min_margin (redrawing the others)."""
+    seed = hl.seed if x_seed is None else x_seed
+    attempts = np.zeros(T, dtype=np.int64)
+    x = synth.activations(seed, hl.layer, T, hl.H, attempts)
+    k = hl.shape.top_k
+    todo = np.arange(T)
+    for _ in range(max_rounds):
+        m = OL.topk_margin(OL.router_logits(x[todo], hl.wr, hl.bias), k)
+        bad = todo[m < min_margin]
+        if len(bad) == 0:
+            return x, attempts
+        for t in bad:
+            attempts[t] += 1
+            x[t] = synth.activation_row(seed, hl.layer, int(t), hl.H, int(attempts[t]))
+        todo = bad
+    raise RuntimeError("could not reach the router margin")
+
+
+def upload(hl, device="cuda"):
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer
+    s = hl.shape
+    rb = DeviceBank(s.fmt, s.n_experts, s.hidden, s.inter, hl.routed, device)
+    sb = DeviceBank(s.fmt, 1, s.hidden, s.inter, hl.shared, device) if hl.shared is not None else None
+    return DeviceLayer(s.hidden, s.n_experts, s.top_k, s.inter, hl.wr, hl.bias, rb, sb, device)
+
+
+def upload_rows(a, device="cuda"):
+    from quantized_expert_ffn_02_amd.device_layer import to_device
+    return to_device(a, device)

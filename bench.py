@@ -1,0 +1,215 @@
+"""Benchmark of the quantized MoE layer on one MI355X.
+
+Workload (the decode configuration): one real-shape MoE layer -- hidden 2,560,
+512 experts, top-10 routed + 1 shared, SwiGLU experts with intermediate 640 in
+2-bit 32-weight blocks with fp16 scales -- run on a decode step of T tokens
+(default 4 = 1 token + 3 MTP drafts verified in one pass; T = 1 is reported
+alongside).  One step = one moe_layer_forward (route, permute, expert FFNs,
+shared expert, combine) on device-resident inputs.  To keep the 256 MB Infinity
+Cache from serving the weights, steps rotate over ``--rotate`` distinct layers
+(each with its own weights) and a pool of distinct token batches.
+
+Prints one JSON line with the throughput, the dominant kernel's roofline
+(algorithmic bytes / its average duration measured with HIP events on its
+stream), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def q2_expert_bytes(H, I):
+    """Bytes of one 2-bit expert: 3*H*I codes at 2 bits + one fp16 scale per 32 weights."""
+    w = 3 * H * I
+    return w // 4 + (w // 32) * 2
+
+
+def gateup_bytes_per_expert(H, I):
+    w = 2 * H * I
+    return w // 4 + (w // 32) * 2
+
+
+def cpu_baseline(hl_args, T, seconds):
+    """The fp64 oracle (tests' reference implementation, untuned) on a bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import formats as OF
+    from oracle import layer as OL
+    seed, shape, wr, routed, shared = hl_args
+    H, I, k = shape.hidden, shape.inter, shape.top_k
+    smat = OF.expert_matrices(shape.fmt, shared, H, I)
+    t0 = time.perf_counter()
+    tokens, batches = 0, 0
+    while True:
+        x = synth.activations(seed + 7000, batches, T, H)
+        fn = OL.bank_expert_fn(shape.fmt, routed, H, I)      # fresh: every used expert is dequantised again
+        OL.layer_forward(x, wr, k, fn, lambda: smat)
+        tokens += T
+        batches += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{batches} decode batches of T={T} tokens on layer 0 (fp64 numpy, experts dequantised on "
+                      f"demand), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--tokens", type=int, default=4)
+    ap.add_argument("--rotate", type=int, default=16, help="distinct layers cycled through")
+    ap.add_argument("--pool", type=int, default=64, help="distinct token batches cycled through")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    wl = synth.CONFIGS["decode"]
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    R, T = args.rotate, args.tokens
+
+    layers, host0 = [], None
+    for l in range(R):
+        wr = synth.router_weight(wl.seed, l, E, H)
+        routed = synth.bank(wl.seed, l, s.fmt, range(E), H, I, workers=16)
+        shared = synth.bank(wl.seed, l, s.fmt, [E], H, I)
+        rb = DeviceBank(s.fmt, E, H, I, routed)
+        sb = DeviceBank(s.fmt, 1, H, I, shared)
+        layers.append(DeviceLayer(H, E, k, I, wr, None, rb, sb))
+        if l == 0:
+            host0 = (wl.seed, s, wr, routed, shared)
+        del routed
+    pool = [to_device(synth.activations(wl.seed + 5000, j, T, H)) for j in range(args.pool)]
+
+    def run(T_, steps, warm, time_kernels):
+        """Headline loop (no events inside), then, if asked, a second loop with one-shot
+        HIP events around the router, gate/up and down kernels of every step."""
+        ws = layers[0].workspace(T_)
+        out = torch.empty((T_, H), dtype=torch.float32, device="cuda")
+        ids = torch.empty((max(steps, 1), T_, k), dtype=torch.int32, device="cuda")
+        xs = pool if T_ == T else [to_device(synth.activations(wl.seed + 6000, j, T_, H)) for j in range(args.pool)]
+        for i in range(warm):
+            B.layer_forward(layers[i % R].struct, xs[i % len(xs)], T_, out, ws, topk_ids=ids[0])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            B.layer_forward(layers[i % R].struct, xs[i % len(xs)], T_, out, ws, topk_ids=ids[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        ids_h = ids.cpu().numpy()
+        uniq = np.array([len(np.unique(ids_h[i])) for i in range(steps)])
+        kms = {}
+        if time_kernels:
+            kev = {}
+            for kern in (B.KERNEL_ROUTER, B.KERNEL_GATEUP_GEMV, B.KERNEL_DOWN_GEMV):
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(steps)]
+                for a, b in evs:      # create the underlying hipEvents
+                    a.record()
+                    b.record()
+                kev[kern] = evs
+            torch.cuda.synchronize()
+            for i in range(steps):
+                for kern, evs in kev.items():
+                    B.time_next_launch(kern, evs[i][0].cuda_event, evs[i][1].cuda_event)
+                B.layer_forward(layers[i % R].struct, xs[i % len(xs)], T_, out, ws)
+            torch.cuda.synchronize()
+            kms = {kern: float(np.mean([a.elapsed_time(b) for a, b in evs])) for kern, evs in kev.items()}
+        return ms, kms, uniq
+
+    ms, kms, uniq = run(T, args.steps, args.warmup, True)
+    ms_step = ms / args.steps
+    d_avg = float(uniq.mean())
+    eb = q2_expert_bytes(H, I)
+    step_bytes = E * H * 2 + (d_avg + 1) * eb + T * H * 2 + T * H * 4
+    gu_bytes = (d_avg + 1) * gateup_bytes_per_expert(H, I) + T * H * 2 + (T * k + T) * I * 4
+    gu_ms = kms[B.KERNEL_GATEUP_GEMV]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    # T = 1 alongside (same layers, no kernel events)
+    ms1, _, uniq1 = run(1, max(args.steps // 2, 1), args.warmup, False)
+    ms1_step = ms1 / max(args.steps // 2, 1)
+    step_bytes1 = E * H * 2 + (float(uniq1.mean()) + 1) * eb + H * 2 + H * 4
+
+    result = {
+        "metric": "MoE-layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"decode: one real-shape 2-bit MoE layer, T={T} tokens (1 + 3 MTP drafts), "
+                        f"{R} distinct layers rotated",
+            "hidden": H, "experts": E, "top_k": k, "shared_experts": 1, "inter": I,
+            "weights": "2-bit codes, 32-weight blocks, fp16 scales (1,536,000 B per expert)",
+            "arithmetic": "bf16 activations x exact 2-bit codes, fp32 accumulation, fp32 output",
+            "tokens": T, "layers_rotated": R,
+        },
+        "decode": {
+            "layer_us": ms_step * 1e3,
+            "unique_experts_per_step": d_avg,
+            "algorithmic_bytes_per_step": step_bytes,
+            "layer_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+            "layer_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_us": {"router": kms[B.KERNEL_ROUTER] * 1e3, "gateup_gemv": gu_ms * 1e3,
+                          "down_gemv": kms[B.KERNEL_DOWN_GEMV] * 1e3},
+            "T1": {"tokens_per_s": 1 / (ms1_step * 1e-3), "layer_us": ms1_step * 1e3,
+                   "layer_GBps": step_bytes1 / (ms1_step * 1e-3) / 1e9},
+        },
+        "roofline": {
+            "kernel": "k_gemv_quant (gate/up + SwiGLU, 2-bit dequant-GEMV)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gu_bytes,
+            "avg_launch_us": gu_ms * 1e3,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(host0, T, args.cpu_seconds)
+        result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -183,6 +183,21 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                              int32_t* miss_rows, int32_t* n_miss,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement support.  Records start_event / stop_event (hipEvent_t, created by
+ * the caller) on the call's stream immediately before and after the NEXT launch of
+ * the named kernel by any call above, then forgets them (one-shot).  Lets a
+ * benchmark time one kernel of a fused call with events on the stream it runs on.
+ * Process-global and not thread-safe: meant for benchmarks only. */
+enum {
+  MOE_KERNEL_ROUTER = 0,       /* router logits (GEMV or MFMA GEMM) */
+  MOE_KERNEL_GATEUP_GEMV = 1,  /* dequant-GEMV gate/up + SwiGLU */
+  MOE_KERNEL_DOWN_GEMV = 2,    /* dequant-GEMV down projection */
+  MOE_KERNEL_GATEUP_GEMM = 3,  /* MFMA grouped GEMM gate/up + SwiGLU */
+  MOE_KERNEL_DOWN_GEMM = 4,    /* MFMA grouped GEMM down projection */
+  MOE_KERNEL_COUNT = 5
+};
+int moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event);
+
 /* Static description of a status code. */
 const char* moe_strerror(int code);
 

@@ -14,6 +14,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 FMT_NONE, FMT_BF16, FMT_Q2, FMT_Q3 = -1, 0, 1, 2
 FMT_BY_NAME = {"bf16": FMT_BF16, "q2": FMT_Q2, "q3": FMT_Q3}
 WS_CONTROL_BYTES = 65536
+KERNEL_ROUTER, KERNEL_GATEUP_GEMV, KERNEL_DOWN_GEMV, KERNEL_GATEUP_GEMM, KERNEL_DOWN_GEMM = 0, 1, 2, 3, 4
 
 # Every function the header declares, with (restype, argtypes).
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -49,6 +50,7 @@ _SIGS = {
     "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_forward_cached": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank), _vp,
                                                 _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_time_next_launch": (ctypes.c_int, [_i32, _vp, _vp]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -67,6 +69,9 @@ def lib():
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_expert_ffn_02_amd.build`")
+        # torch ships its own HIP runtime with the same soname; importing torch first
+        # makes libmoe bind to that one instance, so torch streams are valid here
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)
@@ -172,3 +177,8 @@ def layer_forward_cached(layer, layer_idx, n_layers, slot_of, slot_pool, x, T, o
         ctypes.byref(layer), int(layer_idx), int(n_layers), ptr(slot_of), ctypes.byref(slot_pool), ptr(x), int(T),
         ptr(out), ptr(topk_ids), ptr(topk_gates), ptr(miss_rows), ptr(n_miss), ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def time_next_launch(kernel, start_event, stop_event):
+    """Arm hipEvent_t handles (ints) around the next launch of ``kernel``."""
+    _check("moe_time_next_launch", lib().moe_time_next_launch(int(kernel), start_event, stop_event))

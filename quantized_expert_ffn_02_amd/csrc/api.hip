@@ -54,7 +54,7 @@ bool has_shared(const moe_layer_t* L) { return L->shared.fmt != MOE_FMT_NONE; }
 // Workspace layout of every call for a layer shape and up to T tokens.
 struct Layout {
   size_t logits, ids, gates, margin;
-  size_t counts, base, offsets, sorted_rows, row_to_sorted, active, n_active;
+  size_t counts, base, offsets, sorted_rows, row_to_sorted, items, n_items;
   size_t xtab_pairs, xtab_init, xf32;
   size_t h, htab_pairs, htab_init, y;
   size_t out_f32, xa, xb;     // stack ping-pong buffers
@@ -84,8 +84,8 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.offsets = take((E + 2) * 4);
   o.sorted_rows = take(n * 4);
   o.row_to_sorted = take(n * 4);
-  o.active = take((E + 1) * 4);
-  o.n_active = take(4);
+  o.items = take(n * 3 * 4);
+  o.n_items = take(4);
   o.xtab_pairs = take(dense ? 0 : T * (H / 32) * planes * 16 * 4);
   o.xtab_init = take(dense ? 0 : T * (H / 32) * 4);
   o.xf32 = take(dense ? T * H * 4 : 0);
@@ -115,6 +115,27 @@ int check_ws(void* ws, size_t ws_bytes, const Layout& lay) {
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// One-shot event pairs for moe_time_next_launch.
+struct TimedLaunch {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+TimedLaunch g_timed[MOE_KERNEL_COUNT];
+
+// Runs ``launch`` bracketed by the pending events of ``kernel`` (if any).
+template <typename F>
+hipError_t timed(int kernel, hipStream_t s, F&& launch) {
+  TimedLaunch t = g_timed[kernel];
+  if (t.start) {
+    g_timed[kernel] = TimedLaunch();
+    hipError_t e = hipEventRecord(t.start, s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    return hipEventRecord(t.stop, s);
+  }
+  return launch();
+}
+
 #define MOE_TRY(expr)                   \
   do {                                  \
     hipError_t e_ = (expr);             \
@@ -126,17 +147,20 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float* gates, float* margin, void* ws,
              const Layout& lay, hipStream_t s) {
   float* logits = at<float>(ws, lay.logits);
-  MOE_TRY(launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s));
+  MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] {
+    return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+  }));
   MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
   return MOE_OK;
 }
 
 int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef& perm, int n_entries,
-                  float* y_sorted, void* ws, const Layout& lay, hipStream_t s,
+                  float* y_sorted, void* ws, const Layout& lay, hipStream_t s, bool x_table_ready = false,
                   const moe_bank_t* routed_override = nullptr) {
   const moe_bank_t& rb = routed_override ? *routed_override : L->routed;
   const int H = L->hidden, I = L->inter, E = L->n_experts;
-  const int max_groups = std::min(E + 1, n_entries);
+  (void)E;
+  const int max_groups = n_entries;   // upper bound on work items
   const MatRef r13 = mat_w13(rb), r2 = mat_w2(rb);
   const MatRef s13 = has_shared(L) ? mat_w13(L->shared) : MatRef(), s2 = has_shared(L) ? mat_w2(L->shared) : MatRef();
   float* h = at<float>(ws, lay.h);
@@ -152,21 +176,38 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
   xt.pairs = at<uint32_t>(ws, lay.xtab_pairs);
   xt.init = at<float>(ws, lay.xtab_init);
   xt.sets = q3 ? 2 : 1;
-  MOE_TRY(launch_prep_table_bf16(x, T, H, q3, const_cast<uint32_t*>(xt.pairs), const_cast<float*>(xt.init), s));
-  MOE_TRY(launch_gemv_quant(GemvKind::GateUp, rb.fmt, r13, s13, 2 * I, H, I, perm, max_groups, xt, h, s));
+  if (!x_table_ready)
+    MOE_TRY(launch_prep_table_bf16(x, T, H, q3, const_cast<uint32_t*>(xt.pairs), const_cast<float*>(xt.init), s));
   TableRef ht;
   ht.pairs = at<uint32_t>(ws, lay.htab_pairs);
   ht.init = at<float>(ws, lay.htab_init);
   ht.sets = (q3 ? 2 : 1) * 2;
-  MOE_TRY(launch_prep_table_f32(h, n_entries, I, q3, const_cast<uint32_t*>(ht.pairs), const_cast<float*>(ht.init),
-                                s));
-  MOE_TRY(launch_gemv_quant(GemvKind::Down, rb.fmt, r2, s2, H, I, I, perm, max_groups, ht, y_sorted, s));
+  MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] {
+    return launch_gemv_quant(GemvKind::GateUp, rb.fmt, r13, s13, 2 * I, H, I, perm, max_groups, xt, h,
+                             const_cast<uint32_t*>(ht.pairs), const_cast<float*>(ht.init), s);
+  }));
+  MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] {
+    return launch_gemv_quant(GemvKind::Down, rb.fmt, r2, s2, H, I, I, perm, max_groups, ht, y_sorted, nullptr,
+                             nullptr, s);
+  }));
   return MOE_OK;
 }
+
+// Entries per GEMV work item: one token per block for decode-sized batches
+// (most parallel), four for larger batches.
+int items_per_for(int T) { return T <= 16 ? 1 : 4; }
 
 }  // namespace
 
 extern "C" {
+
+int moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event) {
+  if (kernel < 0 || kernel >= MOE_KERNEL_COUNT) return MOE_EINVAL;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_EINVAL;
+  g_timed[kernel].start = (hipEvent_t)start_event;
+  g_timed[kernel].stop = (hipEvent_t)stop_event;
+  return MOE_OK;
+}
 
 const char* moe_strerror(int code) {
   switch (code) {
@@ -208,19 +249,14 @@ int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_
   if ((int64_t)T * (k + 1) > (int64_t)1 << 30) return MOE_EINVAL;
   const int n = T * k + (with_shared ? T : 0);
   const int nc = permute_chunks(n);
-  const size_t need = MOE_WS_CONTROL_BYTES + align_up((size_t)nc * (E + 2) * 4) * 2 + align_up((size_t)(E + 1) * 4) +
-                      align_up(4);
+  const size_t need = MOE_WS_CONTROL_BYTES + align_up((size_t)nc * (E + 2) * 4) * 2;
   if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign || ws_bytes < need) return MOE_EWORKSPACE;
   size_t p = MOE_WS_CONTROL_BYTES;
   int32_t* counts = at<int32_t>(ws, p);
   p += align_up((size_t)nc * (E + 2) * 4);
   int32_t* base = at<int32_t>(ws, p);
-  p += align_up((size_t)nc * (E + 2) * 4);
-  int32_t* active = at<int32_t>(ws, p);
-  p += align_up((size_t)(E + 1) * 4);
-  int32_t* n_active = at<int32_t>(ws, p);
-  return hip_rc(launch_permute(topk_ids, T, k, E, with_shared ? 1 : 0, offsets, sorted_rows, row_to_sorted, active,
-                               n_active, counts, base, (hipStream_t)stream));
+  return hip_rc(launch_permute(topk_ids, T, k, E, with_shared ? 1 : 0, offsets, sorted_rows, row_to_sorted, counts,
+                               base, (hipStream_t)stream));
 }
 
 int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T, const int32_t* offsets,
@@ -234,13 +270,13 @@ int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
   PermRef perm;
   perm.offsets = offsets;
   perm.sorted_rows = sorted_rows;
-  perm.active = at<int32_t>(ws, lay.active);
-  perm.n_active = at<int32_t>(ws, lay.n_active);
+  perm.items = at<int32_t>(ws, lay.items);
+  perm.n_items = at<int32_t>(ws, lay.n_items);
   perm.T = T;
   perm.k = L->top_k;
   perm.E = L->n_experts;
-  MOE_TRY(launch_active_from_offsets(offsets, L->n_experts, const_cast<int32_t*>(perm.active),
-                                     const_cast<int32_t*>(perm.n_active), s));
+  MOE_TRY(launch_items_from_offsets(offsets, L->n_experts, items_per_for(T), const_cast<int32_t*>(perm.items),
+                                    const_cast<int32_t*>(perm.n_items), s));
   const int n = T * L->top_k + (has_shared(L) ? T : 0);
   return do_expert_ffn(L, x, T, perm, n, y_sorted, ws, lay, s);
 }
@@ -260,27 +296,58 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   const int k = L->top_k, E = L->n_experts;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
-  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
-  if (rc) return rc;
   const int with_shared = has_shared(L) ? 1 : 0;
   const int n = T * k + (with_shared ? T : 0);
   int32_t* offsets = at<int32_t>(ws, lay.offsets);
   int32_t* srt = at<int32_t>(ws, lay.sorted_rows);
   int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
-  int32_t* active = at<int32_t>(ws, lay.active);
-  int32_t* n_active = at<int32_t>(ws, lay.n_active);
-  MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, active, n_active, at<int32_t>(ws, lay.counts),
-                         at<int32_t>(ws, lay.base), s));
+  int32_t* items = at<int32_t>(ws, lay.items);
+  int32_t* n_items = at<int32_t>(ws, lay.n_items);
+  const bool quant = L->routed.fmt != MOE_FMT_BF16;
+  bool x_table_ready = false;
+  if (n <= kSmallRouteMaxEntries) {
+    // decode / MTP-verify batch: router, activation table, top-k and permutation in one launch
+    SmallRouteArgs a;
+    a.x = x;
+    a.T = T;
+    a.E = E;
+    a.H = L->hidden;
+    a.k = k;
+    a.with_shared = with_shared;
+    a.q3 = L->routed.fmt == MOE_FMT_Q3;
+    a.wr = L->w_router;
+    a.bias = L->router_bias;
+    a.logits = at<float>(ws, lay.logits);
+    a.xpairs = quant ? at<uint32_t>(ws, lay.xtab_pairs) : nullptr;
+    a.xinit = quant ? at<float>(ws, lay.xtab_init) : nullptr;
+    a.ids = ids;
+    a.gates = gates;
+    a.margin = margin;
+    a.offsets = offsets;
+    a.sorted_rows = srt;
+    a.row_to_sorted = inv;
+    a.items = items;
+    a.n_items = n_items;
+    a.items_per = items_per_for(T);
+    MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_small(a, s); }));
+    x_table_ready = quant;
+  } else {
+    int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
+    if (rc) return rc;
+    MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                           at<int32_t>(ws, lay.base), s));
+    MOE_TRY(launch_items_from_offsets(offsets, E, items_per_for(T), items, n_items, s));
+  }
   PermRef perm;
   perm.offsets = offsets;
   perm.sorted_rows = srt;
-  perm.active = active;
-  perm.n_active = n_active;
+  perm.items = items;
+  perm.n_items = n_items;
   perm.T = T;
   perm.k = k;
   perm.E = E;
   float* y = at<float>(ws, lay.y);
-  rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s);
+  int rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s, x_table_ready);
   if (rc) return rc;
   MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
   return MOE_OK;

@@ -1,0 +1,211 @@
+// Decode front end: router logits, activation-table prep, top-k and the
+// permutation of a small token batch (T*k + T <= 1024 entries: a decode step or
+// an MTP verify batch of 1 + 3 tokens, page "Strata Runs 125B Qwen3.8-Flash-Next
+// on a 12GB Gaming GPU", section "How a 125B model fits in 12 GB") in two
+// launches.
+//
+// k_route_front: every block computes the logits of 4 experts (one wave per
+// bf16 router row, the row's and the tokens' 16-byte chunks all loaded before
+// any arithmetic) and a slice of the activation pair table.
+// k_route_select: one block runs top-k for every token (a wave per token) and a
+// stable counting sort of the T*k (+T shared) entries into offsets, sorted rows,
+// the inverse map and the GEMV work items.  (A single fused launch with a
+// last-block ticket needs agent-scope release/acquire fences on every block,
+// which cost more than the second launch.)
+#include <math.h>
+
+#include "device.h"
+#include "internal.h"
+#include "table.h"
+#include "topk.h"
+
+namespace moe {
+
+// logits of expert row e for tokens [t0, t0 + TB): the row's NC 16-byte chunks
+// per lane and the matching x chunks of all TB tokens are loaded before any
+// arithmetic (one memory round trip per call).
+template <int TB, int NC>
+__device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T, int t0,
+                                           const uint16_t* __restrict__ wr, float b, int E, int H, int e,
+                                           float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const uint4* __restrict__ wrow = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
+  const int nch = H / 8;
+  uint4 w[NC], xv[TB][NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int c = lane + 64 * u;
+    w[u] = c < nch ? wrow[c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      xv[i][u] = (c < nch && t0 + i < T) ? reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H)[c]
+                                         : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      a = dot2_bf16(w[u].x, xv[i][u].x, a);
+      a = dot2_bf16(w[u].y, xv[i][u].y, a);
+      a = dot2_bf16(w[u].z, xv[i][u].z, a);
+      a = dot2_bf16(w[u].w, xv[i][u].w, a);
+    }
+    const float sum = wave_sum(a);
+    if (lane == 0 && t0 + i < T) logits[(size_t)(t0 + i) * E + e] = sum + b;
+  }
+}
+
+// all tokens, 4 at a time, for H <= 64 * 8 * NC
+template <int NC>
+__device__ __forceinline__ void router_row_all(const uint16_t* __restrict__ x, int T,
+                                               const uint16_t* __restrict__ wr, float b, int E, int H, int e,
+                                               float* __restrict__ logits) {
+  for (int t0 = 0; t0 < T; t0 += 4) router_row<4, NC>(x, T, t0, wr, b, E, H, e, logits);
+}
+
+__device__ __forceinline__ void router_row_dispatch(const uint16_t* __restrict__ x, int T,
+                                                    const uint16_t* __restrict__ wr, float b, int E, int H, int e,
+                                                    float* __restrict__ logits) {
+  if (H <= 2560)
+    router_row_all<5>(x, T, wr, b, E, H, e, logits);
+  else
+    router_row_all<8>(x, T, wr, b, E, H, e, logits);
+}
+
+// Router GEMV for any T: one wave per expert row, tokens 4 at a time.
+__global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, int T,
+                                                     const uint16_t* __restrict__ wr,
+                                                     const float* __restrict__ bias, int E, int H,
+                                                     float* __restrict__ logits) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const float b = bias ? bias[e] : 0.0f;
+  router_row_dispatch(x, T, wr, b, E, H, e, logits);
+}
+
+hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
+                              float* logits, hipStream_t s) {
+  hipLaunchKernelGGL(k_router_gemv, dim3((E + 3) / 4), dim3(256), 0, s, x, T, wr, bias, E, H, logits);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_route_front(SmallRouteArgs a) {
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int e = blockIdx.x * 4 + wv;
+  if (e < a.E) {
+    const float b = a.bias ? a.bias[e] : 0.0f;
+    router_row_dispatch(a.x, a.T, a.wr, b, a.E, a.H, e, a.logits);
+  }
+  if (a.xpairs) {
+    const int nblk = a.H / 32;
+    const int items = a.T * nblk * 16;
+    for (int it = blockIdx.x * 256 + tid; it < items; it += gridDim.x * 256) {
+      const int row = it / (nblk * 16), rem = it % (nblk * 16);
+      prep_x_item(a.x, row, a.H, rem >> 4, (rem >> 3) & 1, rem & 7, a.q3 != 0, a.xpairs, a.xinit);
+    }
+  }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void k_route_select(SmallRouteArgs a) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_grp[1024 + 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+  // ---- phase 2: top-k, one wave per token
+  const int k = a.k, T = a.T, E = a.E;
+  for (int t = wv; t < T; t += 4)
+    wave_topk_row<VPL>(a.logits + (size_t)t * E, E, k, a.ids + (size_t)t * k, a.gates + (size_t)t * k,
+                       a.margin ? a.margin + t : nullptr, s_grp + t * k);
+  // ---- phase 3: stable counting sort of n entries over G = E + 1 groups
+  const int G = E + 1;
+  const int n = T * k + (a.with_shared ? T : 0);
+  for (int g = tid; g < 1024; g += 256) s_cnt[g] = 0;
+  for (int r = T * k + tid; r < n; r += 256) s_grp[r] = E;
+  __syncthreads();
+  for (int r = tid; r < n; r += 256) atomicAdd(&s_cnt[s_grp[r]], 1);
+  __syncthreads();
+  // exclusive scans over the groups (each thread owns 4 consecutive groups) of
+  // the entry counts and of the work-item counts ceil(count / items_per)
+  const int IP = a.items_per;
+  int c4[4], loc = 0, nzi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c4[i] = s_cnt[tid * 4 + i];
+    loc += c4[i];
+    nzi += (c4[i] + IP - 1) / IP;
+  }
+  int inc = loc, inci = nzi;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64), oi = __shfl_up(inci, off, 64);
+    if (lane >= off) {
+      inc += o;
+      inci += oi;
+    }
+  }
+  __shared__ int s_w[4], s_wi[4];
+  if (lane == 63) {
+    s_w[wv] = inc;
+    s_wi[wv] = inci;
+  }
+  __syncthreads();
+  int base = 0, basei = 0, tot = 0, toti = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (i < wv) {
+      base += s_w[i];
+      basei += s_wi[i];
+    }
+    tot += s_w[i];
+    toti += s_wi[i];
+  }
+  int run = base + inc - loc, runi = basei + inci - nzi;
+  __syncthreads();   // everyone has read s_cnt; reuse it for the offsets
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = tid * 4 + i;
+    if (g < G) {
+      a.offsets[g] = run;
+      s_cnt[g] = run;
+      for (int q = 0; q < c4[i]; q += IP) {
+        a.items[3 * runi + 0] = g;
+        a.items[3 * runi + 1] = run + q;
+        a.items[3 * runi + 2] = min(IP, c4[i] - q);
+        ++runi;
+      }
+    }
+    run += c4[i];
+  }
+  if (tid == 0) {
+    a.offsets[G] = tot;
+    *a.n_items = toti;
+  }
+  __syncthreads();
+  // stable position: offset of the group + number of earlier entries in it
+  for (int r = tid; r < n; r += 256) {
+    const int g = s_grp[r];
+    int rank = 0;
+    for (int q = 0; q < r; ++q) rank += s_grp[q] == g;
+    const int pos = s_cnt[g] + rank;
+    a.sorted_rows[pos] = r;
+    a.row_to_sorted[r] = pos;
+  }
+}
+
+hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  if (a.E <= 64)
+    hipLaunchKernelGGL(k_route_select<1>, dim3(1), dim3(256), 0, s, a);
+  else if (a.E <= 128)
+    hipLaunchKernelGGL(k_route_select<2>, dim3(1), dim3(256), 0, s, a);
+  else if (a.E <= 256)
+    hipLaunchKernelGGL(k_route_select<4>, dim3(1), dim3(256), 0, s, a);
+  else if (a.E <= 512)
+    hipLaunchKernelGGL(k_route_select<8>, dim3(1), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_route_select<16>, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -16,10 +16,9 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 
 // fp32 -> bf16, round to nearest even (finite inputs; NaN keeps a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) | 0x40u) : r;   // NaN stays a quiet NaN
 }
 
 __device__ __forceinline__ float fp16_to_f32(uint32_t bits16) {

@@ -20,51 +20,9 @@
 
 #include "device.h"
 #include "internal.h"
+#include "table.h"
 
 namespace moe {
-
-// exponent shift p of lo-plane pair j and q of hi-plane pair j (device.h tables)
-__device__ __forceinline__ int lo_shift(int j) {
-  const int P[8] = {0, 2, 4, 0, 2, 4, 0, 2};
-  return P[j];
-}
-__device__ __forceinline__ int hi_shift(int j) { return j < 7 ? j : 0; }
-
-// ---------------------------------------------------------------------------
-// Activation tables.  One block of 256 threads per input row; 16 threads per
-// 32-column block: thread (wi, j) handles the pair (16 wi + j, 16 wi + j + 8).
-// Sets per block: [split][plane] with split = hi, lo (fp32 input only) and
-// plane = lo codes, hi bits (Q3 only).
-// ---------------------------------------------------------------------------
-template <bool Q3, bool SPLIT>
-__device__ void prep_row(const float v0, const float v1, int row, int b, int wi, int j, int nblk,
-                         uint32_t* __restrict__ pairs, float* __restrict__ init) {
-  constexpr int PLANES = Q3 ? 2 : 1;
-  constexpr int SETS = PLANES * (SPLIT ? 2 : 1);
-  const float sp = ldexpf(1.0f, -lo_shift(j));
-  const float sq = ldexpf(4.0f, -hi_shift(j));
-  float hi0 = v0, hi1 = v1, lo0 = 0.0f, lo1 = 0.0f;
-  if (SPLIT) {
-    hi0 = bf16_to_f32(f32_to_bf16_rne(v0));
-    hi1 = bf16_to_f32(f32_to_bf16_rne(v1));
-    lo0 = bf16_to_f32(f32_to_bf16_rne(v0 - hi0));
-    lo1 = bf16_to_f32(f32_to_bf16_rne(v1 - hi1));
-  }
-  uint32_t* __restrict__ dst = pairs + ((size_t)row * nblk + b) * (SETS * 16) + wi * 8 + j;
-  const float parts0[2] = {hi0, lo0}, parts1[2] = {hi1, lo1};
-#pragma unroll
-  for (int s = 0; s < (SPLIT ? 2 : 1); ++s) {
-    dst[(s * PLANES) * 16] = f32_to_bf16_rne(parts0[s] * sp) | (f32_to_bf16_rne(parts1[s] * sp) << 16);
-    if (Q3)
-      dst[(s * PLANES + 1) * 16] = f32_to_bf16_rne(parts0[s] * sq) | (f32_to_bf16_rne(parts1[s] * sq) << 16);
-  }
-  // init = -sum_k (128 2^-p + [512 2^-q] + offset) * value_k over the block's 32 weights
-  const float mult = 128.0f * sp + (Q3 ? 128.0f * sq + 4.0f : 2.0f);
-  float term = mult * (hi0 + lo0) + mult * (hi1 + lo1);
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) term += __shfl_xor(term, off, 16);
-  if (wi == 0 && j == 0) init[(size_t)row * nblk + b] = -term;
-}
 
 template <bool Q3>
 __global__ __launch_bounds__(256) void k_prep_table_bf16(const uint16_t* __restrict__ x, int K,
@@ -125,17 +83,18 @@ hipError_t launch_bf16_rows_to_f32(const uint16_t* x, int rows, int K, float* ou
 }
 
 // ---------------------------------------------------------------------------
-// Group lookup shared by the GEMV kernels.
+// Work-item lookup for the dense kernel (the quantized kernel reads the same
+// fields from its own __restrict__ arguments).
 // ---------------------------------------------------------------------------
-struct GroupView {
+struct ItemView {
   int g, start, cnt;
 };
 
-__device__ __forceinline__ bool load_group(const PermRef& P, int slot, GroupView& v) {
-  if (slot >= __builtin_amdgcn_readfirstlane(*P.n_active)) return false;
-  v.g = __builtin_amdgcn_readfirstlane(P.active[slot]);
-  v.start = __builtin_amdgcn_readfirstlane(P.offsets[v.g]);
-  v.cnt = __builtin_amdgcn_readfirstlane(P.offsets[v.g + 1]) - v.start;
+__device__ __forceinline__ bool load_item(const PermRef& P, int slot, ItemView& v) {
+  if (slot >= __builtin_amdgcn_readfirstlane(*P.n_items)) return false;
+  v.g = __builtin_amdgcn_readfirstlane(P.items[3 * slot]);
+  v.start = __builtin_amdgcn_readfirstlane(P.items[3 * slot + 1]);
+  v.cnt = __builtin_amdgcn_readfirstlane(P.items[3 * slot + 2]);
   return true;
 }
 
@@ -147,71 +106,103 @@ __device__ __forceinline__ int token_of(const PermRef& P, int p) {
 }
 
 // ---------------------------------------------------------------------------
-// Quantized GEMV.  grid = (max_groups, row groups), block = W waves; wave w
-// covers a contiguous range of the 64-column chunks; tokens of the group are
-// processed TB at a time; partial sums meet in LDS in wave order.
+// Quantized GEMV.  grid = (max_groups, row groups), block = W waves; wave w owns
+// CPW consecutive 64-column chunks and issues ALL of their code / scale loads
+// before any arithmetic, so a block keeps W * CPW KB of codes per matrix in
+// flight (HBM latency is paid once, not once per chunk).  The weights stay in
+// registers while the group's tokens are processed TB at a time; partial sums
+// meet in LDS in wave order.
 // ---------------------------------------------------------------------------
-template <GemvKind KIND, bool Q3, int W, int TB>
-__global__ __launch_bounds__(W * 64) void k_gemv_quant(MatRef routed, MatRef shared, int N, int K, int inter,
-                                                       PermRef P, TableRef tab, float* __restrict__ out) {
+// Every pointer is a separate __restrict__ kernel argument: that is what lets
+// the compiler prove the activation table is never written by this kernel and
+// read it with scalar loads (s_load) instead of per-lane vector loads.
+template <GemvKind KIND, bool Q3, int W, int CPW, int TB>
+__global__ __launch_bounds__(W * 64) void k_gemv_quant(
+    const uint8_t* __restrict__ r_codes, const uint8_t* __restrict__ r_hi, const uint16_t* __restrict__ r_scales,
+    const uint8_t* __restrict__ s_codes, const uint8_t* __restrict__ s_hi, const uint16_t* __restrict__ s_scales,
+    size_t code_stride, size_t hi_stride, size_t scale_stride, int N, int K, int inter,
+    const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ items,
+    const int32_t* __restrict__ n_items, int T, int k, int E,
+    const uint32_t* __restrict__ tpairs, const float* __restrict__ tinit, float* __restrict__ out,
+    uint32_t* __restrict__ down_pairs, float* __restrict__ down_init) {
   constexpr int NMAT = KIND == GemvKind::GateUp ? 2 : 1;
   constexpr bool SPLIT = KIND == GemvKind::Down;
   constexpr int PLANES = Q3 ? 2 : 1;
   constexpr int SETS = PLANES * (SPLIT ? 2 : 1);
   __shared__ float red[W][NMAT][TB][64];
 
-  GroupView G;
-  if (!load_group(P, blockIdx.x, G)) return;
+  const int slot = blockIdx.x;
+  if (slot >= n_items[0]) return;
+  const int grp = items[3 * slot];
+  const int gstart = items[3 * slot + 1];
+  const int gcnt = items[3 * slot + 2];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const bool is_shared = G.g == P.E;
-  const MatRef& M = is_shared ? shared : routed;
-  const size_t eidx = is_shared ? 0 : (size_t)G.g;
-  const uint4* __restrict__ codes = reinterpret_cast<const uint4*>(M.codes + eidx * M.code_stride);
-  const uint32_t* __restrict__ scales = reinterpret_cast<const uint32_t*>(M.scales + eidx * M.scale_stride);
-  const uint2* __restrict__ hib = Q3 ? reinterpret_cast<const uint2*>(M.hi + eidx * M.hi_stride) : nullptr;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, provably
+  const bool is_shared = grp == E;
+  const size_t eidx = is_shared ? 0 : (size_t)grp;
+  const uint4* __restrict__ codes =
+      reinterpret_cast<const uint4*>((is_shared ? s_codes : r_codes) + eidx * code_stride);
+  const uint32_t* __restrict__ scales =
+      reinterpret_cast<const uint32_t*>((is_shared ? s_scales : r_scales) + eidx * scale_stride);
+  const uint2* __restrict__ hib =
+      Q3 ? reinterpret_cast<const uint2*>((is_shared ? s_hi : r_hi) + eidx * hi_stride) : nullptr;
 
   const int nch = K / 64, nblk = K / 32, n128 = K / 128;
   int ng[NMAT];
   ng[0] = blockIdx.y;
   if (NMAT == 2) ng[NMAT - 1] = blockIdx.y + inter / 64;
-  const int cpw = (nch + W - 1) / W;
-  const int c0 = wv * cpw, c1 = min(nch, c0 + cpw);
+  const int c0 = wv * CPW;
+
+  // ---- all weight loads of this wave first
+  uint4 w[NMAT][CPW];
+  uint32_t sc[NMAT][CPW];
+  uint2 hw[NMAT][CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    const int c = c0 + u < nch ? c0 + u : nch - 1;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const size_t tile = (size_t)ng[m] * nch + c;
+      w[m][u] = codes[tile * 64 + lane];
+      sc[m][u] = scales[(((size_t)ng[m] * n128 + (c >> 1)) * 64 + lane) * 2 + (c & 1)];
+      if (Q3) hw[m][u] = hib[tile * 64 + lane];
+    }
+  }
   const Q2Masks MQ = q2_masks();
   Q3Masks MH;
   if (Q3) MH = q3_masks();
 
-  for (int b0 = 0; b0 < G.cnt; b0 += TB) {
-    const int nb = min(TB, G.cnt - b0);
-    int rows[TB];
-#pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      const int p = G.start + b0 + (i < nb ? i : 0);
-      rows[i] = KIND == GemvKind::GateUp ? token_of(P, p) : p;
-    }
-    float acc[NMAT][TB];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int i = 0; i < TB; ++i) acc[m][i] = 0.0f;
-
-    for (int c = c0; c < c1; ++c) {
-      uint4 w[NMAT];
-      uint32_t sc[NMAT];
-      uint2 hw[NMAT];
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const size_t tile = (size_t)ng[m] * nch + c;
-        w[m] = codes[tile * 64 + lane];
-        sc[m] = scales[(((size_t)ng[m] * n128 + (c >> 1)) * 64 + lane) * 2 + (c & 1)];
-        if (Q3) hw[m] = hib[tile * 64 + lane];
+  const int Tk = T * k;
+  for (int b0 = 0; b0 < gcnt; b0 += TB) {
+    const int nb = min(TB, gcnt - b0);
+#pragma unroll 1
+    for (int i = 0; i < nb; ++i) {
+      const int p = gstart + b0 + i;
+      int row = p;
+      if (KIND == GemvKind::GateUp) {
+        const int r = sorted_rows[p];
+        row = r < Tk ? r / k : r - Tk;
       }
+      const uint32_t* __restrict__ xrow = tpairs + (size_t)row * nblk * (SETS * 16);
+      const float* __restrict__ irow = tinit + (size_t)row * nblk;
+      // Keep the code unpacking inside this loop: without this the compiler hoists
+      // the unpacked pairs of every chunk out of the token loop and spills them.
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        if (i < nb) {
-          const uint32_t* __restrict__ xp = tab.pairs + ((size_t)rows[i] * nblk + 2 * c) * (SETS * 16);
-          const float i0 = tab.init[(size_t)rows[i] * nblk + 2 * c];
-          const float i1 = tab.init[(size_t)rows[i] * nblk + 2 * c + 1];
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+          asm volatile("" : "+v"(w[m][u].x), "+v"(w[m][u].y), "+v"(w[m][u].z), "+v"(w[m][u].w));
+          if (Q3) asm volatile("" : "+v"(hw[m][u].x), "+v"(hw[m][u].y));
+        }
+      float acc[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) acc[m] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int c = c0 + u;
+        if (c < nch) {
+          const uint32_t* __restrict__ xp = xrow + (size_t)(2 * c) * (SETS * 16);
+          const float i0 = irow[2 * c], i1 = irow[2 * c + 1];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
             float a0 = i0, a1 = i1;
@@ -219,27 +210,25 @@ __global__ __launch_bounds__(W * 64) void k_gemv_quant(MatRef routed, MatRef sha
             for (int s = 0; s < (SPLIT ? 2 : 1); ++s) {
               const uint32_t* __restrict__ x0 = xp + (s * PLANES) * 16;
               const uint32_t* __restrict__ x1 = xp + SETS * 16 + (s * PLANES) * 16;
-              a0 = q2_word_dot(w[m].x, x0, a0, MQ);
-              a0 = q2_word_dot(w[m].y, x0 + 8, a0, MQ);
-              a1 = q2_word_dot(w[m].z, x1, a1, MQ);
-              a1 = q2_word_dot(w[m].w, x1 + 8, a1, MQ);
+              a0 = q2_word_dot(w[m][u].x, x0, a0, MQ);
+              a0 = q2_word_dot(w[m][u].y, x0 + 8, a0, MQ);
+              a1 = q2_word_dot(w[m][u].z, x1, a1, MQ);
+              a1 = q2_word_dot(w[m][u].w, x1 + 8, a1, MQ);
               if (Q3) {
-                a0 = q3_hi_dot(hw[m].x, x0 + 16, a0, MH);
-                a0 = q3_hi_dot(hw[m].x >> 8, x0 + 24, a0, MH);
-                a1 = q3_hi_dot(hw[m].y, x1 + 16, a1, MH);
-                a1 = q3_hi_dot(hw[m].y >> 8, x1 + 24, a1, MH);
+                a0 = q3_hi_dot(hw[m][u].x, x0 + 16, a0, MH);
+                a0 = q3_hi_dot(hw[m][u].x >> 8, x0 + 24, a0, MH);
+                a1 = q3_hi_dot(hw[m][u].y, x1 + 16, a1, MH);
+                a1 = q3_hi_dot(hw[m][u].y >> 8, x1 + 24, a1, MH);
               }
             }
-            acc[m][i] = fmaf(fp16_to_f32(sc[m] & 0xFFFFu), a0, acc[m][i]);
-            acc[m][i] = fmaf(fp16_to_f32(sc[m] >> 16), a1, acc[m][i]);
+            acc[m] = fmaf(fp16_to_f32(sc[m][u] & 0xFFFFu), a0, acc[m]);
+            acc[m] = fmaf(fp16_to_f32(sc[m][u] >> 16), a1, acc[m]);
           }
         }
       }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) red[wv][m][i][lane] = acc[m];
     }
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int i = 0; i < TB; ++i) red[wv][m][i][lane] = acc[m][i];
     __syncthreads();
     if (wv == 0) {
 #pragma unroll
@@ -252,10 +241,14 @@ __global__ __launch_bounds__(W * 64) void k_gemv_quant(MatRef routed, MatRef sha
             for (int u = 1; u < W; ++u) s += red[u][m][i][lane];
             v[m] = s;
           }
-          const size_t p = (size_t)(G.start + b0 + i);
+          const size_t p = (size_t)(gstart + b0 + i);
           if (KIND == GemvKind::GateUp) {
             const float a = v[0], b = v[NMAT - 1];
-            out[p * inter + (size_t)blockIdx.y * 64 + lane] = a / (1.0f + expf(-a)) * b;
+            const float hv = a / (1.0f + expf(-a)) * b;
+            if (down_pairs)
+              emit_down_table<Q3>(hv, (int)p, blockIdx.y, inter, down_pairs, down_init);
+            else
+              out[p * inter + (size_t)blockIdx.y * 64 + lane] = hv;
           } else {
             out[p * N + (size_t)blockIdx.y * 64 + lane] = v[0];
           }
@@ -266,31 +259,50 @@ __global__ __launch_bounds__(W * 64) void k_gemv_quant(MatRef routed, MatRef sha
   }
 }
 
-template <GemvKind KIND, bool Q3, int W>
-static void launch_quant_t(const MatRef& r, const MatRef& sh, int N, int K, int inter, const PermRef& P,
-                           int max_groups, const TableRef& tab, float* out, hipStream_t s) {
+// Launch shapes with their own register budgets: gate/up 8 waves x 5 chunks
+// (K = 2560), down 5 waves x 2 chunks (K = 640); other K use 16 waves x
+// ceil(K / 1024) chunks.
+template <GemvKind KIND, bool Q3>
+static hipError_t launch_quant_t(const MatRef& r, const MatRef& sh, int N, int K, int inter, const PermRef& P,
+                                 int max_groups, const TableRef& tab, float* out, uint32_t* dp, float* di,
+                                 hipStream_t s) {
   const int rowgroups = KIND == GemvKind::GateUp ? inter / 64 : N / 64;
-  hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, W, 4>), dim3(max_groups, rowgroups), dim3(W * 64), 0, s, r, sh, N, K,
-                     inter, P, tab, out);
+  const int nch = K / 64;
+  dim3 grid(max_groups, rowgroups);
+#define MOE_GEMV_ARGS                                                                                          \
+  r.codes, r.hi, r.scales, sh.codes, sh.hi, sh.scales, r.code_stride, r.hi_stride, r.scale_stride, N, K, inter, \
+      P.sorted_rows, P.items, P.n_items, P.T, P.k, P.E, tab.pairs, tab.init, out, dp, di
+  if (KIND == GemvKind::GateUp && nch == 40) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
+  } else if (KIND == GemvKind::Down && nch == 10) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 5, 2, 4>), grid, dim3(320), 0, s, MOE_GEMV_ARGS);
+  } else if (nch <= 16) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 1, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
+  } else if (nch <= 32) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 2, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
+  } else if (nch <= 64) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 4, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MOE_GEMV_ARGS
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_quant(GemvKind kind, int fmt, const MatRef& routed, const MatRef& shared, int N, int K,
                              int inter, const PermRef& perm, int max_groups, const TableRef& tab, float* out,
-                             hipStream_t s) {
+                             uint32_t* down_pairs, float* down_init, hipStream_t s) {
   if (max_groups <= 0) return hipSuccess;
   const bool q3 = fmt == MOE_FMT_Q3;
-  if (kind == GemvKind::GateUp) {
-    if (q3)
-      launch_quant_t<GemvKind::GateUp, true, 4>(routed, shared, N, K, inter, perm, max_groups, tab, out, s);
-    else
-      launch_quant_t<GemvKind::GateUp, false, 4>(routed, shared, N, K, inter, perm, max_groups, tab, out, s);
-  } else {
-    if (q3)
-      launch_quant_t<GemvKind::Down, true, 2>(routed, shared, N, K, inter, perm, max_groups, tab, out, s);
-    else
-      launch_quant_t<GemvKind::Down, false, 2>(routed, shared, N, K, inter, perm, max_groups, tab, out, s);
-  }
-  return hipGetLastError();
+  if (kind == GemvKind::GateUp)
+    return q3 ? launch_quant_t<GemvKind::GateUp, true>(routed, shared, N, K, inter, perm, max_groups, tab, out,
+                                                       down_pairs, down_init, s)
+              : launch_quant_t<GemvKind::GateUp, false>(routed, shared, N, K, inter, perm, max_groups, tab, out,
+                                                        down_pairs, down_init, s);
+  return q3 ? launch_quant_t<GemvKind::Down, true>(routed, shared, N, K, inter, perm, max_groups, tab, out,
+                                                   nullptr, nullptr, s)
+            : launch_quant_t<GemvKind::Down, false>(routed, shared, N, K, inter, perm, max_groups, tab, out,
+                                                    nullptr, nullptr, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -303,8 +315,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_dense(MatRef routed, MatRef sha
                                                        float* __restrict__ out) {
   constexpr int NMAT = KIND == GemvKind::GateUp ? 2 : 1;
   __shared__ float red[W][NMAT][64];
-  GroupView G;
-  if (!load_group(P, blockIdx.x, G)) return;
+  ItemView G;
+  if (!load_item(P, blockIdx.x, G)) return;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const bool is_shared = G.g == P.E;
   const MatRef& M = is_shared ? shared : routed;

@@ -43,12 +43,15 @@ inline MatRef mat_w2(const moe_bank_t& b) {
   return m;
 }
 
-// Groups of a permutation: group g < E is routed expert g, group E the shared expert.
+// Groups of a permutation: group g < E is routed expert g, group E the shared
+// expert.  The GEMV kernels walk "work items": (group, first sorted position,
+// count <= items_per) triples covering every entry of every non-empty group,
+// groups ascending, so a group with many tokens is spread over several blocks.
 struct PermRef {
   const int32_t* offsets = nullptr;      // [E + 2]
   const int32_t* sorted_rows = nullptr;  // [n]
-  const int32_t* active = nullptr;       // non-empty groups, ascending [<= E + 1]
-  const int32_t* n_active = nullptr;     // device scalar
+  const int32_t* items = nullptr;        // [max_items][3]: group, start, count
+  const int32_t* n_items = nullptr;      // device scalar
   int32_t T = 0, k = 0, E = 0;
 };
 
@@ -62,6 +65,28 @@ struct TableRef {
 
 enum class GemvKind { GateUp, Down };
 
+// Decode front end (router + activation table + top-k + small permutation), one launch.
+struct SmallRouteArgs {
+  const uint16_t* x;
+  int T, E, H, k, with_shared, q3;
+  const uint16_t* wr;
+  const float* bias;
+  float* logits;
+  uint32_t* xpairs;    // activation table (NULL: not built)
+  float* xinit;
+  int32_t* ids;
+  float* gates;
+  float* margin;       // may be NULL
+  int32_t* offsets;
+  int32_t* sorted_rows;
+  int32_t* row_to_sorted;
+  int32_t* items;       // work items [n][3]
+  int32_t* n_items;
+  int items_per;        // entries per work item
+};
+// Largest T * k (+ T) the decode front end sorts in one block.
+static constexpr int kSmallRouteMaxEntries = 1024;
+
 // ---- launchers (return hipGetLastError()) ----
 hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s);
 
@@ -69,16 +94,18 @@ hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, cons
                               float* logits, hipStream_t s);
 hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s);
+hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
                        hipStream_t s);
 
-// permutation: counts/base are [n_chunks][E + 2] int32 scratch; active/n_active outputs
+// permutation: counts/base are [n_chunks][E + 2] int32 scratch
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
-                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* active, int32_t* n_active,
-                          int32_t* counts, int32_t* base, hipStream_t s);
+                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
+                          hipStream_t s);
 int permute_chunks(int n_entries);
-hipError_t launch_active_from_offsets(const int32_t* offsets, int E, int32_t* active, int32_t* n_active,
-                                      hipStream_t s);
+// work items of a permutation (see PermRef), from its offsets
+hipError_t launch_items_from_offsets(const int32_t* offsets, int E, int items_per, int32_t* items,
+                                     int32_t* n_items, hipStream_t s);
 
 // activation tables
 hipError_t launch_prep_table_bf16(const uint16_t* x, int rows, int K, bool q3, uint32_t* pairs, float* init,
@@ -88,9 +115,11 @@ hipError_t launch_prep_table_f32(const float* h, int rows, int K, bool q3, uint3
 hipError_t launch_bf16_rows_to_f32(const uint16_t* x, int rows, int K, float* out, hipStream_t s);
 
 // dequant GEMV over the groups of a permutation
+// GateUp: writes h = SiLU(gate) * up either as fp32 rows into ``out`` or, when
+// down_pairs is set, directly as the down projection's activation table.
 hipError_t launch_gemv_quant(GemvKind kind, int fmt, const MatRef& routed, const MatRef& shared, int N, int K,
                              int inter, const PermRef& perm, int max_groups, const TableRef& tab, float* out,
-                             hipStream_t s);
+                             uint32_t* down_pairs, float* down_init, hipStream_t s);
 hipError_t launch_gemv_dense(GemvKind kind, const MatRef& routed, const MatRef& shared, int N, int K, int inter,
                              const PermRef& perm, int max_groups, const float* in_rows, float* out,
                              hipStream_t s);

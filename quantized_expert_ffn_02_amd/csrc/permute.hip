@@ -61,11 +61,9 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return base + incl - v;
 }
 
-// One block of 1024 threads, thread g = group: totals, offsets, per-chunk bases,
-// and the ascending list of non-empty groups.
+// One block of 1024 threads, thread g = group: totals, offsets and per-chunk bases.
 __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
-                                                    int32_t* __restrict__ base, int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+                                                    int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
   const int G = E + 1;
   const int g = threadIdx.x;
   int tot = 0;
@@ -73,8 +71,6 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
     for (int c = 0; c < n_chunks; ++c) tot += counts[(size_t)c * G + g];
   int n_all = 0;
   const int off = block_exclusive_scan_1024(g < G ? tot : 0, &n_all);
-  int n_act = 0;
-  const int apos = block_exclusive_scan_1024(g < G && tot > 0 ? 1 : 0, &n_act);
   if (g < G) {
     offsets[g] = off;
     int run = off;
@@ -82,12 +78,8 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
       base[(size_t)c * G + g] = run;
       run += counts[(size_t)c * G + g];
     }
-    if (tot > 0) active[apos] = g;
   }
-  if (g == 0) {
-    offsets[G] = n_all;
-    *n_active = n_act;
-  }
+  if (g == 0) offsets[G] = n_all;
 }
 
 // One wave per chunk: entries in ascending r, 64 at a time; the rank of an
@@ -134,33 +126,40 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
-                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* active, int32_t* n_active,
-                          int32_t* counts, int32_t* base, hipStream_t s) {
+                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
+                          hipStream_t s) {
   const int Tk = T * k;
   const int n = Tk + (with_shared ? T : 0);
   const int nc = permute_chunks(n);
   hipLaunchKernelGGL(k_perm_hist, dim3(nc), dim3(256), 0, s, ids, Tk, n, E, counts);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets, active, n_active);
+  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets);
   hipLaunchKernelGGL(k_perm_scatter, dim3(nc), dim3(64), 0, s, ids, Tk, n, E, base, sorted_rows, row_to_sorted);
   return hipGetLastError();
 }
 
-// Non-empty groups of an existing offsets array (for callers that permuted themselves).
-__global__ __launch_bounds__(1024) void k_active_from_offsets(const int32_t* __restrict__ offsets, int E,
-                                                              int32_t* __restrict__ active,
-                                                              int32_t* __restrict__ n_active) {
+// Work items from offsets: group g yields ceil(count / items_per) items, placed
+// after the items of every lower group.
+__global__ __launch_bounds__(1024) void k_items_from_offsets(const int32_t* __restrict__ offsets, int E,
+                                                             int items_per, int32_t* __restrict__ items,
+                                                             int32_t* __restrict__ n_items) {
   const int G = E + 1;
   const int g = threadIdx.x;
-  const bool ne = g < G && offsets[g + 1] > offsets[g];
-  int n_act = 0;
-  const int pos = block_exclusive_scan_1024(ne ? 1 : 0, &n_act);
-  if (ne) active[pos] = g;
-  if (g == 0) *n_active = n_act;
+  const int start = g < G ? offsets[g] : 0;
+  const int cnt = g < G ? offsets[g + 1] - start : 0;
+  const int ni = (cnt + items_per - 1) / items_per;
+  int total = 0;
+  const int pos = block_exclusive_scan_1024(ni, &total);
+  for (int i = 0; i < ni; ++i) {
+    items[(size_t)(pos + i) * 3 + 0] = g;
+    items[(size_t)(pos + i) * 3 + 1] = start + i * items_per;
+    items[(size_t)(pos + i) * 3 + 2] = min(items_per, cnt - i * items_per);
+  }
+  if (g == 0) *n_items = total;
 }
 
-hipError_t launch_active_from_offsets(const int32_t* offsets, int E, int32_t* active, int32_t* n_active,
-                                      hipStream_t s) {
-  hipLaunchKernelGGL(k_active_from_offsets, dim3(1), dim3(1024), 0, s, offsets, E, active, n_active);
+hipError_t launch_items_from_offsets(const int32_t* offsets, int E, int items_per, int32_t* items,
+                                     int32_t* n_items, hipStream_t s) {
+  hipLaunchKernelGGL(k_items_from_offsets, dim3(1), dim3(1024), 0, s, offsets, E, items_per, items, n_items);
   return hipGetLastError();
 }
 

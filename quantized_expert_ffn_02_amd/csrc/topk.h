@@ -1,0 +1,107 @@
+// Wave64 top-k selection over one token's router logits.
+//
+// Order: logit descending, expert index ascending (so exactly equal logits go to
+// the lower index).  Each lane holds VPL logits (experts lane + 64 j), sorted once
+// per lane; then k + 1 rounds of a wave arg-max over the lanes' heads pick the
+// experts in order and the (k+1)-th logit for the margin.  The arg-max compares
+// one 64-bit key per lane with DPP moves (four steps inside each 16-lane row, two
+// row broadcasts across rows) and reads the winner from lane 63, instead of
+// LDS-routed shuffles.
+#pragma once
+
+#include <math.h>
+
+#include "device.h"
+
+namespace moe {
+
+// Total order as one 64-bit key: order-preserving bits of the logit in the
+// high word, the complement of the expert index in the low word, so the
+// largest key is the largest logit with the lowest index.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(~e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float(ord ^ ((ord >> 31) ? 0x80000000u : 0xFFFFFFFFu));
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t key) {
+  const int lo = (int)(uint32_t)key, hi = (int)(uint32_t)(key >> 32);
+  // rows outside ROW_MASK and lanes without a source keep their own key
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > key ? o : key;
+}
+
+// Wave-uniform maximum key over the 64 lanes.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+  key = dpp_max_step<0xB1, 0xF>(key);    // quad_perm [1,0,3,2]
+  key = dpp_max_step<0x4E, 0xF>(key);    // quad_perm [2,3,0,1]
+  key = dpp_max_step<0x124, 0xF>(key);   // row_ror:4
+  key = dpp_max_step<0x128, 0xF>(key);   // row_ror:8  -> every lane holds its row's max
+  key = dpp_max_step<0x142, 0xA>(key);   // row_bcast:15 -> rows 1, 3 include rows 0, 2
+  key = dpp_max_step<0x143, 0xC>(key);   // row_bcast:31 -> rows 2, 3 include row 1 (lane 63 = all)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Top-k of one token: logits row [E] -> ids[k], gates[k], margin.
+// Lanes < k end up holding (my_e, gate); the function writes the outputs itself.
+template <int VPL>
+__device__ void wave_topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
+                              float* __restrict__ gates_out, float* __restrict__ margin_out,
+                              int32_t* __restrict__ ids_lds = nullptr) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? topk_key(row[e], e) : 0ull;   // 0 sorts below every real key
+  }
+  // per-lane descending sort of the VPL keys
+#pragma unroll
+  for (int a = 1; a < VPL; ++a)
+#pragma unroll
+    for (int b = a; b > 0; --b)
+      if (key[b] > key[b - 1]) {
+        const uint64_t t = key[b];
+        key[b] = key[b - 1];
+        key[b - 1] = t;
+      }
+  uint64_t mine = 0, last = 0, next = 0;
+  const int rounds = k < E ? k + 1 : k;
+  for (int r = 0; r < rounds; ++r) {
+    const uint64_t best = wave_max_key(key[0]);
+    if (r < k) {
+      if (lane == r) mine = best;
+      last = best;
+      if (key[0] == best) {   // the lane holding it pops its head
+#pragma unroll
+        for (int j = 0; j + 1 < VPL; ++j) key[j] = key[j + 1];
+        key[VPL - 1] = 0ull;
+      }
+    } else {
+      next = best;
+    }
+  }
+  const float my_v = key_value(mine);
+  const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+  const float ex = lane < k ? expf(my_v - top) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    const int my_e = key_index(mine);
+    ids_out[lane] = my_e;
+    gates_out[lane] = ex / sum;
+    if (ids_lds) ids_lds[lane] = my_e;
+  }
+  if (margin_out && lane == 0) *margin_out = k < E ? key_value(last) - key_value(next) : INFINITY;
+}
+
+}  // namespace moe

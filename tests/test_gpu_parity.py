@@ -149,7 +149,8 @@ def run_layer(d, x, T, residual=None):
     return host(out), host(out_bf), host(ids), host(gates), host(margin), ws
 
 
-@pytest.mark.parametrize("workload,T", [("tiny", 4), ("decode", 1), ("decode", 4)])
+@pytest.mark.parametrize("workload,T", [("tiny", 4), ("decode", 1), ("decode", 4), ("decode", 64),
+                                        ("decode", 100)])
 def test_layer_forward_parity(workload, T):
     hl = W.host_layer(workload)
     x, _ = W.activations_with_margin(hl, T)
@@ -160,6 +161,7 @@ def test_layer_forward_parity(workload, T):
     err = OL.rel_max_err(out, ref)
     print(f"{workload} T={T}: max|err|/rms = {err:.3e}")
     assert err <= OUT_TOL
+    np.testing.assert_allclose(margin, m_r, rtol=0, atol=1e-5)
     # bf16 copy = RNE of the fp32 output
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
 

@@ -66,6 +66,75 @@ def cpu_baseline(hl_args, T, seconds):
                       f"demand), {el:.1f} s"}
 
 
+def bench_prefill(steps):
+    """One 8,192-token prefill chunk of a real-shape 2-bit layer with Zipf(1.1)-skewed routing."""
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+    wl = synth.CONFIGS["prefill"]
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    T = wl.tokens[0]
+    wr = synth.router_weight(wl.seed, 0, E, H)
+    bias = synth.zipf_bias(wl.seed, 0, E, s.zipf)
+    rb = DeviceBank(s.fmt, E, H, I, synth.bank(wl.seed, 0, s.fmt, range(E), H, I, workers=16))
+    sb = DeviceBank(s.fmt, 1, H, I, synth.bank(wl.seed, 0, s.fmt, [E], H, I))
+    layer = DeviceLayer(H, E, k, I, wr, bias, rb, sb)
+    xs = [to_device(synth.activations(wl.seed + 9000, j, T, H)) for j in range(2)]
+    ws = layer.workspace(T)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    for i in range(3):
+        B.layer_forward(layer.struct, xs[i % 2], T, out, ws, topk_ids=ids)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        B.layer_forward(layer.struct, xs[i % 2], T, out, ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kev = {}
+    for kern in (B.KERNEL_ROUTER, B.KERNEL_GATEUP_GEMM, B.KERNEL_DOWN_GEMM, B.KERNEL_GATEUP_GEMV,
+                 B.KERNEL_DOWN_GEMV):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            b.record()
+        kev[kern] = evs
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for kern, evs in kev.items():
+            B.time_next_launch(kern, evs[i][0].cuda_event, evs[i][1].cuda_event)
+        B.layer_forward(layer.struct, xs[i % 2], T, out, ws, topk_ids=ids)
+    torch.cuda.synchronize()
+    kms = {kern: float(np.mean([a.elapsed_time(b) for a, b in evs])) for kern, evs in kev.items()}
+    ids_h = ids.cpu().numpy()
+    counts = np.bincount(ids_h.reshape(-1), minlength=E)
+    # algorithmic FLOPs: router 2*T*H*E + every (token, expert) pair incl. the shared one: 6*H*I each
+    flops = 2.0 * T * H * E + T * (k + 1) * 6.0 * H * I
+    big = counts >= 32
+    gemm_rows = int(counts[big].sum()) + T        # shared expert rows all go to the GEMM
+    gemm_flops_gu = gemm_rows * 4.0 * H * I
+    gemm_flops_dn = gemm_rows * 2.0 * H * I
+    return {
+        "workload": f"prefill: one 8,192-token chunk, real-shape 2-bit layer, Zipf(1.1) routing",
+        "tokens": T, "layer_ms": ms, "tokens_per_s": T / (ms * 1e-3),
+        "TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "mfma_frac_of_fp16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "algorithmic_GFLOP": flops / 1e9,
+        "experts_on_gemm": int(big.sum()), "experts_empty": int((counts == 0).sum()),
+        "kernel_us": {"router": kms[B.KERNEL_ROUTER] * 1e3, "gateup_gemm": kms[B.KERNEL_GATEUP_GEMM] * 1e3,
+                      "down_gemm": kms[B.KERNEL_DOWN_GEMM] * 1e3, "gateup_gemv": kms[B.KERNEL_GATEUP_GEMV] * 1e3,
+                      "down_gemv": kms[B.KERNEL_DOWN_GEMV] * 1e3},
+        "gateup_gemm_TFLOPs": gemm_flops_gu / (kms[B.KERNEL_GATEUP_GEMM] * 1e-3) / 1e12,
+        "down_gemm_TFLOPs": gemm_flops_dn / (kms[B.KERNEL_DOWN_GEMM] * 1e-3) / 1e12,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +145,8 @@ def main():
     ap.add_argument("--pool", type=int, default=64, help="distinct token batches cycled through")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -205,6 +276,8 @@ def main():
             "avg_launch_us": gu_ms * 1e3,
         },
     }
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(args.prefill_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host0, T, args.cpu_seconds)
         result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]

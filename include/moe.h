@@ -161,10 +161,19 @@ int moe_layer_forward(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
                       float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates,
                       float* margin, void* ws, size_t ws_bytes, void* stream);
 
+/* Parameter-free RMSNorm of each bf16 row: out = bf16(x / sqrt(mean(x^2) + eps)),
+ * rounded to nearest even, fp32 arithmetic; x, out bf16 [T x H] (may not overlap). */
+#define MOE_RMS_EPS 1e-6f
+int moe_rmsnorm_bf16(const uint16_t* x, int32_t T, int32_t H, uint16_t* out, void* stream);
+
 /* A stack of n_layers layers joined by residual adds (48 layers in the model, first
- * page, section "What it is"): x_{l+1} = bf16(x_l + MoE_l(x_l)).  x0 bf16 [T x H];
- * x_out bf16 [T x H] = x_{n_layers}; out_last (optional) fp32 [T x H] = the last
- * layer's fp32 x + MoE(x).  ``layers`` is a host array of n_layers layer structs. */
+ * page, section "What it is"), each layer reading the RMS-normalised stream:
+ *   x_{l+1} = bf16(x_l + MoE_l(RMSNorm(x_l)))
+ * (the pages do not describe the normalisation around the MoE block; without one
+ * a residual chain of random-weight SwiGLU experts diverges).  x0 bf16 [T x H];
+ * x_out bf16 [T x H] = x_{n_layers} (must not overlap x0); out_last (optional)
+ * fp32 [T x H] = the last layer's fp32 x + MoE(RMSNorm(x)).  ``layers`` is a host
+ * array of n_layers layer structs. */
 int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_t* x0, int32_t T,
                       uint16_t* x_out, float* out_last, void* ws, size_t ws_bytes, void* stream);
 

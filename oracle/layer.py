@@ -189,6 +189,26 @@ def residual_bf16(x_bits, out):
     return f64_to_bf16_bits(bf16_to_f64(x_bits) + out)
 
 
+RMS_EPS = 1e-6
+
+
+def rms_norm_bf16(x_bits, eps=RMS_EPS):
+    """Parameter-free RMSNorm of each token row, rounded to bf16:
+    x / sqrt(mean(x^2) + eps).  The MoE input of every layer of a stack (the
+    pages describe 48 layers but not the normalisation around the MoE block;
+    without one the residual stream of random-weight SwiGLU experts diverges)."""
+    x = bf16_to_f64(x_bits)
+    r = np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    return f64_to_bf16_bits(x / r)
+
+
+def stack_step(x_bits, layer_fn):
+    """One layer of a stack: x_{l+1} = bf16(x_l + MoE_l(RMSNorm(x_l))).
+    layer_fn(xn_bits) returns the layer's MoE output (float64 [T, H])."""
+    xn = rms_norm_bf16(x_bits)
+    return residual_bf16(x_bits, layer_fn(xn)), xn
+
+
 # ---------------------------------------------------------------- expert cache [A "How a 125B model fits", C]
 
 def cached_layer_forward(x_bits, wr_bits, k, slot_row, slot_fn, shared_fn=None, bias=None):

@@ -51,6 +51,7 @@ _SIGS = {
     "moe_layer_forward_cached": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank), _vp,
                                                 _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_time_next_launch": (ctypes.c_int, [_i32, _vp, _vp]),
+    "moe_rmsnorm_bf16": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -182,3 +183,7 @@ def layer_forward_cached(layer, layer_idx, n_layers, slot_of, slot_pool, x, T, o
 def time_next_launch(kernel, start_event, stop_event):
     """Arm hipEvent_t handles (ints) around the next launch of ``kernel``."""
     _check("moe_time_next_launch", lib().moe_time_next_launch(int(kernel), start_event, stop_event))
+
+
+def rmsnorm_bf16(x, T, H, out, stream=None):
+    _check("moe_rmsnorm_bf16", lib().moe_rmsnorm_bf16(ptr(x), int(T), int(H), ptr(out), _stream(stream)))

@@ -55,9 +55,9 @@ bool has_shared(const moe_layer_t* L) { return L->shared.fmt != MOE_FMT_NONE; }
 struct Layout {
   size_t logits, ids, gates, margin;
   size_t counts, base, offsets, sorted_rows, row_to_sorted, items, n_items;
-  size_t xtab_pairs, xtab_init, xf32;
+  size_t xtab_pairs, xtab_init, xf32, xf16, hf16, tiles, n_tiles;
   size_t h, htab_pairs, htab_init, y;
-  size_t out_f32, xa, xb;     // stack ping-pong buffers
+  size_t out_f32, xa, xb, xn;     // stack ping-pong buffers and the normalised layer input
   size_t miss_flag;
   size_t total;
 };
@@ -89,6 +89,10 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xtab_pairs = take(dense ? 0 : T * (H / 32) * planes * 16 * 4);
   o.xtab_init = take(dense ? 0 : T * (H / 32) * 4);
   o.xf32 = take(dense ? T * H * 4 : 0);
+  o.xf16 = take(dense ? 0 : T * H * 2);
+  o.hf16 = take(dense ? 0 : n * I * 2);
+  o.tiles = take((n / 128 + E + 2) * 3 * 4);
+  o.n_tiles = take(4);
   o.h = take(n * I * 4);
   o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
   o.htab_init = take(dense ? 0 : n * (I / 32) * 4);
@@ -96,6 +100,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.out_f32 = take(T * H * 4);
   o.xa = take(T * H * 2);
   o.xb = take(T * H * 2);
+  o.xn = take(T * H * 2);
   o.miss_flag = take(T * k * 4);
   o.total = p;
   return o;
@@ -144,11 +149,16 @@ hipError_t timed(int kernel, hipStream_t s, F&& launch) {
 
 // ---- steps shared by the public calls (arguments already validated) ----
 
+int items_per_for(int T);
+bool use_gemm_path(int n_entries);
+int mfma_min_rows(int T);
+
 int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float* gates, float* margin, void* ws,
              const Layout& lay, hipStream_t s) {
   float* logits = at<float>(ws, lay.logits);
   MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] {
-    return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+    return T >= 64 ? launch_router_mfma(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s)
+                   : launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
   }));
   MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
   return MOE_OK;
@@ -156,11 +166,17 @@ int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float
 
 int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef& perm, int n_entries,
                   float* y_sorted, void* ws, const Layout& lay, hipStream_t s, bool x_table_ready = false,
+                  const int32_t* gemm_tiles = nullptr, const int32_t* n_gemm_tiles = nullptr,
                   const moe_bank_t* routed_override = nullptr) {
   const moe_bank_t& rb = routed_override ? *routed_override : L->routed;
   const int H = L->hidden, I = L->inter, E = L->n_experts;
-  (void)E;
-  const int max_groups = n_entries;   // upper bound on work items
+  // upper bound on GEMV work items: every entry, or, when the MFMA GEMM takes
+  // the groups of min_rows or more entries, the items of the smaller groups
+  int max_groups = n_entries;
+  if (gemm_tiles) {
+    const int mr = mfma_min_rows(T), ip = items_per_for(T);
+    max_groups = std::min(n_entries, (E + 1) * ((mr - 1 + ip - 1) / ip));
+  }
   const MatRef r13 = mat_w13(rb), r2 = mat_w2(rb);
   const MatRef s13 = has_shared(L) ? mat_w13(L->shared) : MatRef(), s2 = has_shared(L) ? mat_w2(L->shared) : MatRef();
   float* h = at<float>(ws, lay.h);
@@ -182,10 +198,28 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
   ht.pairs = at<uint32_t>(ws, lay.htab_pairs);
   ht.init = at<float>(ws, lay.htab_init);
   ht.sets = (q3 ? 2 : 1) * 2;
+  // groups with many entries: MFMA grouped GEMM (2-bit banks)
+  const bool gemm = gemm_tiles && !q3;
+  const int max_tiles = gemm ? n_entries / gemm_tile_rows() + E + 2 : 0;
+  uint16_t* hf = at<uint16_t>(ws, lay.hf16);
+  if (gemm) {
+    uint16_t* xf = at<uint16_t>(ws, lay.xf16);
+    MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
+    MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
+      return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles,
+                            perm.sorted_rows, T, perm.k, xf, hf, s);
+    }));
+  }
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] {
     return launch_gemv_quant(GemvKind::GateUp, rb.fmt, r13, s13, 2 * I, H, I, perm, max_groups, xt, h,
                              const_cast<uint32_t*>(ht.pairs), const_cast<float*>(ht.init), s);
   }));
+  if (gemm) {
+    MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
+      return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles, nullptr, T,
+                            perm.k, hf, y_sorted, s);
+    }));
+  }
   MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] {
     return launch_gemv_quant(GemvKind::Down, rb.fmt, r2, s2, H, I, I, perm, max_groups, ht, y_sorted, nullptr,
                              nullptr, s);
@@ -197,9 +231,21 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
 // (most parallel), four for larger batches.
 int items_per_for(int T) { return T <= 16 ? 1 : 4; }
 
+// Groups with at least this many entries go to the MFMA grouped GEMM (only for
+// batches beyond the decode front end's size); smaller groups use the GEMV.
+constexpr int kMfmaMinRows = 32;
+// For a prompt-sized chunk every non-empty group goes to the GEMM.
+int mfma_min_rows(int T) { return T >= 1024 ? 1 : kMfmaMinRows; }
+bool use_gemm_path(int n_entries) { return n_entries > kSmallRouteMaxEntries; }
+
 }  // namespace
 
 extern "C" {
+
+int moe_rmsnorm_bf16(const uint16_t* x, int32_t T, int32_t H, uint16_t* out, void* stream) {
+  if (!x || !out || T <= 0 || H <= 0) return MOE_EINVAL;
+  return hip_rc(launch_rmsnorm_bf16(x, T, H, MOE_RMS_EPS, out, (hipStream_t)stream));
+}
 
 int moe_time_next_launch(int32_t kernel, void* start_event, void* stop_event) {
   if (kernel < 0 || kernel >= MOE_KERNEL_COUNT) return MOE_EINVAL;
@@ -275,10 +321,14 @@ int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
   perm.T = T;
   perm.k = L->top_k;
   perm.E = L->n_experts;
-  MOE_TRY(launch_items_from_offsets(offsets, L->n_experts, items_per_for(T), const_cast<int32_t*>(perm.items),
-                                    const_cast<int32_t*>(perm.n_items), s));
   const int n = T * L->top_k + (has_shared(L) ? T : 0);
-  return do_expert_ffn(L, x, T, perm, n, y_sorted, ws, lay, s);
+  const bool gemm = use_gemm_path(n) && L->routed.fmt == MOE_FMT_Q2;
+  int32_t* tiles = at<int32_t>(ws, lay.tiles);
+  int32_t* n_tiles = at<int32_t>(ws, lay.n_tiles);
+  MOE_TRY(launch_plan(offsets, L->n_experts, gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T), tiles, n_tiles,
+                      const_cast<int32_t*>(perm.items), const_cast<int32_t*>(perm.n_items), s));
+  return do_expert_ffn(L, x, T, perm, n, y_sorted, ws, lay, s, false, gemm ? tiles : nullptr,
+                       gemm ? n_tiles : nullptr);
 }
 
 int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* topk_gates, int32_t T, int32_t k,
@@ -304,7 +354,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   int32_t* items = at<int32_t>(ws, lay.items);
   int32_t* n_items = at<int32_t>(ws, lay.n_items);
   const bool quant = L->routed.fmt != MOE_FMT_BF16;
-  bool x_table_ready = false;
+  bool x_table_ready = false, gemm = false;
   if (n <= kSmallRouteMaxEntries) {
     // decode / MTP-verify batch: router, activation table, top-k and permutation in one launch
     SmallRouteArgs a;
@@ -336,7 +386,9 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     if (rc) return rc;
     MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
                            at<int32_t>(ws, lay.base), s));
-    MOE_TRY(launch_items_from_offsets(offsets, E, items_per_for(T), items, n_items, s));
+    gemm = quant && L->routed.fmt == MOE_FMT_Q2;
+    MOE_TRY(launch_plan(offsets, E, gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T), at<int32_t>(ws, lay.tiles),
+                        at<int32_t>(ws, lay.n_tiles), items, n_items, s));
   }
   PermRef perm;
   perm.offsets = offsets;
@@ -347,7 +399,8 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   perm.k = k;
   perm.E = E;
   float* y = at<float>(ws, lay.y);
-  int rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s, x_table_ready);
+  int rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s, x_table_ready, gemm ? at<int32_t>(ws, lay.tiles) : nullptr,
+                         gemm ? at<int32_t>(ws, lay.n_tiles) : nullptr);
   if (rc) return rc;
   MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
   return MOE_OK;
@@ -382,7 +435,9 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
     const Layout lay = make_layout(&layers[l], T);
     uint16_t* nxt = (l == n_layers - 1) ? x_out : at<uint16_t>(ws, (l % 2) ? lay.xb : lay.xa);
     float* of = (l == n_layers - 1 && out_last) ? out_last : at<float>(ws, lay.out_f32);
-    rc = layer_forward_impl(&layers[l], cur, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s);
+    uint16_t* xn = at<uint16_t>(ws, lay.xn);
+    MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
+    rc = layer_forward_impl(&layers[l], xn, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s);
     if (rc) return rc;
     cur = nxt;
   }
@@ -393,9 +448,82 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                              const moe_bank_t* slot_pool, const uint16_t* x, int32_t T, float* out,
                              int32_t* topk_ids, float* topk_gates, int32_t* miss_rows, int32_t* n_miss, void* ws,
                              size_t ws_bytes, void* stream) {
-  (void)L; (void)layer_idx; (void)n_layers; (void)slot_of; (void)slot_pool; (void)x; (void)T; (void)out;
-  (void)topk_ids; (void)topk_gates; (void)miss_rows; (void)n_miss; (void)ws; (void)ws_bytes; (void)stream;
-  return MOE_EUNSUPPORTED;
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (!L->w_router || !slot_of || !slot_pool || !x || !out || !miss_rows || !n_miss || T <= 0) return MOE_EINVAL;
+  if (n_layers < 1 || layer_idx < 0 || layer_idx >= n_layers) return MOE_EINVAL;
+  if ((rc = check_bank(*slot_pool, 1, L->hidden, L->inter))) return rc;
+  if (slot_pool->fmt == MOE_FMT_BF16) return MOE_EUNSUPPORTED;
+  if (L->shared.fmt != MOE_FMT_NONE) {
+    if ((rc = check_bank(L->shared, 1, L->hidden, L->inter))) return rc;
+    if (L->shared.fmt != slot_pool->fmt) return MOE_EUNSUPPORTED;
+  }
+  // the slot pool stands in for the routed bank (same format and expert shape)
+  moe_layer_t Lc = *L;
+  Lc.routed = *slot_pool;
+  Lc.routed.n_experts = L->n_experts;
+  const Layout lay = make_layout(&Lc, T);
+  if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = L->top_k, E = L->n_experts;
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
+  float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
+  const int with_shared = has_shared(L) ? 1 : 0;
+  const int n = T * k + (with_shared ? T : 0);
+  int32_t* offsets = at<int32_t>(ws, lay.offsets);
+  int32_t* srt = at<int32_t>(ws, lay.sorted_rows);
+  int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
+  int32_t* items = at<int32_t>(ws, lay.items);
+  int32_t* n_items = at<int32_t>(ws, lay.n_items);
+  bool x_table_ready = false;
+  if (n <= kSmallRouteMaxEntries) {
+    SmallRouteArgs a;
+    a.x = x;
+    a.T = T;
+    a.E = E;
+    a.H = L->hidden;
+    a.k = k;
+    a.with_shared = with_shared;
+    a.q3 = slot_pool->fmt == MOE_FMT_Q3;
+    a.wr = L->w_router;
+    a.bias = L->router_bias;
+    a.logits = at<float>(ws, lay.logits);
+    a.xpairs = at<uint32_t>(ws, lay.xtab_pairs);
+    a.xinit = at<float>(ws, lay.xtab_init);
+    a.ids = ids;
+    a.gates = gates;
+    a.margin = nullptr;
+    a.offsets = offsets;
+    a.sorted_rows = srt;
+    a.row_to_sorted = inv;
+    a.items = items;
+    a.n_items = n_items;
+    a.items_per = items_per_for(T);
+    MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_small(a, s); }));
+    x_table_ready = true;
+  } else {
+    rc = do_route(L, x, T, ids, gates, nullptr, ws, lay, s);
+    if (rc) return rc;
+    MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                           at<int32_t>(ws, lay.base), s));
+    MOE_TRY(launch_plan(offsets, E, 0x7FFFFFFF, items_per_for(T), at<int32_t>(ws, lay.tiles),
+                        at<int32_t>(ws, lay.n_tiles), items, n_items, s));
+  }
+  PermRef perm;
+  perm.offsets = offsets;
+  perm.sorted_rows = srt;
+  perm.items = items;
+  perm.n_items = n_items;
+  perm.slot_map = slot_of + (size_t)layer_idx * E;
+  perm.T = T;
+  perm.k = k;
+  perm.E = E;
+  float* y = at<float>(ws, lay.y);
+  rc = do_expert_ffn(&Lc, x, T, perm, n, y, ws, lay, s, x_table_ready);
+  if (rc) return rc;
+  MOE_TRY(launch_miss_list(ids, T * k, perm.slot_map, miss_rows, n_miss, s));
+  MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, nullptr, out, nullptr, s));
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -64,6 +64,32 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, c
   return hipGetLastError();
 }
 
+// Parameter-free RMSNorm of each bf16 row: bf16(x / sqrt(mean(x^2) + eps)), one
+// block per row, fixed-order fp32 reduction (the input of every layer of a stack).
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const uint16_t* __restrict__ x, int H, float eps,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* __restrict__ xr = x + (size_t)row * H;
+  float ss = 0.0f;
+  for (int h = tid; h < H; h += 256) {
+    const float v = bf16_to_f32(xr[h]);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  for (int h = tid; h < H; h += 256) out[(size_t)row * H + h] = f32_to_bf16_rne(bf16_to_f32(xr[h]) * inv);
+}
+
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(T), dim3(256), 0, s, x, H, eps, out);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
 }

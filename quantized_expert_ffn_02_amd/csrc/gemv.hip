@@ -124,22 +124,31 @@ __global__ __launch_bounds__(W * 64) void k_gemv_quant(
     const int32_t* __restrict__ sorted_rows, const int32_t* __restrict__ items,
     const int32_t* __restrict__ n_items, int T, int k, int E,
     const uint32_t* __restrict__ tpairs, const float* __restrict__ tinit, float* __restrict__ out,
-    uint32_t* __restrict__ down_pairs, float* __restrict__ down_init) {
+    uint32_t* __restrict__ down_pairs, float* __restrict__ down_init, const int32_t* __restrict__ slot_map) {
   constexpr int NMAT = KIND == GemvKind::GateUp ? 2 : 1;
   constexpr bool SPLIT = KIND == GemvKind::Down;
   constexpr int PLANES = Q3 ? 2 : 1;
   constexpr int SETS = PLANES * (SPLIT ? 2 : 1);
   __shared__ float red[W][NMAT][TB][64];
 
-  const int slot = blockIdx.x;
-  if (slot >= n_items[0]) return;
-  const int grp = items[3 * slot];
-  const int gstart = items[3 * slot + 1];
-  const int gcnt = items[3 * slot + 2];
+  const int item = blockIdx.x;
+  if (item >= n_items[0]) return;
+  const int grp = items[3 * item];
+  const int gstart = items[3 * item + 1];
+  const int gcnt = items[3 * item + 2];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, provably
   const bool is_shared = grp == E;
-  const size_t eidx = is_shared ? 0 : (size_t)grp;
+  // expert-cache mode: routed expert grp lives in slot slot_map[grp] of the bank, or is a miss
+  const int slot = (slot_map && !is_shared) ? slot_map[grp] : grp;
+  if (slot < 0) {
+    if (KIND == GemvKind::Down) {   // a miss contributes zero to the combine
+      for (int i = 0; i < gcnt; ++i)
+        for (int c = threadIdx.x; c < 64; c += blockDim.x) out[(size_t)(gstart + i) * N + blockIdx.y * 64 + c] = 0.0f;
+    }
+    return;
+  }
+  const size_t eidx = is_shared ? 0 : (size_t)slot;
   const uint4* __restrict__ codes =
       reinterpret_cast<const uint4*>((is_shared ? s_codes : r_codes) + eidx * code_stride);
   const uint32_t* __restrict__ scales =
@@ -271,7 +280,7 @@ static hipError_t launch_quant_t(const MatRef& r, const MatRef& sh, int N, int K
   dim3 grid(max_groups, rowgroups);
 #define MOE_GEMV_ARGS                                                                                          \
   r.codes, r.hi, r.scales, sh.codes, sh.hi, sh.scales, r.code_stride, r.hi_stride, r.scale_stride, N, K, inter, \
-      P.sorted_rows, P.items, P.n_items, P.T, P.k, P.E, tab.pairs, tab.init, out, dp, di
+      P.sorted_rows, P.items, P.n_items, P.T, P.k, P.E, tab.pairs, tab.init, out, dp, di, P.slot_map
   if (KIND == GemvKind::GateUp && nch == 40) {
     hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (KIND == GemvKind::Down && nch == 10) {

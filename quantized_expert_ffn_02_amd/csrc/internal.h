@@ -52,6 +52,7 @@ struct PermRef {
   const int32_t* sorted_rows = nullptr;  // [n]
   const int32_t* items = nullptr;        // [max_items][3]: group, start, count
   const int32_t* n_items = nullptr;      // device scalar
+  const int32_t* slot_map = nullptr;     // expert-cache mode: bank slot of routed expert g, or -1
   int32_t T = 0, k = 0, E = 0;
 };
 
@@ -123,6 +124,21 @@ hipError_t launch_gemv_quant(GemvKind kind, int fmt, const MatRef& routed, const
 hipError_t launch_gemv_dense(GemvKind kind, const MatRef& routed, const MatRef& shared, int N, int K, int inter,
                              const PermRef& perm, int max_groups, const float* in_rows, float* out,
                              hipStream_t s);
+
+// MFMA path (gemm.hip)
+hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
+hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
+                          const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
+                          int T, int k, const uint16_t* a_f16, void* out, hipStream_t s);
+hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_per, int32_t* tiles,
+                       int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s);
+int gemm_tile_rows();
+
+// miss list of the expert-cache mode: entries r < T*k with slot_map[ids[r]] < 0, ascending
+hipError_t launch_miss_list(const int32_t* ids, int Tk, const int32_t* slot_map, int32_t* miss_rows, int32_t* n_miss,
+                            hipStream_t s);
+
+hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s);
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
                           int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,

@@ -163,4 +163,27 @@ hipError_t launch_items_from_offsets(const int32_t* offsets, int E, int items_pe
   return hipGetLastError();
 }
 
+// Expert-cache miss list: one block walks the entries in chunks of 1024 in
+// ascending r; a block scan of the miss flags gives each miss its position.
+__global__ __launch_bounds__(1024) void k_miss_list(const int32_t* __restrict__ ids, int Tk,
+                                                    const int32_t* __restrict__ slot_map,
+                                                    int32_t* __restrict__ miss_rows, int32_t* __restrict__ n_miss) {
+  int base = 0;
+  for (int r0 = 0; r0 < Tk; r0 += 1024) {
+    const int r = r0 + threadIdx.x;
+    const bool miss = r < Tk && slot_map[ids[r]] < 0;
+    int total = 0;
+    const int pos = block_exclusive_scan_1024(miss ? 1 : 0, &total);
+    if (miss) miss_rows[base + pos] = r;
+    base += total;
+  }
+  if (threadIdx.x == 0) *n_miss = base;
+}
+
+hipError_t launch_miss_list(const int32_t* ids, int Tk, const int32_t* slot_map, int32_t* miss_rows, int32_t* n_miss,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_miss_list, dim3(1), dim3(1024), 0, s, ids, Tk, slot_map, miss_rows, n_miss);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -1,0 +1,76 @@
+"""GPU parity of the 3-bit path and of the expert-cache mode (slot table, hit
+outputs, per-token miss list) against the fp64 oracle, through the C ABI.
+Bars: top-k sets bit-exact, miss list and count bit-exact, outputs within 1e-2
+of the oracle relative to its RMS."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as OF
+from oracle import layer as OL
+from quantized_expert_ffn_02_amd import binding as B
+from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+from tests import workloads as W
+from tests.test_gpu_parity import assert_route_matches, host, run_layer
+
+pytestmark = pytest.mark.gpu
+OUT_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def pool():
+    assert torch.cuda.is_available()
+    slot_of, pool = W.cache_pool("cache")
+    s = synth.CONFIGS["cache"].shape
+    dpool = DeviceBank(s.fmt, synth.CONFIGS["cache"].slots, s.hidden, s.inter, pool)
+    return slot_of, pool, dpool
+
+
+@pytest.mark.parametrize("T", [4, 64])
+def test_q3_layer_forward(T):
+    # a plain (uncached) 3-bit layer: all 512 experts resident
+    hl = W.host_layer("cache")
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+    assert_route_matches(ids, gates, hl.logits(x), hl.shape.top_k, f"q3 T={T}")
+    err = OL.rel_max_err(out, ref)
+    print(f"q3 layer T={T}: max|err|/rms = {err:.3e}")
+    assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("layer", [0, 17, 47])
+def test_cached_layer(pool, layer):
+    slot_of, hpool, dpool = pool
+    w = synth.CONFIGS["cache"]
+    s = w.shape
+    T, k, E = w.tokens[0], s.top_k, s.n_experts
+    hl = W.cache_layer("cache", layer, hpool)
+    x, _ = W.activations_with_margin(hl, T)
+    sb = DeviceBank(s.fmt, 1, s.hidden, s.inter, hl.shared)
+    dl = DeviceLayer(s.hidden, E, k, s.inter, hl.wr, hl.bias, dpool, sb)
+    ws = dl.workspace(T)
+    out = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    n_miss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_slot = to_device(slot_of)
+    B.layer_forward_cached(dl.struct, layer, w.layers, d_slot, dpool.struct, to_device(x), T, out, ids, gates,
+                           miss, n_miss, ws)
+    torch.cuda.synchronize()
+    smat = OF.expert_matrices(s.fmt, hl.shared, s.hidden, s.inter)
+    slot_fn = lambda sl: OF.expert_matrices(s.fmt, hpool, s.hidden, s.inter, sl)
+    ref, ids_r, gates_r, misses_r, _ = OL.cached_layer_forward(x, hl.wr, k, slot_of[layer], slot_fn, lambda: smat,
+                                                                bias=hl.bias)
+    assert_route_matches(host(ids), host(gates), hl.logits(x), k, f"cache layer {layer}")
+    nm = int(host(n_miss)[0])
+    assert nm == len(misses_r)
+    np.testing.assert_array_equal(host(miss)[:nm], misses_r)
+    assert (host(miss)[nm:] == -7).all()                      # nothing written past the count
+    err = OL.rel_max_err(host(out), ref)
+    hits = T * k - nm
+    print(f"cache layer {layer}: hits {hits}/{T * k}, max|err|/rms = {err:.3e}")
+    assert err <= OUT_TOL

@@ -218,3 +218,48 @@ def test_steps_match_fused_layer():
     assert OL.rel_max_err(host(out), ref_out) <= OUT_TOL
     out_f, *_ = run_layer(d, x, T)
     np.testing.assert_array_equal(host(out), out_f)     # same kernels, same bits
+
+
+# ------------------------------------------------------------------ prefill (MFMA grouped GEMM)
+
+def test_gemm_path_medium_full_compare():
+    # 300 Zipf-routed tokens: 3,300 routed + 300 shared entries, beyond the decode
+    # front end, so hot experts (>= 32 rows) take the MFMA GEMM with ragged tiles
+    hl = W.host_layer("prefill")
+    T = 300
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+    assert_route_matches(ids, gates, hl.logits(x), hl.shape.top_k, "prefill T=300")
+    counts = np.bincount(ids.reshape(-1), minlength=hl.shape.n_experts)
+    assert (counts >= 32).sum() >= 3 and ((counts >= 32) & (counts % 128 != 0)).any()
+    err = OL.rel_max_err(out, ref)
+    print(f"prefill T=300: max|err|/rms = {err:.3e}, experts on MFMA: {(counts >= 32).sum()}")
+    assert err <= OUT_TOL
+
+
+def test_prefill_8192_sampled():
+    # the full prefill chunk; top-k checked for every token, outputs on a sample
+    # of tokens recomputed one by one by the oracle
+    hl = W.host_layer("prefill")
+    T = 8192
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    logits = hl.logits(x)
+    assert_route_matches(ids, gates, logits, hl.shape.top_k, "prefill T=8192")
+    counts = np.bincount(ids.reshape(-1), minlength=hl.shape.n_experts)
+    hot = np.argsort(-counts)[:3]
+    cold = np.flatnonzero((counts > 0) & (counts < 32))
+    rng = np.random.default_rng(5)
+    pick = set(rng.choice(T, 24, replace=False).tolist())
+    for e in list(hot) + list(cold[:8]):                 # tokens of hot (MFMA) and cold (GEMV) experts
+        pick.update(np.flatnonzero((ids == e).any(axis=1))[:3].tolist())
+    pick = np.array(sorted(pick))
+    ref, ids_r, _, _ = hl.oracle_forward(x[pick])
+    np.testing.assert_array_equal(np.sort(ids[pick], axis=1), np.sort(ids_r, axis=1))
+    err = OL.rel_max_err(out[pick], ref)
+    print(f"prefill T=8192: {len(pick)} sampled tokens, max|err|/rms = {err:.3e}; "
+          f"experts >= 32 rows: {(counts >= 32).sum()}, empty: {(counts == 0).sum()}")
+    assert err <= OUT_TOL

@@ -452,6 +452,25 @@ def test_residual_bf16_hand_cases():
     assert int(L.residual_bf16(one, np.array([[-3.0]]))[0, 0]) == 0xC000                 # 1 - 3 = -2
 
 
+def test_rms_norm_closed_forms():
+    # a constant row c normalises to sign(c) * 1/sqrt(1 + eps/c^2): exactly 1.0 in bf16 for |c| >= 1
+    x = np.full((2, 64), 0x4040, dtype=np.uint16)          # 3.0
+    x[1] = 0xC040                                           # -3.0
+    xn = L.rms_norm_bf16(x)
+    assert (xn[0] == 0x3F80).all() and (xn[1] == 0xBF80).all()
+    # scaling a row by a power of two leaves its normalisation unchanged (eps aside: rows of O(1))
+    rng = np.random.default_rng(4)
+    xb = _bf16(rng.standard_normal((5, 256)))
+    x2 = _bf16(F.bf16_to_f64(xb) * 4.0)
+    np.testing.assert_array_equal(L.rms_norm_bf16(xb, eps=0.0), L.rms_norm_bf16(x2, eps=0.0))
+    # unit RMS up to bf16 rounding
+    v = F.bf16_to_f64(L.rms_norm_bf16(xb))
+    assert np.all(np.abs(np.sqrt((v * v).mean(axis=1)) - 1.0) < 4e-3)
+    # one stack step: residual of the normalised layer input
+    step, xn2 = L.stack_step(xb, lambda z: np.ones((5, 256)))
+    np.testing.assert_array_equal(step, L.residual_bf16(xb, np.ones((5, 256))))
+
+
 def test_rel_max_err():
     assert L.rel_max_err([1.0, 1.0], [1.0, -1.0]) == 2.0
     assert L.rel_max_err([3.0, 4.0], [3.0, 4.0]) == 0.0

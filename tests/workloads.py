@@ -95,3 +95,28 @@ def upload(hl, device="cuda"):
 def upload_rows(a, device="cuda"):
     from quantized_expert_ffn_02_amd.device_layer import to_device
     return to_device(a, device)
+
+
+def cache_pool(workload="cache"):
+    """Expert-cache setup: slot table [L, E] and the slot pool (experts in slot order:
+    slot l * per_layer + rank = the rank-th most popular expert of layer l)."""
+    w = synth.CONFIGS[workload]
+    s = w.shape
+    slot_of = synth.hot_slot_table(w.seed, w.layers, s.n_experts, w.slots_per_layer)
+    parts = []
+    for l in range(w.layers):
+        ranks = synth.zipf_ranks(w.seed, l, s.n_experts)
+        order = np.argsort(ranks)[:w.slots_per_layer]          # experts by rank 0, 1, ...
+        parts.append(synth.bank(w.seed, l, s.fmt, order, s.hidden, s.inter))
+    pool = {name: np.concatenate([p[name] for p in parts]) for name in parts[0]}
+    return slot_of, pool
+
+
+def cache_layer(workload, layer, pool):
+    """Router, bias and shared expert of one layer of the cache workload (routed experts come from the pool)."""
+    w = synth.CONFIGS[workload]
+    s = w.shape
+    wr = synth.router_weight(w.seed, layer, s.n_experts, s.hidden)
+    bias = synth.zipf_bias(w.seed, layer, s.n_experts, s.zipf)
+    shared = synth.bank(w.seed, layer, s.fmt, [s.n_experts], s.hidden, s.inter)
+    return HostLayer(w.seed, layer, s, wr, bias, pool, shared)

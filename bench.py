@@ -135,6 +135,149 @@ def bench_prefill(steps):
     }
 
 
+def q3_expert_bytes(H, I):
+    w = 3 * H * I
+    return w // 4 + w // 8 + (w // 32) * 2
+
+
+def bench_stack(steps):
+    """48 independent real-shape 2-bit layers (37.9 GB resident), pre-norm residual chain,
+    batch 1 and 32 x 4 = 128 verify tokens; eager calls and one HIP graph per step."""
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+    wl = synth.CONFIGS["stack"]
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    layers = []
+    for l in range(wl.layers):
+        wr = synth.router_weight(wl.seed, l, E, H)
+        bias = synth.zipf_bias(wl.seed, l, E, s.zipf)
+        rb = DeviceBank(s.fmt, E, H, I, synth.bank(wl.seed, l, s.fmt, range(E), H, I, workers=16))
+        sb = DeviceBank(s.fmt, 1, H, I, synth.bank(wl.seed, l, s.fmt, [E], H, I))
+        layers.append(DeviceLayer(H, E, k, I, wr, bias, rb, sb))
+    structs = [d.struct for d in layers]
+    res = {"workload": "stack: 48 independent real-shape 2-bit layers, x_{l+1} = x_l + MoE_l(RMSNorm(x_l)), "
+                       "Zipf(1.1) routing per layer", "resident_GB": sum(d.routed.nbytes() + d.shared.nbytes()
+                                                                         for d in layers) / 1e9}
+    for T in wl.tokens:
+        x0 = to_device(synth.activations(wl.seed + 11000, 0, T, H))
+        ws = layers[0].workspace(T)
+        x_out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        # bytes: per layer router + unique routed experts + shared, from one instrumented pass
+        uniq = []
+        cur = x0
+        for d in layers:
+            ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+            nxt = torch.empty((T, H), dtype=torch.int16, device="cuda")
+            xn = torch.empty((T, H), dtype=torch.int16, device="cuda")
+            B.rmsnorm_bf16(cur, T, H, xn)
+            B.layer_forward(d.struct, xn, T, out, ws, residual=cur, out_bf16=nxt, topk_ids=ids)
+            uniq.append(len(np.unique(ids.cpu().numpy())))
+            cur = nxt
+        step_bytes = sum(E * H * 2 + E * 4 + (u + 1) * q2_expert_bytes(H, I) for u in uniq) + 2 * T * H * 2
+        for _ in range(3):
+            B.stack_forward(structs, x0, T, x_out, ws)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            B.stack_forward(structs, x0, T, x_out, ws)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        # the same step captured once into a HIP graph and replayed
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            B.stack_forward(structs, x0, T, x_out, ws)
+        g.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms_g = t0.elapsed_time(t1) / steps
+        best = min(ms, ms_g)
+        res[f"T{T}"] = {"step_ms_eager": ms, "step_ms_graph": ms_g, "tokens_per_s": T / (best * 1e-3),
+                        "avg_unique_experts_per_layer": float(np.mean(uniq)), "algorithmic_GB_per_step":
+                        step_bytes / 1e9, "sustained_GBps": step_bytes / (best * 1e-3) / 1e9,
+                        "hbm_frac": step_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del g
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_cache(steps):
+    """3-bit layer with a 3,072-slot expert cache (top 64 experts of each of 48 layers), 64 tokens,
+    layer index swept over all 48 layers."""
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+    wl = synth.CONFIGS["cache"]
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    T = wl.tokens[0]
+    slot_of = synth.hot_slot_table(wl.seed, wl.layers, E, wl.slots_per_layer)
+    parts = []
+    for l in range(wl.layers):
+        order = np.argsort(synth.zipf_ranks(wl.seed, l, E))[:wl.slots_per_layer]
+        parts.append(synth.bank(wl.seed, l, s.fmt, order, H, I))
+    pool = DeviceBank(s.fmt, wl.slots, H, I, {n: np.concatenate([p[n] for p in parts]) for n in parts[0]})
+    del parts
+    layers = []
+    for l in range(wl.layers):
+        wr = synth.router_weight(wl.seed, l, E, H)
+        bias = synth.zipf_bias(wl.seed, l, E, s.zipf)
+        sb = DeviceBank(s.fmt, 1, H, I, synth.bank(wl.seed, l, s.fmt, [E], H, I))
+        layers.append(DeviceLayer(H, E, k, I, wr, bias, pool, sb))
+    d_slot = to_device(slot_of)
+    xs = [to_device(synth.activations(wl.seed + 12000, j, T, H)) for j in range(8)]
+    ws = layers[0].workspace(T)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((wl.layers, T, k), dtype=torch.int32, device="cuda")
+    miss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    nmiss = torch.empty(wl.layers, dtype=torch.int32, device="cuda")
+    for l in range(wl.layers):
+        B.layer_forward_cached(layers[l].struct, l, wl.layers, d_slot, pool.struct, xs[l % 8], T, out, ids[l], None,
+                               miss, nmiss[l:l + 1], ws)
+    torch.cuda.synchronize()
+    ids_h, nm = ids.cpu().numpy(), nmiss.cpu().numpy()
+    hit_bytes = []
+    for l in range(wl.layers):
+        u = np.unique(ids_h[l])
+        hits = int((slot_of[l][u] >= 0).sum())
+        hit_bytes.append(E * H * 2 + E * 4 + (hits + 1) * q3_expert_bytes(H, I))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    n = 0
+    for _ in range(steps):
+        for l in range(wl.layers):
+            B.layer_forward_cached(layers[l].struct, l, wl.layers, d_slot, pool.struct, xs[l % 8], T, out, None,
+                                   None, miss, nmiss[l:l + 1], ws)
+            n += 1
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n
+    gb = float(np.mean(hit_bytes))
+    res = {"workload": "cache: real-shape 3-bit layer, 3,072-slot expert cache (top 64 of 512 per layer x 48 "
+                       "layers, 6.6 GB), Zipf(1.1) routing, 64 tokens, layer index swept over 48 layers",
+           "layer_us": ms * 1e3, "tokens_per_s": T / (ms * 1e-3), "hit_rate": 1 - float(nm.mean()) / (T * k),
+           "algorithmic_MB_per_call": gb / 1e6, "GBps": gb / (ms * 1e-3) / 1e9,
+           "hbm_frac": gb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del layers, pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +290,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--cache-steps", type=int, default=5)
+    ap.add_argument("--no-cache", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -276,8 +423,14 @@ def main():
             "avg_launch_us": gu_ms * 1e3,
         },
     }
+    del layers, pool
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args.prefill_steps)
+    if not args.no_stack:
+        result["stack"] = bench_stack(args.stack_steps)
+    if not args.no_cache:
+        result["cache"] = bench_cache(args.cache_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host0, T, args.cpu_seconds)
         result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]

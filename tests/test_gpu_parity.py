@@ -263,3 +263,30 @@ def test_prefill_8192_sampled():
     print(f"prefill T=8192: {len(pick)} sampled tokens, max|err|/rms = {err:.3e}; "
           f"experts >= 32 rows: {(counts >= 32).sum()}, empty: {(counts == 0).sum()}")
     assert err <= OUT_TOL
+
+
+def test_graph_replay_matches_eager():
+    # the whole layer call captured into one HIP graph; every replay (with other
+    # eager work between them) must equal the eager result bit for bit
+    hl = W.host_layer("decode")
+    T = 4
+    x, _ = W.activations_with_margin(hl, T)
+    x2 = synth.activations(31, 0, T, hl.H)
+    d = W.upload(hl)
+    ws = d.workspace(T)
+    xd, x2d = dev(x), dev(x2)
+    out = torch.empty((T, hl.H), dtype=torch.float32, device="cuda")
+    other = torch.empty_like(out)
+    B.layer_forward(d.struct, xd, T, out, ws)
+    torch.cuda.synchronize()
+    eager = host(out).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.layer_forward(d.struct, xd, T, out, ws)
+    for rep in range(4):
+        out.zero_()
+        B.layer_forward(d.struct, x2d, T, other, ws)      # eager work on the same workspace in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), eager, err_msg=f"replay {rep}")

@@ -322,7 +322,7 @@ int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
   perm.k = L->top_k;
   perm.E = L->n_experts;
   const int n = T * L->top_k + (has_shared(L) ? T : 0);
-  const bool gemm = use_gemm_path(n) && L->routed.fmt == MOE_FMT_Q2;
+  const bool gemm = use_gemm_path(n) && L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter);
   int32_t* tiles = at<int32_t>(ws, lay.tiles);
   int32_t* n_tiles = at<int32_t>(ws, lay.n_tiles);
   MOE_TRY(launch_plan(offsets, L->n_experts, gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T), tiles, n_tiles,
@@ -386,7 +386,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     if (rc) return rc;
     MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
                            at<int32_t>(ws, lay.base), s));
-    gemm = quant && L->routed.fmt == MOE_FMT_Q2;
+    gemm = L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter);
     MOE_TRY(launch_plan(offsets, E, gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T), at<int32_t>(ws, lay.tiles),
                         at<int32_t>(ws, lay.n_tiles), items, n_items, s));
   }

@@ -36,6 +36,9 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+// native 128-bit vector (HIP's uint4 is a struct whose copies into LDS keep a
+// private-memory temporary alive)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 static constexpr int BM = 128, BN = 128, BK = 64;
 static constexpr int LDS_STRIDE = BK + 8;   // halves per LDS row (padding against bank conflicts)
@@ -75,103 +78,126 @@ hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out,
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Exact fp16 dequantisation of one 2-bit word (16 weights) into 8 pair-order
-// dwords: pair j = (w_j, w_{j+8}) as (fp16, fp16).  Codes at bits 0..9 of each
-// half fit the fp16 significand under the exponent of 1024 (value 1024 + c 2^p);
-// v_pk_fma_f16 turns that into c - 2 exactly and v_pk_mul_f16 applies the scale.
-// ---------------------------------------------------------------------------
-struct Dq16 {
-  uint32_t mask[5];   // 0x00030003 << 2j, j = 0..4
-  uint32_t magic;     // 0x64006400
-  h2_t mul[5];        // 2^-p
-  h2_t add[5];        // -(1024 * 2^-p + 2)
-};
-
-__device__ __forceinline__ Dq16 dq16_consts() {
-  Dq16 d;
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    d.mask[j] = vgpr_const(0x00030003u << (2 * j));
-    const float m = ldexpf(1.0f, -2 * j);
-    d.mul[j] = h2_t{(_Float16)m, (_Float16)m};
-    d.add[j] = h2_t{(_Float16)(-(1024.0f * m + 2.0f)), (_Float16)(-(1024.0f * m + 2.0f))};
-  }
-  d.magic = vgpr_const(0x64006400u);
-  return d;
-}
-
-__device__ __forceinline__ uint32_t dq_pair(uint32_t w, int j, const Dq16& d, h2_t s2) {
-  // pairs 0..4 in place, 5..7 from w >> 10 at positions 0..2
-  const int q = j < 5 ? j : j - 5;
-  const uint32_t src = j < 5 ? w : (w >> 10);
-  const uint32_t v = (src & d.mask[q]) | d.magic;
-  h2_t f = __builtin_bit_cast(h2_t, v);
-  f = f * d.mul[q] + d.add[q];      // exact: c - 2
-  f = f * s2;                        // exact: s * (c - 2)
-  return __builtin_bit_cast(uint32_t, f);
-}
-
-// ---------------------------------------------------------------------------
-// MFMA fragments from LDS and the 2 x 2 wave tile
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ h8_t lds_frag(const uint16_t* base, int row, int k) {
-  return *reinterpret_cast<const h8_t*>(base + row * LDS_STRIDE + k);
-}
-
-// acc[mi][ni] += A[rows a0 + 32 mi ..][k] * B[cols b0 + 32 ni ..][k] over one BK step
-__device__ __forceinline__ void wave_mfma_step(const uint16_t* As, const uint16_t* Bs, int a0, int b0_0, int b0_1,
-                                               f16x_t acc[2][2]) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 31, kh = (lane >> 5) * 8;
-#pragma unroll
-  for (int k16 = 0; k16 < BK; k16 += 16) {
-    const h8_t fa0 = lds_frag(As, a0 + r, k16 + kh);
-    const h8_t fa1 = lds_frag(As, a0 + 32 + r, k16 + kh);
-    const h8_t fb0 = lds_frag(Bs, b0_0 + r, k16 + kh);
-    const h8_t fb1 = lds_frag(Bs, b0_1 + r, k16 + kh);
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa0, fb0, acc[0][0], 0, 0, 0);
-    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa0, fb1, acc[0][1], 0, 0, 0);
-    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa1, fb0, acc[1][0], 0, 0, 0);
-    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa1, fb1, acc[1][1], 0, 0, 0);
-  }
-}
-
 // row (0..31) of accumulator register r for this lane, column = lane & 31
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Global loads of one K step for one thread: 32 fp16 activations, 2 code words
-// and the block's fp16 scale.
-struct Prefetch {
-  uint4 a[4];
-  uint2 b;
-  uint32_t s;
+// ---------------------------------------------------------------------------
+// Grouped GEMM over the 2-bit experts.
+//
+// A block owns one M-tile (up to GBM = 128 sorted rows of one expert group) and
+// 4 x 64 weight rows ("columns" of the product); each of its 4 waves computes
+// all 128 rows x its own 64 columns as 4 x 2 MFMA 32x32x16 tiles.  The
+// activations A are shared by the 4 waves and go through LDS (double-buffered,
+// rows padded to 72 halves so that the fragment reads are free of bank
+// conflicts).  The weights B are used by exactly one wave, so each wave reads
+// its 2-bit codes straight from global memory into registers and dequantises
+// them there into MFMA B fragments: no LDS traffic and no duplicated work for B.
+//
+// B fragment of a 32x32x16 MFMA: lane l holds 8 consecutive K positions
+// 8 (l / 32) .. + 7 of column l % 32.  In pair order, positions 8h .. 8h + 7 of
+// a 16-group are the pairs (w_{4h+q}, w_{4h+q+8}), q = 0..3, whose codes sit at
+// bits 2q and 16 + 2q of the code word shifted right by 8h.  OR-ing a code under
+// the exponent of 1024 gives the fp16 value 1024 + c 4^q; one v_pk_fma_f16 turns
+// it into c - 2 (exact) and one v_pk_mul_f16 applies the block scale (exact).
+// ---------------------------------------------------------------------------
+static constexpr int GBM = 128;              // rows per M-tile
+static constexpr int GBK = 64;               // K per pipeline step
+static constexpr int A_STRIDE = GBK + 8;     // halves per LDS row
+static constexpr int GCOLS = 256;            // weight rows per block (4 waves x 64)
+
+struct BConst {
+  uint32_t mask[4];   // 0x00030003 << 2q
+  h2_t mul[4];        // 4^-q
+  h2_t add[4];        // -(1024 * 4^-q + 2)
+  uint32_t magic;     // 0x64006400
 };
 
-// Software pipeline over the K steps with two register sets: while the MFMAs of
-// step kc run out of LDS buffer kc % 2, the loads of step kc + 2 are in flight
-// and step kc + 1 (loaded one iteration earlier) is dequantised into the other
-// buffer.  Unrolled by two so that both register sets have static names.
-#define K_PIPELINE(MFMA_BUF0, MFMA_BUF1)                 \
-  Prefetch P0, P1;                                       \
-  load_step(P0, 0);                                      \
-  if (nch > 1) load_step(P1, 1);                         \
-  store_step(P0, 0);                                     \
-  __syncthreads();                                       \
-  for (int kc = 0; kc < nch; kc += 2) {                  \
-    if (kc + 2 < nch) load_step(P0, kc + 2);             \
-    MFMA_BUF0;                                           \
-    if (kc + 1 < nch) store_step(P1, 1);                 \
-    __syncthreads();                                     \
-    if (kc + 1 >= nch) break;                            \
-    if (kc + 3 < nch) load_step(P1, kc + 3);             \
-    MFMA_BUF1;                                           \
-    if (kc + 2 < nch) store_step(P0, 0);                 \
-    __syncthreads();                                     \
+__device__ __forceinline__ BConst bconst() {
+  BConst c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c.mask[q] = vgpr_const(0x00030003u << (2 * q));
+    const float m = ldexpf(1.0f, -2 * q);
+    c.mul[q] = h2_t{(_Float16)m, (_Float16)m};
+    const _Float16 a = (_Float16)(-(1024.0f * m + 2.0f));
+    c.add[q] = h2_t{a, a};
   }
+  c.magic = vgpr_const(0x64006400u);
+  return c;
+}
+
+// B fragment (8 fp16 in pair order) of one lane from its code word w (already
+// shifted right by 8 * lane-half) and the block scale pair s2.
+__device__ __forceinline__ h8_t b_frag(uint32_t w, h2_t s2, const BConst& c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h2_t f = __builtin_bit_cast(h2_t, (w & c.mask[q]) | c.magic);
+    f = f * c.mul[q] + c.add[q];   // c - 2, exact
+    f = f * s2;                    // s (c - 2), exact
+    o[q] = __builtin_bit_cast(uint32_t, f);
+  }
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(h8_t, u4v{o[0], o[1], o[2], o[3]});
+}
+
+__device__ __forceinline__ h2_t scale_pair(uint32_t d, bool hi) {
+  const uint32_t v = hi ? ((d >> 16) | (d & 0xFFFF0000u)) : ((d & 0xFFFFu) | (d << 16));
+  return __builtin_bit_cast(h2_t, v);
+}
+
+// Registers of one pipeline step: 64 K of A for this thread's LDS row slice and
+// the codes + scales of the wave's two B columns.
+struct StepRegs {
+  u32x4 a0, a1, a2, a3;
+  u32x4 c0, c1;
+  uint32_t s0, s1;
+};
+
+struct BCol {
+  const u32x4* __restrict__ codes;   // this lane's column: 16 B per step
+  const uint32_t* __restrict__ scales;
+};
+
+// Column n of a tiled 2-bit matrix with K columns: pointer to its first 16-byte
+// code chunk (steps advance by 1024 B) and to its scale dword of blocks 0, 1.
+__device__ __forceinline__ BCol b_column(const uint8_t* codes, const uint16_t* scales, int n, int K) {
+  BCol b;
+  const int nt = n >> 6, nl = n & 63;
+  b.codes = reinterpret_cast<const u32x4*>(codes + ((size_t)nt * (K / 64) * 64 + nl) * 16);
+  b.scales = reinterpret_cast<const uint32_t*>(scales + ((size_t)nt * (K / 128) * 64 + nl) * 4);
+  return b;
+}
+
+// step kc: codes at + kc * 64 uint4; scales of blocks 2kc, 2kc+1 at dword
+// (kc / 2) * 128 + (kc % 2)
+__device__ __forceinline__ void load_b(const BCol& b, int kc, u32x4& c, uint32_t& s) {
+  c = b.codes[(size_t)kc * 64];
+  s = b.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
+}
+
+// One K step of a wave: 4 x (2 B fragments, 4 A fragments, 8 MFMAs).
+__device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const StepRegs& R, int shift,
+                                          const BConst& bc, f16x_t acc[4][2]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+  const uint32_t cw0[4] = {R.c0.x, R.c0.y, R.c0.z, R.c0.w};
+  const uint32_t cw1[4] = {R.c1.x, R.c1.y, R.c1.z, R.c1.w};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const h8_t b0 = b_frag(cw0[s] >> shift, scale_pair(R.s0, s >= 2), bc);
+    const h8_t b1 = b_frag(cw1[s] >> shift, scale_pair(R.s1, s >= 2), bc);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const h8_t a = *reinterpret_cast<const h8_t*>(As + (mi * 32 + r) * A_STRIDE + s * 16 + kh);
+      acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[mi][0], 0, 0, 0);
+      acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[mi][1], 0, 0, 0);
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM tiles: (group, first sorted position, rows <= BM) per M-tile.
+// Grouped GEMM tiles: (group, first sorted position, rows <= GBM) per M-tile.
 // ---------------------------------------------------------------------------
 struct GemmTile {
   int g, m0, rows, n;   // n = column-tile index
@@ -204,167 +230,129 @@ __device__ __forceinline__ bool load_tile(const int32_t* __restrict__ tiles, con
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up: h[p, n] = SiLU(x_t . Wg[n]) * (x_t . Wu[n]) for the tile's rows p
-// (token t of sorted position p), columns n in [64 * t.n, +64).
-// LDS B rows 0..63 = gate rows, 64..127 = the matching up rows.
+// The grouped GEMM kernel for both projections.
+//   GateUp: rows p of the tile are tokens t(p) (x_f16 rows), K = H; wave w of
+//           column tile j owns gate rows 128 j + 32 w + (0..31) and the same up
+//           rows; the epilogue writes h = SiLU(gate) * up in fp16, pair order.
+//   Down:   rows p are rows of h (K = I); wave w of column tile j owns output
+//           columns 256 j + 64 w + (0..63); the epilogue writes fp32 y.
+// K / 64 (the number of steps) is even: H and I are multiples of 128.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_gemm_gateup_q2(
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void k_gemm_q2(
     const uint8_t* __restrict__ r_codes, const uint16_t* __restrict__ r_scales, const uint8_t* __restrict__ s_codes,
     const uint16_t* __restrict__ s_scales, size_t code_stride, size_t scale_stride, int H, int I, int E,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ sorted_rows,
-    int T, int k, const uint16_t* __restrict__ xh, uint16_t* __restrict__ h_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+    int T, int k, const uint16_t* __restrict__ a_src, uint16_t* __restrict__ h_out, float* __restrict__ y_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * A_STRIDE];
   GemmTile t;
   if (!load_tile(tiles, n_tiles, t)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool sh = t.g == E;
   const size_t eidx = sh ? 0 : (size_t)t.g;
-  const uint8_t* __restrict__ codes = (sh ? s_codes : r_codes) + eidx * code_stride;
-  const uint16_t* __restrict__ scales = (sh ? s_scales : r_scales) + eidx * scale_stride;
-  const int nch = H / 64, n128 = H / 128;
+  const uint8_t* codes = (sh ? s_codes : r_codes) + eidx * code_stride;
+  const uint16_t* scales = (sh ? s_scales : r_scales) + eidx * scale_stride;
+  const int K = GATEUP ? H : I;
+  const int nch = K / GBK;
 
-  // A: thread -> (row ra = tid / 2, half ha = tid % 2): 32 fp16 of the row per step
+  // A staging: thread -> (row ra = tid / 2, 32-half slice ha = tid % 2) of the step
   const int ra = tid >> 1, ha = tid & 1;
-  int tok;
-  {
-    const int p = t.m0 + (ra < t.rows ? ra : 0);
-    const int r = sorted_rows[p];
+  const int pa = t.m0 + (ra < t.rows ? ra : 0);
+  size_t arow;
+  if (GATEUP) {
+    const int r = sorted_rows[pa];
     const int Tk = T * k;
-    tok = r < Tk ? r / k : r - Tk;
+    arow = (size_t)(r < Tk ? r / k : r - Tk);
+  } else {
+    arow = (size_t)pa;
   }
-  const uint4* __restrict__ arow = reinterpret_cast<const uint4*>(xh + (size_t)tok * H) + ha * 4;
-  // B: thread -> (LDS row rb = tid / 2: gate rows 0..63, up rows 64..127; half hb = block within the chunk)
-  const int rb = tid >> 1, hb = tid & 1;
-  const int wrow = (rb < 64) ? t.n * 64 + rb : I + t.n * 64 + (rb - 64);
-  const int ng = wrow >> 6, rl = wrow & 63;
-  const uint2* __restrict__ bcode = reinterpret_cast<const uint2*>(codes) + ((size_t)ng * nch * 64 + rl) * 2 + hb;
-  const Dq16 D = dq16_consts();
+  const u32x4* __restrict__ ag = reinterpret_cast<const u32x4*>(a_src + arow * K) + ha * 4;
+  uint16_t* const as_dst0 = &As[0][ra * A_STRIDE + ha * 32];
+  uint16_t* const as_dst1 = &As[1][ra * A_STRIDE + ha * 32];
 
-  auto load_step = [&](Prefetch& P, int kc) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) P.a[q] = arow[kc * 8 + q];
-    P.b = bcode[(size_t)kc * 64 * 2];
-    const int blk = 2 * kc + hb;
-    P.s = scales[(((size_t)ng * n128 + (blk >> 2)) * 64 + rl) * 4 + (blk & 3)];
-  };
-  auto store_step = [&](const Prefetch& P, int buf) {
-    uint16_t* a = &As[buf][ra * LDS_STRIDE + ha * 32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) reinterpret_cast<uint4*>(a)[q] = P.a[q];
-    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)P.s);
-    const h2_t s2 = h2_t{sv, sv};
-    uint32_t o[16];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      o[j] = dq_pair(P.b.x, j, D, s2);
-      o[8 + j] = dq_pair(P.b.y, j, D, s2);
-    }
-    uint4* b = reinterpret_cast<uint4*>(&Bs[buf][rb * LDS_STRIDE + hb * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-  };
+  // B columns of this lane
+  int n0, n1;
+  if (GATEUP) {
+    n0 = t.n * 128 + wv * 32 + (lane & 31);
+    n1 = I + n0;
+  } else {
+    n0 = t.n * GCOLS + wv * 64 + (lane & 31);
+    n1 = n0 + 32;
+  }
+  const BCol B0 = b_column(codes, scales, n0, K);
+  const BCol B1 = b_column(codes, scales, n1, K);
+  const int shift = (lane >> 5) * 8;
+  const BConst bc = bconst();
 
-  f16x_t acc[2][2];
+  f16x_t acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // wave tile: rows (wv >> 1) * 64, gate cols (wv & 1) * 32 and the matching up cols
-  const int a0 = (wv >> 1) * 64;
-  const int bg = (wv & 1) * 32, bu = 64 + (wv & 1) * 32;
-
-  K_PIPELINE(wave_mfma_step(As[0], Bs[0], a0, bg, bu, acc), wave_mfma_step(As[1], Bs[1], a0, bg, bu, acc));
-  // epilogue: SwiGLU in registers, h stored in pair order
-  const int col = t.n * 64 + (wv & 1) * 32 + (lane & 31);
-  const int pcol = (col & ~15) + pair_pos(col & 15);
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = a0 + 32 * mi + acc_row(r, lane);
-      if (row < t.rows) {
-        const float g = acc[mi][0][r], u = acc[mi][1][r];
-        const float hv = g / (1.0f + expf(-g)) * u;
-        h_out[(size_t)(t.m0 + row) * I + pcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Down: y[p, n] = h[p] . Wd[n] for the tile's rows, n in [128 * t.n, +128).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void k_gemm_down_q2(
-    const uint8_t* __restrict__ r_codes, const uint16_t* __restrict__ r_scales, const uint8_t* __restrict__ s_codes,
-    const uint16_t* __restrict__ s_scales, size_t code_stride, size_t scale_stride, int H, int I, int E,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles, const uint16_t* __restrict__ hh,
-    float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
-  GemmTile t;
-  if (!load_tile(tiles, n_tiles, t)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool sh = t.g == E;
-  const size_t eidx = sh ? 0 : (size_t)t.g;
-  const uint8_t* __restrict__ codes = (sh ? s_codes : r_codes) + eidx * code_stride;
-  const uint16_t* __restrict__ scales = (sh ? s_scales : r_scales) + eidx * scale_stride;
-  const int nch = I / 64, n128 = I / 128;
-
-  const int ra = tid >> 1, ha = tid & 1;
-  const int prow = t.m0 + (ra < t.rows ? ra : 0);
-  const uint4* __restrict__ arow = reinterpret_cast<const uint4*>(hh + (size_t)prow * I) + ha * 4;
-  const int rb = tid >> 1, hb = tid & 1;
-  const int wrow = t.n * 128 + rb;
-  const int ng = wrow >> 6, rl = wrow & 63;
-  const uint2* __restrict__ bcode = reinterpret_cast<const uint2*>(codes) + ((size_t)ng * nch * 64 + rl) * 2 + hb;
-  const Dq16 D = dq16_consts();
-
-  auto load_step = [&](Prefetch& P, int kc) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) P.a[q] = arow[kc * 8 + q];
-    P.b = bcode[(size_t)kc * 64 * 2];
-    const int blk = 2 * kc + hb;
-    P.s = scales[(((size_t)ng * n128 + (blk >> 2)) * 64 + rl) * 4 + (blk & 3)];
+  auto load_step = [&](StepRegs& R, int kc) {
+    R.a0 = ag[kc * 8 + 0];
+    R.a1 = ag[kc * 8 + 1];
+    R.a2 = ag[kc * 8 + 2];
+    R.a3 = ag[kc * 8 + 3];
+    load_b(B0, kc, R.c0, R.s0);
+    load_b(B1, kc, R.c1, R.s1);
   };
-  auto store_step = [&](const Prefetch& P, int buf) {
-    uint16_t* a = &As[buf][ra * LDS_STRIDE + ha * 32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) reinterpret_cast<uint4*>(a)[q] = P.a[q];
-    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)P.s);
-    const h2_t s2 = h2_t{sv, sv};
-    uint32_t o[16];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      o[j] = dq_pair(P.b.x, j, D, s2);
-      o[8 + j] = dq_pair(P.b.y, j, D, s2);
-    }
-    uint4* b = reinterpret_cast<uint4*>(&Bs[buf][rb * LDS_STRIDE + hb * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  auto store_a = [&](const StepRegs& R, uint16_t* dst) {
+    u32x4* d = reinterpret_cast<u32x4*>(dst);
+    d[0] = R.a0;
+    d[1] = R.a1;
+    d[2] = R.a2;
+    d[3] = R.a3;
   };
 
-  f16x_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const int a0 = (wv >> 1) * 64, b0 = (wv & 1) * 64;
+  // Two register sets; the loop is unrolled by two so both keep static names.
+  // Step kc computes from LDS buffer kc % 2 and register set kc % 2 while the
+  // loads of step kc + 1 (other set) are in flight.
+  StepRegs R0, R1;
+  load_step(R0, 0);
+  store_a(R0, as_dst0);
+  __syncthreads();
+  for (int kc = 0; kc < nch; kc += 2) {
+    load_step(R1, kc + 1);
+    wave_step(As[0], R0, shift, bc, acc);
+    store_a(R1, as_dst1);
+    __syncthreads();
+    if (kc + 2 < nch) load_step(R0, kc + 2);
+    wave_step(As[1], R1, shift, bc, acc);
+    if (kc + 2 < nch) store_a(R0, as_dst0);
+    __syncthreads();
+  }
 
-  K_PIPELINE(wave_mfma_step(As[0], Bs[0], a0, b0, b0 + 32, acc), wave_mfma_step(As[1], Bs[1], a0, b0, b0 + 32, acc));
+  if (GATEUP) {
+    // h = SiLU(gate) * up, fp16, stored at the pair-order position of its column
+    const int col = t.n * 128 + wv * 32 + (lane & 31);
+    const int pcol = (col & ~15) + pair_pos(col & 15);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = a0 + 32 * mi + acc_row(r, lane);
-        if (row < t.rows) y[(size_t)(t.m0 + row) * H + t.n * 128 + b0 + 32 * ni + (lane & 31)] = acc[mi][ni][r];
+        const int row = mi * 32 + acc_row(r, lane);
+        if (row < t.rows) {
+          const float g = acc[mi][0][r], u = acc[mi][1][r];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          h_out[(size_t)(t.m0 + row) * I + pcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+        }
       }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mi * 32 + acc_row(r, lane);
+          if (row < t.rows) y_out[(size_t)(t.m0 + row) * H + (f ? n1 : n0)] = acc[mi][f][r];
+        }
+  }
 }
 
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
@@ -372,13 +360,13 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   if (kind == GemvKind::GateUp) {
-    hipLaunchKernelGGL(k_gemm_gateup_q2, dim3(max_tiles, I / 64), dim3(256), 0, s, routed.codes, routed.scales,
+    hipLaunchKernelGGL(k_gemm_q2<true>, dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
                        shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
-                       sorted_rows, T, k, a_f16, (uint16_t*)out);
+                       sorted_rows, T, k, a_f16, (uint16_t*)out, nullptr);
   } else {
-    hipLaunchKernelGGL(k_gemm_down_q2, dim3(max_tiles, H / 128), dim3(256), 0, s, routed.codes, routed.scales,
+    hipLaunchKernelGGL(k_gemm_q2<false>, dim3(max_tiles, H / GCOLS), dim3(256), 0, s, routed.codes, routed.scales,
                        shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
-                       a_f16, (float*)out);
+                       nullptr, T, k, a_f16, nullptr, (float*)out);
   }
   return hipGetLastError();
 }
@@ -401,10 +389,10 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const int ra = tid >> 1, ha = tid & 1;
   const int arow_i = min(m0 + ra, T - 1), brow_i = min(n0 + ra, E - 1);
-  const uint4* __restrict__ arow = reinterpret_cast<const uint4*>(x + (size_t)arow_i * H) + ha * 4;
-  const uint4* __restrict__ brow = reinterpret_cast<const uint4*>(wr + (size_t)brow_i * H) + ha * 4;
+  const u32x4* __restrict__ arow = reinterpret_cast<const u32x4*>(x + (size_t)arow_i * H) + ha * 4;
+  const u32x4* __restrict__ brow = reinterpret_cast<const u32x4*>(wr + (size_t)brow_i * H) + ha * 4;
   const int nch = H / 64;
-  uint4 pa[4], pb[4];
+  u32x4 pa[4], pb[4];
   auto load_step = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -415,8 +403,8 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
   auto store_step = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      reinterpret_cast<uint4*>(&As[buf][ra * LDS_STRIDE + ha * 32])[q] = pa[q];
-      reinterpret_cast<uint4*>(&Bs[buf][ra * LDS_STRIDE + ha * 32])[q] = pb[q];
+      reinterpret_cast<u32x4*>(&As[buf][ra * LDS_STRIDE + ha * 32])[q] = pa[q];
+      reinterpret_cast<u32x4*>(&Bs[buf][ra * LDS_STRIDE + ha * 32])[q] = pb[q];
     }
   };
   f16x_t acc[2][2];
@@ -531,6 +519,7 @@ hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_pe
   return hipGetLastError();
 }
 
-int gemm_tile_rows() { return BM; }
+int gemm_tile_rows() { return GBM; }
+bool gemm_shape_ok(int H, int I) { return H % GCOLS == 0 && I % 128 == 0; }
 
 }  // namespace moe

@@ -269,8 +269,8 @@ __global__ __launch_bounds__(W * 64) void k_gemv_quant(
 }
 
 // Launch shapes with their own register budgets: gate/up 8 waves x 5 chunks
-// (K = 2560), down 5 waves x 2 chunks (K = 640); other K use 16 waves x
-// ceil(K / 1024) chunks.
+// (K = 2560), down 5 waves x 2 chunks (K = 640); other K use 8 waves of up to
+// 5 chunks, and 16 waves x 4 chunks beyond K = 2560.
 template <GemvKind KIND, bool Q3>
 static hipError_t launch_quant_t(const MatRef& r, const MatRef& sh, int N, int K, int inter, const PermRef& P,
                                  int max_groups, const TableRef& tab, float* out, uint32_t* dp, float* di,
@@ -285,10 +285,12 @@ static hipError_t launch_quant_t(const MatRef& r, const MatRef& sh, int N, int K
     hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (KIND == GemvKind::Down && nch == 10) {
     hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 5, 2, 4>), grid, dim3(320), 0, s, MOE_GEMV_ARGS);
+  } else if (nch <= 8) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 1, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (nch <= 16) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 1, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
-  } else if (nch <= 32) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 2, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 2, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
+  } else if (nch <= 40) {
+    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (nch <= 64) {
     hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 4, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
   } else {

@@ -133,6 +133,8 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
 hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_per, int32_t* tiles,
                        int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s);
 int gemm_tile_rows();
+// shapes the grouped GEMM covers (column tiles of 128 gate/up and 256 down rows)
+bool gemm_shape_ok(int H, int I);
 
 // miss list of the expert-cache mode: entries r < T*k with slot_map[ids[r]] < 0, ascending
 hipError_t launch_miss_list(const int32_t* ids, int Tk, const int32_t* slot_map, int32_t* miss_rows, int32_t* n_miss,

@@ -355,6 +355,54 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   int32_t* n_items = at<int32_t>(ws, lay.n_items);
   const bool quant = L->routed.fmt != MOE_FMT_BF16;
   bool x_table_ready = false, gemm = false;
+  if (n <= kSmallRouteMaxEntries && quant && decode_direct_ok(T, k, with_shared, L->hidden, L->inter)) {
+    // decode / MTP-verify batch, entries addressed directly: router front end,
+    // gate/up with the top-k inside, down, combine
+    SmallRouteArgs a;
+    a.x = x;
+    a.T = T;
+    a.E = E;
+    a.H = L->hidden;
+    a.k = k;
+    a.with_shared = with_shared;
+    a.q3 = L->routed.fmt == MOE_FMT_Q3;
+    a.wr = L->w_router;
+    a.bias = L->router_bias;
+    a.logits = at<float>(ws, lay.logits);
+    a.xpairs = at<uint32_t>(ws, lay.xtab_pairs);
+    a.xinit = at<float>(ws, lay.xtab_init);
+    MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_front(a, s); }));
+    DecodeFfnArgs d;
+    d.r13 = mat_w13(L->routed);
+    d.r2 = mat_w2(L->routed);
+    if (with_shared) {
+      d.s13 = mat_w13(L->shared);
+      d.s2 = mat_w2(L->shared);
+    }
+    d.H = L->hidden;
+    d.I = L->inter;
+    d.T = T;
+    d.k = k;
+    d.E = E;
+    d.with_shared = with_shared;
+    d.q3 = a.q3;
+    d.logits = a.logits;
+    d.ids = ids;
+    d.gates = gates;
+    d.margin = margin;
+    d.xpairs = a.xpairs;
+    d.xinit = a.xinit;
+    d.hpairs = at<uint32_t>(ws, lay.htab_pairs);
+    d.hinit = at<float>(ws, lay.htab_init);
+    d.y = at<float>(ws, lay.y);
+    d.residual = residual;
+    d.out = out;
+    d.out_bf16 = out_bf16;
+    MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] { return launch_decode_gateup(d, s); }));
+    MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] { return launch_decode_down(d, s); }));
+    MOE_TRY(launch_decode_combine(d, s));
+    return MOE_OK;
+  }
   if (n <= kSmallRouteMaxEntries) {
     // decode / MTP-verify batch: router, activation table, top-k and permutation in one launch
     SmallRouteArgs a;

@@ -193,6 +193,11 @@ __global__ __launch_bounds__(256) void k_route_select(SmallRouteArgs a) {
   }
 }
 
+hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
   if (a.E <= 64)

@@ -88,6 +88,31 @@ struct SmallRouteArgs {
 // Largest T * k (+ T) the decode front end sorts in one block.
 static constexpr int kSmallRouteMaxEntries = 1024;
 
+// Decode-sized batches whose entries are addressed directly (decode_ffn.hip):
+// no permutation, top-k inside the gate/up launch, combine inside the down
+// launch.
+static constexpr int kDecodeDirectMaxTokens = 16;
+struct DecodeFfnArgs {
+  MatRef r13, s13, r2, s2;
+  int H = 0, I = 0, T = 0, k = 0, E = 0, with_shared = 0, q3 = 0;
+  const float* logits = nullptr;      // [T][E] router logits
+  int32_t* ids = nullptr;             // [T][k] written by the gate/up launch
+  float* gates = nullptr;             // [T][k]
+  float* margin = nullptr;            // [T] or NULL
+  const uint32_t* xpairs = nullptr;   // activation table of x
+  const float* xinit = nullptr;
+  uint32_t* hpairs = nullptr;         // down projection's table of h, one row per entry
+  float* hinit = nullptr;
+  float* y = nullptr;                 // [entries][H] gate-scaled expert outputs
+  const uint16_t* residual = nullptr; // [T][H] bf16 or NULL
+  float* out = nullptr;               // [T][H]
+  uint16_t* out_bf16 = nullptr;       // [T][H] or NULL
+};
+bool decode_direct_ok(int T, int k, int with_shared, int H, int I);
+hipError_t launch_decode_gateup(const DecodeFfnArgs& a, hipStream_t s);
+hipError_t launch_decode_down(const DecodeFfnArgs& a, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);
+
 // ---- launchers (return hipGetLastError()) ----
 hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s);
 
@@ -96,6 +121,8 @@ hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, cons
 hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s);
 hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s);
+// router logits + activation table only (the first launch of launch_route_small)
+hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
                        hipStream_t s);
 

@@ -52,18 +52,24 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Top-k of one token: logits row [E] -> ids[k], gates[k], margin.
-// Lanes < k end up holding (my_e, gate); the function writes the outputs itself.
+// Keys of one token's top-k: lane r (< k) holds the key of rank r in ``mine``;
+// ``last`` is the k-th key and ``next`` the (k+1)-th (0 when k == E).
+struct TopkKeys {
+  uint64_t mine, last, next;
+};
+
 template <int VPL>
-__device__ void wave_topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
-                              float* __restrict__ gates_out, float* __restrict__ margin_out,
-                              int32_t* __restrict__ ids_lds = nullptr) {
+__device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k) {
   const int lane = threadIdx.x & 63;
+  // all VPL loads in flight at once (clamped index, no branch around a load)
+  float v[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
   uint64_t key[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
     const int e = lane + 64 * j;
-    key[j] = e < E ? topk_key(row[e], e) : 0ull;   // 0 sorts below every real key
+    key[j] = e < E ? topk_key(v[j], e) : 0ull;   // 0 sorts below every real key
   }
   // per-lane descending sort of the VPL keys
 #pragma unroll
@@ -75,33 +81,58 @@ __device__ void wave_topk_row(const float* __restrict__ row, int E, int k, int32
         key[b] = key[b - 1];
         key[b - 1] = t;
       }
-  uint64_t mine = 0, last = 0, next = 0;
+  TopkKeys r;
+  r.mine = r.last = r.next = 0;
   const int rounds = k < E ? k + 1 : k;
-  for (int r = 0; r < rounds; ++r) {
+  for (int q = 0; q < rounds; ++q) {
     const uint64_t best = wave_max_key(key[0]);
-    if (r < k) {
-      if (lane == r) mine = best;
-      last = best;
+    if (q < k) {
+      if (lane == q) r.mine = best;
+      r.last = best;
       if (key[0] == best) {   // the lane holding it pops its head
 #pragma unroll
         for (int j = 0; j + 1 < VPL; ++j) key[j] = key[j + 1];
         key[VPL - 1] = 0ull;
       }
     } else {
-      next = best;
+      r.next = best;
     }
   }
-  const float my_v = key_value(mine);
+  return r;
+}
+
+// Expert id of rank i (wave-uniform).
+__device__ __forceinline__ int topk_rank_id(const TopkKeys& r, int i) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)r.mine, i);
+  return (int)~lo;
+}
+
+// ids[k], gates[k] (softmax of the selected logits = the full softmax
+// renormalised over them) and the margin between rank k-1 and rank k.
+__device__ __forceinline__ void topk_write(const TopkKeys& r, int E, int k, int32_t* __restrict__ ids_out,
+                                           float* __restrict__ gates_out, float* __restrict__ margin_out,
+                                           int32_t* __restrict__ ids_lds = nullptr) {
+  const int lane = threadIdx.x & 63;
+  const float my_v = key_value(r.mine);
   const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
   const float ex = lane < k ? expf(my_v - top) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    const int my_e = key_index(mine);
+    const int my_e = key_index(r.mine);
     ids_out[lane] = my_e;
     gates_out[lane] = ex / sum;
     if (ids_lds) ids_lds[lane] = my_e;
   }
-  if (margin_out && lane == 0) *margin_out = k < E ? key_value(last) - key_value(next) : INFINITY;
+  if (margin_out && lane == 0) *margin_out = k < E ? key_value(r.last) - key_value(r.next) : INFINITY;
+}
+
+// Top-k of one token: logits row [E] -> ids[k], gates[k], margin.
+template <int VPL>
+__device__ void wave_topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
+                              float* __restrict__ gates_out, float* __restrict__ margin_out,
+                              int32_t* __restrict__ ids_lds = nullptr) {
+  const TopkKeys r = wave_topk_keys<VPL>(row, E, k);
+  topk_write(r, E, k, ids_out, gates_out, margin_out, ids_lds);
 }
 
 }  // namespace moe

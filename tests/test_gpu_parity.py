@@ -216,8 +216,11 @@ def test_steps_match_fused_layer():
         assert OL.rel_max_err(y_h[p], ref) <= OUT_TOL, f"row {p}"
     ref_out, *_ = hl.oracle_forward(x)
     assert OL.rel_max_err(host(out), ref_out) <= OUT_TOL
+    # The fused layer addresses a decode batch's entries directly (top-k inside
+    # the gate/up launch, combine inside the down launch, one wave per entry);
+    # the steps sum the same products in another fixed order.
     out_f, *_ = run_layer(d, x, T)
-    np.testing.assert_array_equal(host(out), out_f)     # same kernels, same bits
+    assert OL.rel_max_err(host(out), out_f.astype(np.float64)) <= 1e-5
 
 
 # ------------------------------------------------------------------ prefill (MFMA grouped GEMM)

@@ -10,8 +10,9 @@ Cache from serving the weights, steps rotate over ``--rotate`` distinct layers
 (each with its own weights) and a pool of distinct token batches.
 
 Prints one JSON line with the throughput, the dominant kernel's roofline
-(algorithmic bytes / its average duration measured with HIP events on its
-stream), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+(algorithmic bytes / its average duration, measured with HIP events that the
+runtime stamps from that kernel's own dispatch on its stream), and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -116,7 +117,9 @@ def bench_prefill(steps):
     counts = np.bincount(ids_h.reshape(-1), minlength=E)
     # algorithmic FLOPs: router 2*T*H*E + every (token, expert) pair incl. the shared one: 6*H*I each
     flops = 2.0 * T * H * E + T * (k + 1) * 6.0 * H * I
-    big = counts >= 32
+    # a prompt-sized chunk (T >= 1024) sends every non-empty group to the GEMM,
+    # smaller batches the groups of 32 or more entries
+    big = counts >= (1 if T >= 1024 else 32)
     gemm_rows = int(counts[big].sum()) + T        # shared expert rows all go to the GEMM
     gemm_flops_gu = gemm_rows * 4.0 * H * I
     gemm_flops_dn = gemm_rows * 2.0 * H * I
@@ -412,7 +415,7 @@ def main():
                    "layer_GBps": step_bytes1 / (ms1_step * 1e-3) / 1e9},
         },
         "roofline": {
-            "kernel": "k_gemv_quant (gate/up + SwiGLU, 2-bit dequant-GEMV)",
+            "kernel": "k_decode_gateup (top-k, gate/up + SwiGLU 2-bit dequant-GEMV, down-table epilogue)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -192,11 +192,17 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                              int32_t* miss_rows, int32_t* n_miss,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Measurement support.  Records start_event / stop_event (hipEvent_t, created by
- * the caller) on the call's stream immediately before and after the NEXT launch of
- * the named kernel by any call above, then forgets them (one-shot).  Lets a
- * benchmark time one kernel of a fused call with events on the stream it runs on.
- * Process-global and not thread-safe: meant for benchmarks only. */
+/* Measurement support.  Arms start_event / stop_event (hipEvent_t, created by
+ * the caller) for the NEXT launch of the named kernel by any call above, then
+ * forgets them (one-shot).  The events are attached to that kernel's dispatch
+ * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is the kernel's own
+ * execution time on the stream it runs on, as a kernel trace reports it, without
+ * the dispatch gap in front of it.  Where the named step is two launches (the
+ * small-batch router front end), the interval runs from the first one's start to
+ * the second one's end.  If the step launches nothing, both events are recorded
+ * on the stream back to back.  Returns MOE_EINVAL for an unknown kernel or one
+ * event NULL and the other not; both NULL disarms.  Process-global and not
+ * thread-safe: meant for benchmarks only. */
 enum {
   MOE_KERNEL_ROUTER = 0,       /* router logits (GEMV or MFMA GEMM) */
   MOE_KERNEL_GATEUP_GEMV = 1,  /* dequant-GEMV gate/up + SwiGLU */

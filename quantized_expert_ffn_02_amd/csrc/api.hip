@@ -9,6 +9,11 @@
 
 using namespace moe;
 
+moe::LaunchEvents& moe::launch_events() {
+  static LaunchEvents ev;
+  return ev;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -126,19 +131,26 @@ struct TimedLaunch {
 };
 TimedLaunch g_timed[MOE_KERNEL_COUNT];
 
-// Runs ``launch`` bracketed by the pending events of ``kernel`` (if any).
+// Runs ``launch`` with the pending events of ``kernel`` (if any) attached to
+// its kernel launches (MOE_LAUNCH); if it launched nothing, both events are
+// recorded on the stream so that they still hold a valid (empty) interval.
 template <typename F>
 hipError_t timed(int kernel, hipStream_t s, F&& launch) {
   TimedLaunch t = g_timed[kernel];
-  if (t.start) {
-    g_timed[kernel] = TimedLaunch();
-    hipError_t e = hipEventRecord(t.start, s);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    return hipEventRecord(t.stop, s);
+  if (!t.start) return launch();
+  g_timed[kernel] = TimedLaunch();
+  LaunchEvents& ev = launch_events();
+  ev.start = t.start;
+  ev.stop = t.stop;
+  hipError_t e = launch();
+  const bool none = ev.start != nullptr;
+  ev = LaunchEvents();
+  if (e != hipSuccess) return e;
+  if (none) {
+    e = hipEventRecord(t.start, s);
+    if (e == hipSuccess) e = hipEventRecord(t.stop, s);
   }
-  return launch();
+  return e;
 }
 
 #define MOE_TRY(expr)                   \

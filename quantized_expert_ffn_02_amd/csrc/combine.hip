@@ -59,7 +59,7 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, c
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
   dim3 grid((H / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared,
+  MOE_LAUNCH(k_combine, grid, dim3(256), 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared,
                      residual, out, out_bf16);
   return hipGetLastError();
 }
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const uint16_t* __restrict
 
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(T), dim3(256), 0, s, x, H, eps, out);
+  MOE_LAUNCH(k_rmsnorm_bf16, dim3(T), dim3(256), 0, s, x, H, eps, out);
   return hipGetLastError();
 }
 
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t* __restrict__ p, siz
 hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 4;
   const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
-  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, s, (uint32_t*)ws, n);
+  MOE_LAUNCH(k_fill_zero, dim3(blocks), dim3(256), 0, s, (uint32_t*)ws, n);
   return hipGetLastError();
 }
 

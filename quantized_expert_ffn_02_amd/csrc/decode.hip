@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict_
 
 hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s) {
-  hipLaunchKernelGGL(k_router_gemv, dim3((E + 3) / 4), dim3(256), 0, s, x, T, wr, bias, E, H, logits);
+  MOE_LAUNCH(k_router_gemv, dim3((E + 3) / 4), dim3(256), 0, s, x, T, wr, bias, E, H, logits);
   return hipGetLastError();
 }
 
@@ -194,22 +194,22 @@ __global__ __launch_bounds__(256) void k_route_select(SmallRouteArgs a) {
 }
 
 hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  MOE_LAUNCH(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  MOE_LAUNCH(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
   if (a.E <= 64)
-    hipLaunchKernelGGL(k_route_select<1>, dim3(1), dim3(256), 0, s, a);
+    MOE_LAUNCH(k_route_select<1>, dim3(1), dim3(256), 0, s, a);
   else if (a.E <= 128)
-    hipLaunchKernelGGL(k_route_select<2>, dim3(1), dim3(256), 0, s, a);
+    MOE_LAUNCH(k_route_select<2>, dim3(1), dim3(256), 0, s, a);
   else if (a.E <= 256)
-    hipLaunchKernelGGL(k_route_select<4>, dim3(1), dim3(256), 0, s, a);
+    MOE_LAUNCH(k_route_select<4>, dim3(1), dim3(256), 0, s, a);
   else if (a.E <= 512)
-    hipLaunchKernelGGL(k_route_select<8>, dim3(1), dim3(256), 0, s, a);
+    MOE_LAUNCH(k_route_select<8>, dim3(1), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_route_select<16>, dim3(1), dim3(256), 0, s, a);
+    MOE_LAUNCH(k_route_select<16>, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -271,13 +271,13 @@ static hipError_t launch_gateup_t(const DecodeFfnArgs& a, hipStream_t s) {
   r.codes, r.hi, r.scales, sh.codes, sh.hi, sh.scales, r.code_stride, r.hi_stride, r.scale_stride, a.H, a.I, a.T, \
       a.k, a.E, a.logits, a.ids, a.gates, a.margin, a.xpairs, a.xinit, a.hpairs, a.hinit
   if (nch <= 8)
-    hipLaunchKernelGGL((k_decode_gateup<Q3, 8, 1, VPL>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_gateup<Q3, 8, 1, VPL>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
   else if (nch <= 16)
-    hipLaunchKernelGGL((k_decode_gateup<Q3, 8, 2, VPL>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_gateup<Q3, 8, 2, VPL>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
   else if (nch <= 40)
-    hipLaunchKernelGGL((k_decode_gateup<Q3, 8, 5, VPL>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_gateup<Q3, 8, 5, VPL>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
   else
-    hipLaunchKernelGGL((k_decode_gateup<Q3, 16, 4, VPL>), grid, dim3(1024), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_gateup<Q3, 16, 4, VPL>), grid, dim3(1024), 0, s, MOE_DEC_ARGS);
 #undef MOE_DEC_ARGS
   return hipGetLastError();
 }
@@ -300,11 +300,11 @@ static hipError_t launch_down_t(const DecodeFfnArgs& a, hipStream_t s) {
   r.codes, r.hi, r.scales, sh.codes, sh.hi, sh.scales, r.code_stride, r.hi_stride, r.scale_stride, a.H, a.I, \
       a.T, a.k, a.E, a.ids, a.gates, a.hpairs, a.hinit, a.y
   if (nch <= 10 && a.T == 1)
-    hipLaunchKernelGGL((k_decode_down<Q3, 10, 1>), grid, dim3(640), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_down<Q3, 10, 1>), grid, dim3(640), 0, s, MOE_DEC_ARGS);
   else if (nch <= 10)
-    hipLaunchKernelGGL((k_decode_down<Q3, 5, 2>), grid, dim3(320), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_down<Q3, 5, 2>), grid, dim3(320), 0, s, MOE_DEC_ARGS);
   else
-    hipLaunchKernelGGL((k_decode_down<Q3, 8, 4>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
+    MOE_LAUNCH((k_decode_down<Q3, 8, 4>), grid, dim3(512), 0, s, MOE_DEC_ARGS);
 #undef MOE_DEC_ARGS
   return hipGetLastError();
 }
@@ -315,7 +315,7 @@ hipError_t launch_decode_down(const DecodeFfnArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s) {
   dim3 grid((a.H / 4 + 255) / 256, a.T);
-  hipLaunchKernelGGL(k_decode_combine, grid, dim3(256), 0, s, a.y, a.T, a.k, a.H, a.with_shared, a.residual, a.out,
+  MOE_LAUNCH(k_decode_combine, grid, dim3(256), 0, s, a.y, a.T, a.k, a.H, a.with_shared, a.residual, a.out,
                      a.out_bf16);
   return hipGetLastError();
 }

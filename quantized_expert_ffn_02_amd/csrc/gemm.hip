@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_x_to_f16_pairs(const uint16_t* __restri
 hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s) {
   const size_t n16 = (size_t)T * H / 16;
   const int blocks = (int)((n16 + 255) / 256 < 2048 ? (n16 + 255) / 256 : 2048);
-  hipLaunchKernelGGL(k_x_to_f16_pairs, dim3(blocks), dim3(256), 0, s, x, n16, out);
+  MOE_LAUNCH(k_x_to_f16_pairs, dim3(blocks), dim3(256), 0, s, x, n16, out);
   return hipGetLastError();
 }
 
@@ -360,11 +360,11 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   if (kind == GemvKind::GateUp) {
-    hipLaunchKernelGGL(k_gemm_q2<true>, dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
+    MOE_LAUNCH(k_gemm_q2<true>, dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
                        shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
                        sorted_rows, T, k, a_f16, (uint16_t*)out, nullptr);
   } else {
-    hipLaunchKernelGGL(k_gemm_q2<false>, dim3(max_tiles, H / GCOLS), dim3(256), 0, s, routed.codes, routed.scales,
+    MOE_LAUNCH(k_gemm_q2<false>, dim3(max_tiles, H / GCOLS), dim3(256), 0, s, routed.codes, routed.scales,
                        shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
                        nullptr, T, k, a_f16, nullptr, (float*)out);
   }
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
 hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s) {
   dim3 grid((T + BM - 1) / BM, (E + BN - 1) / BN);
-  hipLaunchKernelGGL(k_router_mfma, grid, dim3(256), 0, s, x, T, wr, bias, E, H, logits);
+  MOE_LAUNCH(k_router_mfma, grid, dim3(256), 0, s, x, T, wr, bias, E, H, logits);
   return hipGetLastError();
 }
 
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 
 hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_per, int32_t* tiles,
                        int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, offsets, E, min_rows, items_per, tiles, n_tiles, items,
+  MOE_LAUNCH(k_plan, dim3(1), dim3(1024), 0, s, offsets, E, min_rows, items_per, tiles, n_tiles, items,
                      n_items);
   return hipGetLastError();
 }

@@ -52,9 +52,9 @@ hipError_t launch_prep_table_bf16(const uint16_t* x, int rows, int K, bool q3, u
                                   hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (q3)
-    hipLaunchKernelGGL(k_prep_table_bf16<true>, dim3(rows), dim3(256), 0, s, x, K, pairs, init);
+    MOE_LAUNCH(k_prep_table_bf16<true>, dim3(rows), dim3(256), 0, s, x, K, pairs, init);
   else
-    hipLaunchKernelGGL(k_prep_table_bf16<false>, dim3(rows), dim3(256), 0, s, x, K, pairs, init);
+    MOE_LAUNCH(k_prep_table_bf16<false>, dim3(rows), dim3(256), 0, s, x, K, pairs, init);
   return hipGetLastError();
 }
 
@@ -62,9 +62,9 @@ hipError_t launch_prep_table_f32(const float* h, int rows, int K, bool q3, uint3
                                  hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (q3)
-    hipLaunchKernelGGL(k_prep_table_f32<true>, dim3(rows), dim3(256), 0, s, h, K, pairs, init);
+    MOE_LAUNCH(k_prep_table_f32<true>, dim3(rows), dim3(256), 0, s, h, K, pairs, init);
   else
-    hipLaunchKernelGGL(k_prep_table_f32<false>, dim3(rows), dim3(256), 0, s, h, K, pairs, init);
+    MOE_LAUNCH(k_prep_table_f32<false>, dim3(rows), dim3(256), 0, s, h, K, pairs, init);
   return hipGetLastError();
 }
 
@@ -78,7 +78,7 @@ hipError_t launch_bf16_rows_to_f32(const uint16_t* x, int rows, int K, float* ou
   const size_t n = (size_t)rows * K;
   if (!n) return hipSuccess;
   const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-  hipLaunchKernelGGL(k_bf16_rows_to_f32, dim3(blocks), dim3(256), 0, s, x, n, out);
+  MOE_LAUNCH(k_bf16_rows_to_f32, dim3(blocks), dim3(256), 0, s, x, n, out);
   return hipGetLastError();
 }
 
@@ -282,17 +282,17 @@ static hipError_t launch_quant_t(const MatRef& r, const MatRef& sh, int N, int K
   r.codes, r.hi, r.scales, sh.codes, sh.hi, sh.scales, r.code_stride, r.hi_stride, r.scale_stride, N, K, inter, \
       P.sorted_rows, P.items, P.n_items, P.T, P.k, P.E, tab.pairs, tab.init, out, dp, di, P.slot_map
   if (KIND == GemvKind::GateUp && nch == 40) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
+    MOE_LAUNCH((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (KIND == GemvKind::Down && nch == 10) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 5, 2, 4>), grid, dim3(320), 0, s, MOE_GEMV_ARGS);
+    MOE_LAUNCH((k_gemv_quant<KIND, Q3, 5, 2, 4>), grid, dim3(320), 0, s, MOE_GEMV_ARGS);
   } else if (nch <= 8) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 1, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
+    MOE_LAUNCH((k_gemv_quant<KIND, Q3, 8, 1, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (nch <= 16) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 2, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
+    MOE_LAUNCH((k_gemv_quant<KIND, Q3, 8, 2, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (nch <= 40) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
+    MOE_LAUNCH((k_gemv_quant<KIND, Q3, 8, 5, 4>), grid, dim3(512), 0, s, MOE_GEMV_ARGS);
   } else if (nch <= 64) {
-    hipLaunchKernelGGL((k_gemv_quant<KIND, Q3, 16, 4, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
+    MOE_LAUNCH((k_gemv_quant<KIND, Q3, 16, 4, 4>), grid, dim3(1024), 0, s, MOE_GEMV_ARGS);
   } else {
     return hipErrorInvalidValue;
   }
@@ -387,10 +387,10 @@ hipError_t launch_gemv_dense(GemvKind kind, const MatRef& routed, const MatRef& 
                              hipStream_t s) {
   if (max_groups <= 0) return hipSuccess;
   if (kind == GemvKind::GateUp)
-    hipLaunchKernelGGL((k_gemv_dense<GemvKind::GateUp, 4>), dim3(max_groups, inter / 64), dim3(256), 0, s, routed,
+    MOE_LAUNCH((k_gemv_dense<GemvKind::GateUp, 4>), dim3(max_groups, inter / 64), dim3(256), 0, s, routed,
                        shared, N, K, inter, perm, in_rows, out);
   else
-    hipLaunchKernelGGL((k_gemv_dense<GemvKind::Down, 2>), dim3(max_groups, N / 64), dim3(128), 0, s, routed,
+    MOE_LAUNCH((k_gemv_dense<GemvKind::Down, 2>), dim3(max_groups, N / 64), dim3(128), 0, s, routed,
                        shared, N, K, inter, perm, in_rows, out);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,25 @@
 #include "../../include/moe.h"
 
 namespace moe {
+
+// Every kernel launch goes through MOE_LAUNCH.  Inside a timed section (the
+// C-ABI timing hook) the first launch carries the pending start event and
+// every launch the stop event; hipExtLaunchKernel has the runtime stamp them
+// from the kernel's own execution, so the elapsed time is kernel time, not
+// kernel time plus the stream's dispatch gap.  Not thread-safe: the hook is a
+// single-threaded measurement aid.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+#define MOE_LAUNCH(kernel, grid, block, shmem, stream, ...)                                              \
+  do {                                                                                                  \
+    ::moe::LaunchEvents& ev_ = ::moe::launch_events();                                                  \
+    hipEvent_t start_ = ev_.start;                                                                      \
+    ev_.start = nullptr;                                                                                \
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, start_, ev_.stop, 0u, __VA_ARGS__);        \
+  } while (0)
 
 // One weight matrix of a bank: [n_experts] x [N rows x K cols].
 struct MatRef {

@@ -131,9 +131,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shar
   const int Tk = T * k;
   const int n = Tk + (with_shared ? T : 0);
   const int nc = permute_chunks(n);
-  hipLaunchKernelGGL(k_perm_hist, dim3(nc), dim3(256), 0, s, ids, Tk, n, E, counts);
-  hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets);
-  hipLaunchKernelGGL(k_perm_scatter, dim3(nc), dim3(64), 0, s, ids, Tk, n, E, base, sorted_rows, row_to_sorted);
+  MOE_LAUNCH(k_perm_hist, dim3(nc), dim3(256), 0, s, ids, Tk, n, E, counts);
+  MOE_LAUNCH(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets);
+  MOE_LAUNCH(k_perm_scatter, dim3(nc), dim3(64), 0, s, ids, Tk, n, E, base, sorted_rows, row_to_sorted);
   return hipGetLastError();
 }
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(1024) void k_items_from_offsets(const int32_t* __re
 
 hipError_t launch_items_from_offsets(const int32_t* offsets, int E, int items_per, int32_t* items,
                                      int32_t* n_items, hipStream_t s) {
-  hipLaunchKernelGGL(k_items_from_offsets, dim3(1), dim3(1024), 0, s, offsets, E, items_per, items, n_items);
+  MOE_LAUNCH(k_items_from_offsets, dim3(1), dim3(1024), 0, s, offsets, E, items_per, items, n_items);
   return hipGetLastError();
 }
 
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(1024) void k_miss_list(const int32_t* __restrict__ 
 
 hipError_t launch_miss_list(const int32_t* ids, int Tk, const int32_t* slot_map, int32_t* miss_rows, int32_t* n_miss,
                             hipStream_t s) {
-  hipLaunchKernelGGL(k_miss_list, dim3(1), dim3(1024), 0, s, ids, Tk, slot_map, miss_rows, n_miss);
+  MOE_LAUNCH(k_miss_list, dim3(1), dim3(1024), 0, s, ids, Tk, slot_map, miss_rows, n_miss);
   return hipGetLastError();
 }
 

@@ -31,15 +31,15 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
                        hipStream_t s) {
   dim3 grid((T + 3) / 4);
   if (E <= 64)
-    hipLaunchKernelGGL(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
+    MOE_LAUNCH(k_topk<1>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
   else if (E <= 128)
-    hipLaunchKernelGGL(k_topk<2>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
+    MOE_LAUNCH(k_topk<2>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
   else if (E <= 256)
-    hipLaunchKernelGGL(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
+    MOE_LAUNCH(k_topk<4>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
   else if (E <= 512)
-    hipLaunchKernelGGL(k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
+    MOE_LAUNCH(k_topk<8>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
   else
-    hipLaunchKernelGGL(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
+    MOE_LAUNCH(k_topk<16>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin);
   return hipGetLastError();
 }
 

@@ -176,10 +176,13 @@ int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float
   return MOE_OK;
 }
 
+// y16 (with gates): the prompt path, every group on the MFMA GEMM, whose down
+// projection writes gate-scaled fp16 rows instead of fp32 y_sorted; no GEMV.
 int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef& perm, int n_entries,
                   float* y_sorted, void* ws, const Layout& lay, hipStream_t s, bool x_table_ready = false,
                   const int32_t* gemm_tiles = nullptr, const int32_t* n_gemm_tiles = nullptr,
-                  const moe_bank_t* routed_override = nullptr) {
+                  const moe_bank_t* routed_override = nullptr, const float* gates = nullptr,
+                  uint16_t* y16 = nullptr) {
   const moe_bank_t& rb = routed_override ? *routed_override : L->routed;
   const int H = L->hidden, I = L->inter, E = L->n_experts;
   // upper bound on GEMV work items: every entry, or, when the MFMA GEMM takes
@@ -204,7 +207,7 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
   xt.pairs = at<uint32_t>(ws, lay.xtab_pairs);
   xt.init = at<float>(ws, lay.xtab_init);
   xt.sets = q3 ? 2 : 1;
-  if (!x_table_ready)
+  if (!x_table_ready && !y16)
     MOE_TRY(launch_prep_table_bf16(x, T, H, q3, const_cast<uint32_t*>(xt.pairs), const_cast<float*>(xt.init), s));
   TableRef ht;
   ht.pairs = at<uint32_t>(ws, lay.htab_pairs);
@@ -222,16 +225,19 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
                             perm.sorted_rows, T, perm.k, xf, hf, s);
     }));
   }
-  MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] {
-    return launch_gemv_quant(GemvKind::GateUp, rb.fmt, r13, s13, 2 * I, H, I, perm, max_groups, xt, h,
-                             const_cast<uint32_t*>(ht.pairs), const_cast<float*>(ht.init), s);
-  }));
-  if (gemm) {
-    MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
-      return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles, nullptr, T,
-                            perm.k, hf, y_sorted, s);
+  if (!y16) {
+    MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] {
+      return launch_gemv_quant(GemvKind::GateUp, rb.fmt, r13, s13, 2 * I, H, I, perm, max_groups, xt, h,
+                               const_cast<uint32_t*>(ht.pairs), const_cast<float*>(ht.init), s);
     }));
   }
+  if (gemm) {
+    MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
+      return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles,
+                            perm.sorted_rows, T, perm.k, hf, y_sorted, s, gates, y16);
+    }));
+  }
+  if (y16) return MOE_OK;
   MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] {
     return launch_gemv_quant(GemvKind::Down, rb.fmt, r2, s2, H, I, I, perm, max_groups, ht, y_sorted, nullptr,
                              nullptr, s);
@@ -459,10 +465,15 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   perm.k = k;
   perm.E = E;
   float* y = at<float>(ws, lay.y);
+  // a prompt-sized chunk puts every group on the GEMM: gate-scaled fp16 rows
+  uint16_t* y16 = gemm && mfma_min_rows(T) == 1 ? at<uint16_t>(ws, lay.y) : nullptr;
   int rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s, x_table_ready, gemm ? at<int32_t>(ws, lay.tiles) : nullptr,
-                         gemm ? at<int32_t>(ws, lay.n_tiles) : nullptr);
+                         gemm ? at<int32_t>(ws, lay.n_tiles) : nullptr, nullptr, gates, y16);
   if (rc) return rc;
-  MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
+  if (y16)
+    MOE_TRY(launch_combine16(y16, inv, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
+  else
+    MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
   return MOE_OK;
 }
 

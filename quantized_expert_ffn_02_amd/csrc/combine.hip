@@ -64,6 +64,64 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, c
   return hipGetLastError();
 }
 
+// The same combine over fp16 rows that already carry their gate (the prompt
+// path's down GEMM writes them): out[t] = sum_i y16[row_to_sorted[t k + i]]
+// (i = 0..k-1) + y16[row_to_sorted[T k + t]] (+ residual), summed in fp32 in
+// that order.  Eight consecutive outputs per thread.
+__global__ __launch_bounds__(256) void k_combine16(const uint16_t* __restrict__ y16,
+                                                   const int32_t* __restrict__ row_to_sorted, int T, int k, int H,
+                                                   int with_shared, const uint16_t* __restrict__ residual,
+                                                   float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+  const int t = blockIdx.y;
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;   // index of 8 consecutive outputs
+  if (q * 8 >= H) return;
+  const size_t H8 = H / 8;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  const int n = k + (with_shared ? 1 : 0);
+  for (int i = 0; i < n; ++i) {
+    const size_t r = i < k ? (size_t)t * k + i : (size_t)T * k + t;
+    const size_t p = (size_t)row_to_sorted[r];
+    const uint4 v = reinterpret_cast<const uint4*>(y16)[p * H8 + q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += fp16_to_f32(w[j] & 0xFFFFu);
+      acc[2 * j + 1] += fp16_to_f32(w[j] >> 16);
+    }
+  }
+  if (residual) {
+    const uint4 rb = reinterpret_cast<const uint4*>(residual + (size_t)t * H)[q];
+    const uint32_t w[4] = {rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += bf16_to_f32(w[j] & 0xFFFFu);
+      acc[2 * j + 1] += bf16_to_f32(w[j] >> 16);
+    }
+  }
+  float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * q;
+  o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (out_bf16) {
+    uint4 b;
+    b.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    b.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    b.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    b.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    reinterpret_cast<uint4*>(out_bf16 + (size_t)t * H)[q] = b;
+  }
+}
+
+hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,
+                            const uint16_t* residual, float* out, uint16_t* out_bf16, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  dim3 grid((H / 8 + 255) / 256, T);
+  MOE_LAUNCH(k_combine16, grid, dim3(256), 0, s, y16, row_to_sorted, T, k, H, with_shared, residual, out,
+             out_bf16);
+  return hipGetLastError();
+}
+
 // Parameter-free RMSNorm of each bf16 row: bf16(x / sqrt(mean(x^2) + eps)), one
 // block per row, fixed-order fp32 reduction (the input of every layer of a stack).
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const uint16_t* __restrict__ x, int H, float eps,

@@ -100,7 +100,7 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 // the exponent of 1024 gives the fp16 value 1024 + c 4^q; one v_pk_fma_f16 turns
 // it into c - 2 (exact) and one v_pk_mul_f16 applies the block scale (exact).
 // ---------------------------------------------------------------------------
-static constexpr int GBM = 128;              // rows per M-tile
+static constexpr int GBM = 128;              // rows per M-tile (32 x fragments per wave)
 static constexpr int GBK = 64;               // K per pipeline step
 static constexpr int A_STRIDE = GBK + 8;     // halves per LDS row
 static constexpr int GCOLS = 256;            // weight rows per block (4 waves x 64)
@@ -146,10 +146,9 @@ __device__ __forceinline__ h2_t scale_pair(uint32_t d, bool hi) {
   return __builtin_bit_cast(h2_t, v);
 }
 
-// Registers of one pipeline step: 64 K of A for this thread's LDS row slice and
-// the codes + scales of the wave's two B columns.
-struct StepRegs {
-  u32x4 a0, a1, a2, a3;
+// Registers of one pipeline step: the codes + scales of the wave's two B
+// columns for 64 K.
+struct BRegs {
   u32x4 c0, c1;
   uint32_t s0, s1;
 };
@@ -171,14 +170,25 @@ __device__ __forceinline__ BCol b_column(const uint8_t* codes, const uint16_t* s
 
 // step kc: codes at + kc * 64 uint4; scales of blocks 2kc, 2kc+1 at dword
 // (kc / 2) * 128 + (kc % 2)
-__device__ __forceinline__ void load_b(const BCol& b, int kc, u32x4& c, uint32_t& s) {
-  c = b.codes[(size_t)kc * 64];
-  s = b.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
+__device__ __forceinline__ void load_b(const BCol& b0, const BCol& b1, int kc, BRegs& R) {
+  R.c0 = b0.codes[(size_t)kc * 64];
+  R.s0 = b0.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
+  R.c1 = b1.codes[(size_t)kc * 64];
+  R.s1 = b1.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
 }
 
-// One K step of a wave: 4 x (2 B fragments, 4 A fragments, 8 MFMAs).
-__device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const StepRegs& R, int shift,
-                                          const BConst& bc, f16x_t acc[4][2]) {
+// Keeps the unpacking of a B register set inside the step that consumes it:
+// without this the scheduler hoists it into earlier steps, right behind the
+// set's loads, and the wave waits for loads it issued two steps ahead.
+__device__ __forceinline__ void pin_b(BRegs& R) {
+  asm volatile("" : "+v"(R.c0), "+v"(R.c1), "+v"(R.s0), "+v"(R.s1));
+}
+
+// One K step of a wave: 4 x (2 B fragments, NMI A fragments, 2 NMI MFMAs);
+// NMI = number of 32-row fragments the tile's rows need.
+template <int NMI, int MAXNMI>
+__device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const BRegs& R, int shift,
+                                          const BConst& bc, f16x_t acc[MAXNMI][2]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, kh = (lane >> 5) * 8;
   const uint32_t cw0[4] = {R.c0.x, R.c0.y, R.c0.z, R.c0.w};
@@ -188,7 +198,7 @@ __device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const
     const h8_t b0 = b_frag(cw0[s] >> shift, scale_pair(R.s0, s >= 2), bc);
     const h8_t b1 = b_frag(cw1[s] >> shift, scale_pair(R.s1, s >= 2), bc);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < NMI; ++mi) {
       const h8_t a = *reinterpret_cast<const h8_t*>(As + (mi * 32 + r) * A_STRIDE + s * 16 + kh);
       acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[mi][0], 0, 0, 0);
       acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[mi][1], 0, 0, 0);
@@ -236,137 +246,247 @@ __device__ __forceinline__ bool load_tile(const int32_t* __restrict__ tiles, con
 //           rows; the epilogue writes h = SiLU(gate) * up in fp16, pair order.
 //   Down:   rows p are rows of h (K = I); wave w of column tile j owns output
 //           columns 256 j + 64 w + (0..63); the epilogue writes fp32 y.
-// K / 64 (the number of steps) is even: H and I are multiples of 128.
+// Pipeline: A (shared through three LDS buffers) and the wave's B codes are both
+// loaded two steps ahead of their use.  A tile of fewer than 128 rows runs
+// only the 32-row fragments it needs (NMI = ceil(rows / 32)).
 // ---------------------------------------------------------------------------
-template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_gemm_q2(
-    const uint8_t* __restrict__ r_codes, const uint16_t* __restrict__ r_scales, const uint8_t* __restrict__ s_codes,
-    const uint16_t* __restrict__ s_scales, size_t code_stride, size_t scale_stride, int H, int I, int E,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ sorted_rows,
-    int T, int k, const uint16_t* __restrict__ a_src, uint16_t* __restrict__ h_out, float* __restrict__ y_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * A_STRIDE];
-  GemmTile t;
-  if (!load_tile(tiles, n_tiles, t)) return;
+struct GemmArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  int H, I, T, k;
+  const int32_t* sorted_rows;
+  const uint16_t* a_src;
+  uint16_t* h_out;
+  float* y_out;           // down, fp32 rows (NULL when y16 is used)
+  uint16_t* y16;          // down, fp16 rows already multiplied by their entry's gate
+  const float* row_gate;  // LDS: gate of each of the tile's rows (y16 only)
+};
+
+// MAXNMI = 32-row fragments per wave (tile height 32 MAXNMI); NMI <= MAXNMI the
+// fragments this tile's rows need.  As holds three LDS buffers of the A tile.
+template <bool GATEUP, int NMI, int MAXNMI>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, uint16_t* As) {
+  constexpr int BMX = 32 * MAXNMI;          // tile rows
+  constexpr int RPT = MAXNMI / 4;           // A rows staged per thread (256 threads, 2 per row)
+  constexpr int ABUF = BMX * A_STRIDE;      // halves per LDS buffer
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool sh = t.g == E;
-  const size_t eidx = sh ? 0 : (size_t)t.g;
-  const uint8_t* codes = (sh ? s_codes : r_codes) + eidx * code_stride;
-  const uint16_t* scales = (sh ? s_scales : r_scales) + eidx * scale_stride;
-  const int K = GATEUP ? H : I;
+  const int K = GATEUP ? g.H : g.I;
   const int nch = K / GBK;
 
-  // A staging: thread -> (row ra = tid / 2, 32-half slice ha = tid % 2) of the step
+  // A staging: thread -> rows ra + 128 j (j < RPT), 32-half slice ha of the
+  // step.  Rows past the tile's rows load its first row (no lane-divergent
+  // branch around the loads; LDS rows past NMI * 32 are never read).
   const int ra = tid >> 1, ha = tid & 1;
-  const int pa = t.m0 + (ra < t.rows ? ra : 0);
-  size_t arow;
-  if (GATEUP) {
-    const int r = sorted_rows[pa];
-    const int Tk = T * k;
-    arow = (size_t)(r < Tk ? r / k : r - Tk);
-  } else {
-    arow = (size_t)pa;
+  const u32x4* ag[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int rr = ra + 128 * j;
+    const int pa = t.m0 + (rr < t.rows ? rr : 0);
+    size_t arow;
+    if (GATEUP) {
+      const int r = g.sorted_rows[pa];
+      const int Tk = g.T * g.k;
+      arow = (size_t)(r < Tk ? r / g.k : r - Tk);
+    } else {
+      arow = (size_t)pa;
+    }
+    ag[j] = reinterpret_cast<const u32x4*>(g.a_src + arow * K) + ha * 4;
   }
-  const u32x4* __restrict__ ag = reinterpret_cast<const u32x4*>(a_src + arow * K) + ha * 4;
-  uint16_t* const as_dst0 = &As[0][ra * A_STRIDE + ha * 32];
-  uint16_t* const as_dst1 = &As[1][ra * A_STRIDE + ha * 32];
+  const int a_off = ra * A_STRIDE + ha * 32;
 
   // B columns of this lane
   int n0, n1;
   if (GATEUP) {
     n0 = t.n * 128 + wv * 32 + (lane & 31);
-    n1 = I + n0;
+    n1 = g.I + n0;
   } else {
     n0 = t.n * GCOLS + wv * 64 + (lane & 31);
     n1 = n0 + 32;
   }
-  const BCol B0 = b_column(codes, scales, n0, K);
-  const BCol B1 = b_column(codes, scales, n1, K);
+  const BCol B0 = b_column(g.codes, g.scales, n0, K);
+  const BCol B1 = b_column(g.codes, g.scales, n1, K);
   const int shift = (lane >> 5) * 8;
   const BConst bc = bconst();
 
-  f16x_t acc[4][2];
+  f16x_t acc[MAXNMI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MAXNMI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto load_step = [&](StepRegs& R, int kc) {
-    R.a0 = ag[kc * 8 + 0];
-    R.a1 = ag[kc * 8 + 1];
-    R.a2 = ag[kc * 8 + 2];
-    R.a3 = ag[kc * 8 + 3];
-    load_b(B0, kc, R.c0, R.s0);
-    load_b(B1, kc, R.c1, R.s1);
+  // Loads past the last step re-load the last step (index clamped): every load
+  // is unconditional, so the wait counts before each use stay exact.
+  struct ARegs {
+    u32x4 a[RPT][4];
   };
-  auto store_a = [&](const StepRegs& R, uint16_t* dst) {
-    u32x4* d = reinterpret_cast<u32x4*>(dst);
-    d[0] = R.a0;
-    d[1] = R.a1;
-    d[2] = R.a2;
-    d[3] = R.a3;
+  auto load_a = [&](int kc, ARegs& R) {
+    kc = kc < nch ? kc : nch - 1;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) R.a[j][q] = ag[j][kc * 8 + q];
   };
+  auto store_a = [&](const ARegs& R, int buf) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      u32x4* d = reinterpret_cast<u32x4*>(As + buf * ABUF + a_off + 128 * j * A_STRIDE);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = R.a[j][q];
+    }
+  };
+  auto load_bc = [&](int kc, BRegs& R) { load_b(B0, B1, kc < nch ? kc : nch - 1, R); };
 
-  // Two register sets; the loop is unrolled by two so both keep static names.
-  // Step kc computes from LDS buffer kc % 2 and register set kc % 2 while the
-  // loads of step kc + 1 (other set) are in flight.
-  StepRegs R0, R1;
-  load_step(R0, 0);
-  store_a(R0, as_dst0);
+  // The loop is unrolled by three so that every rotating resource has a static
+  // name.  Step m computes from LDS buffer m % 3 and B register set m % 3; it
+  // first writes A of step m + 1 (register set (m + 1) % 3, loaded two steps
+  // earlier) into LDS buffer (m + 1) % 3, then issues the loads of A for step
+  // m + 3 and of B for step m + 2.  Both operands get two steps of latency
+  // cover; the scheduling barrier keeps the loads at the top of the step.
+  ARegs AX, AY, AZ;
+  BRegs BX, BY, BZ;
+  load_a(0, AX);
+  load_bc(0, BX);
+  load_a(1, AY);
+  load_bc(1, BY);
+  load_a(2, AZ);
+  store_a(AX, 0);
   __syncthreads();
-  for (int kc = 0; kc < nch; kc += 2) {
-    load_step(R1, kc + 1);
-    wave_step(As[0], R0, shift, bc, acc);
-    store_a(R1, as_dst1);
-    __syncthreads();
-    if (kc + 2 < nch) load_step(R0, kc + 2);
-    wave_step(As[1], R1, shift, bc, acc);
-    if (kc + 2 < nch) store_a(R0, as_dst0);
-    __syncthreads();
+#define MOE_GEMM_STEP(J, ACUR1, ANEW, BCUR, BNEW)                    \
+  {                                                                  \
+    store_a(ACUR1, (J + 1) % 3);                                     \
+    load_a(kc + J + 3, ANEW);                                        \
+    load_bc(kc + J + 2, BNEW);                                       \
+    __builtin_amdgcn_sched_barrier(0);                               \
+    pin_b(BCUR);                                                     \
+    wave_step<NMI, MAXNMI>(As + J * ABUF, BCUR, shift, bc, acc);     \
+    __syncthreads();                                                 \
   }
+  // whole groups of three steps with no branch inside (exact wait counts),
+  // then the remaining zero, one or two steps
+  int kc = 0;
+  for (; kc + 3 <= nch; kc += 3) {
+    MOE_GEMM_STEP(0, AY, AX, BX, BZ)
+    MOE_GEMM_STEP(1, AZ, AY, BY, BX)
+    MOE_GEMM_STEP(2, AX, AZ, BZ, BY)
+  }
+  if (kc < nch) MOE_GEMM_STEP(0, AY, AX, BX, BZ)
+  if (kc + 1 < nch) MOE_GEMM_STEP(1, AZ, AY, BY, BX)
+#undef MOE_GEMM_STEP
 
   if (GATEUP) {
     // h = SiLU(gate) * up, fp16, stored at the pair-order position of its column
     const int col = t.n * 128 + wv * 32 + (lane & 31);
     const int pcol = (col & ~15) + pair_pos(col & 15);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < NMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = mi * 32 + acc_row(r, lane);
         if (row < t.rows) {
-          const float g = acc[mi][0][r], u = acc[mi][1][r];
-          const float hv = g / (1.0f + expf(-g)) * u;
-          h_out[(size_t)(t.m0 + row) * I + pcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+          const float gv = acc[mi][0][r], uv = acc[mi][1][r];
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          g.h_out[(size_t)(t.m0 + row) * g.I + pcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
         }
       }
-  } else {
+  } else if (g.y16) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < NMI; ++mi)
 #pragma unroll
       for (int f = 0; f < 2; ++f)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = mi * 32 + acc_row(r, lane);
-          if (row < t.rows) y_out[(size_t)(t.m0 + row) * H + (f ? n1 : n0)] = acc[mi][f][r];
+          if (row < t.rows)
+            g.y16[(size_t)(t.m0 + row) * g.H + (f ? n1 : n0)] =
+                __builtin_bit_cast(uint16_t, (_Float16)(g.row_gate[row] * acc[mi][f][r]));
         }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < NMI; ++mi)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mi * 32 + acc_row(r, lane);
+          if (row < t.rows) g.y_out[(size_t)(t.m0 + row) * g.H + (f ? n1 : n0)] = acc[mi][f][r];
+        }
+  }
+}
+
+// One kernel per projection and tile height: MAXNMI = 4 (128-row tiles, two
+// blocks per CU) or 8 (256-row tiles, one block of four waves per CU, twice the
+// MFMAs per dequantised B fragment, accumulators in AGPRs).
+template <bool GATEUP, int MAXNMI>
+__global__ __launch_bounds__(256, MAXNMI == 4 ? 2 : 1) void k_gemm_q2(
+    const uint8_t* __restrict__ r_codes, const uint16_t* __restrict__ r_scales, const uint8_t* __restrict__ s_codes,
+    const uint16_t* __restrict__ s_scales, size_t code_stride, size_t scale_stride, int H, int I, int E,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ sorted_rows,
+    int T, int k, const uint16_t* __restrict__ a_src, uint16_t* __restrict__ h_out, float* __restrict__ y_out,
+    const float* __restrict__ gates, uint16_t* __restrict__ y16) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[3 * 32 * MAXNMI * A_STRIDE];
+  __shared__ float row_gate[32 * MAXNMI];
+  GemmTile t;
+  if (!load_tile(tiles, n_tiles, t)) return;
+  if (!GATEUP && y16) {
+    // gate of every row of the tile (1 for the shared expert), read in the
+    // epilogue after the K loop's barriers
+    for (int i = threadIdx.x; i < t.rows; i += blockDim.x) {
+      const int r = sorted_rows[t.m0 + i];
+      row_gate[i] = r < T * k ? gates[r] : 1.0f;
+    }
+  }
+  const bool sh = t.g == E;
+  const size_t eidx = sh ? 0 : (size_t)t.g;
+  GemmArgs g;
+  g.codes = (sh ? s_codes : r_codes) + eidx * code_stride;
+  g.scales = (sh ? s_scales : r_scales) + eidx * scale_stride;
+  g.H = H;
+  g.I = I;
+  g.T = T;
+  g.k = k;
+  g.sorted_rows = sorted_rows;
+  g.a_src = a_src;
+  g.h_out = h_out;
+  g.y_out = y_out;
+  g.y16 = y16;
+  g.row_gate = row_gate;
+  const int nmi = __builtin_amdgcn_readfirstlane((t.rows + 31) >> 5);
+  if (MAXNMI == 4) {
+    switch (nmi) {
+      case 1: gemm_tile<GATEUP, 1, MAXNMI>(g, t, As); break;
+      case 2: gemm_tile<GATEUP, 2, MAXNMI>(g, t, As); break;
+      case 3: gemm_tile<GATEUP, 3, MAXNMI>(g, t, As); break;
+      default: gemm_tile<GATEUP, MAXNMI, MAXNMI>(g, t, As); break;
+    }
+  } else {
+    switch ((nmi + 1) >> 1) {
+      case 1: gemm_tile<GATEUP, 2, MAXNMI>(g, t, As); break;
+      case 2: gemm_tile<GATEUP, 4, MAXNMI>(g, t, As); break;
+      case 3: gemm_tile<GATEUP, 6, MAXNMI>(g, t, As); break;
+      default: gemm_tile<GATEUP, MAXNMI, MAXNMI>(g, t, As); break;
+    }
   }
 }
 
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
-                          int T, int k, const uint16_t* a_f16, void* out, hipStream_t s) {
+                          int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
+                          uint16_t* y16) {
   if (max_tiles <= 0) return hipSuccess;
+  constexpr int MAXNMI = GBM / 32;
   if (kind == GemvKind::GateUp) {
-    MOE_LAUNCH(k_gemm_q2<true>, dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
-                       shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
-                       sorted_rows, T, k, a_f16, (uint16_t*)out, nullptr);
+    MOE_LAUNCH((k_gemm_q2<true, MAXNMI>), dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
+               shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
+               sorted_rows, T, k, a_f16, (uint16_t*)out, (float*)nullptr, (const float*)nullptr,
+               (uint16_t*)nullptr);
   } else {
-    MOE_LAUNCH(k_gemm_q2<false>, dim3(max_tiles, H / GCOLS), dim3(256), 0, s, routed.codes, routed.scales,
-                       shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
-                       nullptr, T, k, a_f16, nullptr, (float*)out);
+    MOE_LAUNCH((k_gemm_q2<false, MAXNMI>), dim3(max_tiles, H / GCOLS), dim3(256), 0, s, routed.codes,
+               routed.scales, shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles,
+               n_tiles, sorted_rows, T, k, a_f16, (uint16_t*)nullptr, y16 ? (float*)nullptr : (float*)out, gates,
+               y16);
   }
   return hipGetLastError();
 }
@@ -457,7 +577,7 @@ hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, cons
 
 // ---------------------------------------------------------------------------
 // Plan: split the groups of a permutation between the MFMA GEMM (groups with at
-// least min_rows entries, cut into BM-row tiles) and the GEMV work items (the
+// least min_rows entries, cut into GBM-row tiles) and the GEMV work items (the
 // rest, items_per entries each).  One block of 1024 threads, thread = group.
 // ---------------------------------------------------------------------------
 __device__ int plan_scan_1024(int v, int* total) {
@@ -491,15 +611,15 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
   const int start = g < G ? offsets[g] : 0;
   const int cnt = g < G ? offsets[g + 1] - start : 0;
   const bool big = cnt >= min_rows;
-  const int nt = big ? (cnt + BM - 1) / BM : 0;
+  const int nt = big ? (cnt + GBM - 1) / GBM : 0;
   const int ni = big ? 0 : (cnt + items_per - 1) / items_per;
   int tot_t = 0, tot_i = 0;
   const int pt = plan_scan_1024(nt, &tot_t);
   const int pi = plan_scan_1024(ni, &tot_i);
   for (int i = 0; i < nt; ++i) {
     tiles[3 * (pt + i)] = g;
-    tiles[3 * (pt + i) + 1] = start + i * BM;
-    tiles[3 * (pt + i) + 2] = min(BM, cnt - i * BM);
+    tiles[3 * (pt + i) + 1] = start + i * GBM;
+    tiles[3 * (pt + i) + 2] = min(GBM, cnt - i * GBM);
   }
   for (int i = 0; i < ni; ++i) {
     items[3 * (pi + i)] = g;

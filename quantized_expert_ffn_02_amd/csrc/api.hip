@@ -96,7 +96,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xf32 = take(dense ? T * H * 4 : 0);
   o.xf16 = take(dense ? 0 : T * H * 2);
   o.hf16 = take(dense ? 0 : n * I * 2);
-  o.tiles = take((n / 128 + E + 2) * 3 * 4);
+  o.tiles = take((n / kSkinnyRows + E + 2) * 3 * 4);   // GEMM tiles or skinny chunks
   o.n_tiles = take(4);
   o.h = take(n * I * 4);
   o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
@@ -169,8 +169,11 @@ int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float
              const Layout& lay, hipStream_t s) {
   float* logits = at<float>(ws, lay.logits);
   MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] {
-    return T >= 64 ? launch_router_mfma(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s)
-                   : launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+    // prompt chunks: 128 x 128 MFMA tiles; verify batches: 32-token chunks with K
+    // split over waves; a decode step: one wave per expert row
+    if (T >= 1024) return launch_router_mfma(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+    if (T > 16) return launch_router_skinny(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+    return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
   }));
   MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
   return MOE_OK;
@@ -419,6 +422,34 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] { return launch_decode_gateup(d, s); }));
     MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] { return launch_decode_down(d, s); }));
     MOE_TRY(launch_decode_combine(d, s));
+    return MOE_OK;
+  }
+  if (T > kDecodeDirectMaxTokens && T < 1024 && L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter)) {
+    // many-sequence verify batch: skinny router, top-k, permutation, 32-row
+    // chunks of every group on the skinny MFMA GEMMs, combine
+    int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
+    if (rc) return rc;
+    MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                           at<int32_t>(ws, lay.base), s));
+    int32_t* chunks = at<int32_t>(ws, lay.tiles);
+    int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
+    MOE_TRY(launch_plan(offsets, E, 1, 1, chunks, n_chunks, items, n_items, s, kSkinnyRows));
+    const int H = L->hidden, I = L->inter;
+    const int max_chunks = n / kSkinnyRows + std::min(E + 1, n) + 1;
+    const MatRef r13 = mat_w13(L->routed), r2 = mat_w2(L->routed);
+    const MatRef s13 = with_shared ? mat_w13(L->shared) : MatRef(), s2 = with_shared ? mat_w2(L->shared) : MatRef();
+    uint16_t* xf = at<uint16_t>(ws, lay.xf16);
+    uint16_t* hf = at<uint16_t>(ws, lay.hf16);
+    float* y = at<float>(ws, lay.y);
+    MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
+    MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
+      return launch_gemm_skinny(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf,
+                                s);
+    }));
+    MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
+      return launch_gemm_skinny(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s);
+    }));
+    MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
     return MOE_OK;
   }
   if (n <= kSmallRouteMaxEntries) {

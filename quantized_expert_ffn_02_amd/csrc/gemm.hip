@@ -29,22 +29,12 @@
 
 #include "device.h"
 #include "internal.h"
+#include "mfma.h"
 
 namespace moe {
 
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
-typedef float f16x_t __attribute__((ext_vector_type(16)));
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-// native 128-bit vector (HIP's uint4 is a struct whose copies into LDS keep a
-// private-memory temporary alive)
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 static constexpr int BM = 128, BN = 128, BK = 64;
 static constexpr int LDS_STRIDE = BK + 8;   // halves per LDS row (padding against bank conflicts)
-
-// position of column k (0..15) of a 16-group in pair order
-__device__ __forceinline__ int pair_pos(int k) { return k < 8 ? 2 * k : 2 * (k - 8) + 1; }
 
 // ---------------------------------------------------------------------------
 // x (bf16) -> fp16 in pair order
@@ -78,9 +68,6 @@ hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out,
   return hipGetLastError();
 }
 
-// row (0..31) of accumulator register r for this lane, column = lane & 31
-__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
 // ---------------------------------------------------------------------------
 // Grouped GEMM over the 2-bit experts.
 //
@@ -93,96 +80,12 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 // its 2-bit codes straight from global memory into registers and dequantises
 // them there into MFMA B fragments: no LDS traffic and no duplicated work for B.
 //
-// B fragment of a 32x32x16 MFMA: lane l holds 8 consecutive K positions
-// 8 (l / 32) .. + 7 of column l % 32.  In pair order, positions 8h .. 8h + 7 of
-// a 16-group are the pairs (w_{4h+q}, w_{4h+q+8}), q = 0..3, whose codes sit at
-// bits 2q and 16 + 2q of the code word shifted right by 8h.  OR-ing a code under
-// the exponent of 1024 gives the fp16 value 1024 + c 4^q; one v_pk_fma_f16 turns
-// it into c - 2 (exact) and one v_pk_mul_f16 applies the block scale (exact).
+// The B fragments are dequantised exactly into fp16 (mfma.h).
 // ---------------------------------------------------------------------------
 static constexpr int GBM = 128;              // rows per M-tile (32 x fragments per wave)
 static constexpr int GBK = 64;               // K per pipeline step
 static constexpr int A_STRIDE = GBK + 8;     // halves per LDS row
 static constexpr int GCOLS = 256;            // weight rows per block (4 waves x 64)
-
-struct BConst {
-  uint32_t mask[4];   // 0x00030003 << 2q
-  h2_t mul[4];        // 4^-q
-  h2_t add[4];        // -(1024 * 4^-q + 2)
-  uint32_t magic;     // 0x64006400
-};
-
-__device__ __forceinline__ BConst bconst() {
-  BConst c;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c.mask[q] = vgpr_const(0x00030003u << (2 * q));
-    const float m = ldexpf(1.0f, -2 * q);
-    c.mul[q] = h2_t{(_Float16)m, (_Float16)m};
-    const _Float16 a = (_Float16)(-(1024.0f * m + 2.0f));
-    c.add[q] = h2_t{a, a};
-  }
-  c.magic = vgpr_const(0x64006400u);
-  return c;
-}
-
-// B fragment (8 fp16 in pair order) of one lane from its code word w (already
-// shifted right by 8 * lane-half) and the block scale pair s2.
-__device__ __forceinline__ h8_t b_frag(uint32_t w, h2_t s2, const BConst& c) {
-  uint32_t o[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    h2_t f = __builtin_bit_cast(h2_t, (w & c.mask[q]) | c.magic);
-    f = f * c.mul[q] + c.add[q];   // c - 2, exact
-    f = f * s2;                    // s (c - 2), exact
-    o[q] = __builtin_bit_cast(uint32_t, f);
-  }
-  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(h8_t, u4v{o[0], o[1], o[2], o[3]});
-}
-
-__device__ __forceinline__ h2_t scale_pair(uint32_t d, bool hi) {
-  const uint32_t v = hi ? ((d >> 16) | (d & 0xFFFF0000u)) : ((d & 0xFFFFu) | (d << 16));
-  return __builtin_bit_cast(h2_t, v);
-}
-
-// Registers of one pipeline step: the codes + scales of the wave's two B
-// columns for 64 K.
-struct BRegs {
-  u32x4 c0, c1;
-  uint32_t s0, s1;
-};
-
-struct BCol {
-  const u32x4* __restrict__ codes;   // this lane's column: 16 B per step
-  const uint32_t* __restrict__ scales;
-};
-
-// Column n of a tiled 2-bit matrix with K columns: pointer to its first 16-byte
-// code chunk (steps advance by 1024 B) and to its scale dword of blocks 0, 1.
-__device__ __forceinline__ BCol b_column(const uint8_t* codes, const uint16_t* scales, int n, int K) {
-  BCol b;
-  const int nt = n >> 6, nl = n & 63;
-  b.codes = reinterpret_cast<const u32x4*>(codes + ((size_t)nt * (K / 64) * 64 + nl) * 16);
-  b.scales = reinterpret_cast<const uint32_t*>(scales + ((size_t)nt * (K / 128) * 64 + nl) * 4);
-  return b;
-}
-
-// step kc: codes at + kc * 64 uint4; scales of blocks 2kc, 2kc+1 at dword
-// (kc / 2) * 128 + (kc % 2)
-__device__ __forceinline__ void load_b(const BCol& b0, const BCol& b1, int kc, BRegs& R) {
-  R.c0 = b0.codes[(size_t)kc * 64];
-  R.s0 = b0.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
-  R.c1 = b1.codes[(size_t)kc * 64];
-  R.s1 = b1.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
-}
-
-// Keeps the unpacking of a B register set inside the step that consumes it:
-// without this the scheduler hoists it into earlier steps, right behind the
-// set's loads, and the wave waits for loads it issued two steps ahead.
-__device__ __forceinline__ void pin_b(BRegs& R) {
-  asm volatile("" : "+v"(R.c0), "+v"(R.c1), "+v"(R.s0), "+v"(R.s1));
-}
 
 // One K step of a wave: 4 x (2 B fragments, NMI A fragments, 2 NMI MFMAs);
 // NMI = number of 32-row fragments the tile's rows need.
@@ -577,7 +480,7 @@ hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, cons
 
 // ---------------------------------------------------------------------------
 // Plan: split the groups of a permutation between the MFMA GEMM (groups with at
-// least min_rows entries, cut into GBM-row tiles) and the GEMV work items (the
+// least min_rows entries, cut into tile_rows-row tiles) and the GEMV work items (the
 // rest, items_per entries each).  One block of 1024 threads, thread = group.
 // ---------------------------------------------------------------------------
 __device__ int plan_scan_1024(int v, int* total) {
@@ -603,7 +506,7 @@ __device__ int plan_scan_1024(int v, int* total) {
 }
 
 __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offsets, int E, int min_rows,
-                                               int items_per, int32_t* __restrict__ tiles,
+                                               int items_per, int tile_rows, int32_t* __restrict__ tiles,
                                                int32_t* __restrict__ n_tiles, int32_t* __restrict__ items,
                                                int32_t* __restrict__ n_items) {
   const int G = E + 1;
@@ -611,15 +514,15 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
   const int start = g < G ? offsets[g] : 0;
   const int cnt = g < G ? offsets[g + 1] - start : 0;
   const bool big = cnt >= min_rows;
-  const int nt = big ? (cnt + GBM - 1) / GBM : 0;
+  const int nt = big ? (cnt + tile_rows - 1) / tile_rows : 0;
   const int ni = big ? 0 : (cnt + items_per - 1) / items_per;
   int tot_t = 0, tot_i = 0;
   const int pt = plan_scan_1024(nt, &tot_t);
   const int pi = plan_scan_1024(ni, &tot_i);
   for (int i = 0; i < nt; ++i) {
     tiles[3 * (pt + i)] = g;
-    tiles[3 * (pt + i) + 1] = start + i * GBM;
-    tiles[3 * (pt + i) + 2] = min(GBM, cnt - i * GBM);
+    tiles[3 * (pt + i) + 1] = start + i * tile_rows;
+    tiles[3 * (pt + i) + 2] = min(tile_rows, cnt - i * tile_rows);
   }
   for (int i = 0; i < ni; ++i) {
     items[3 * (pi + i)] = g;
@@ -633,9 +536,9 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
 }
 
 hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_per, int32_t* tiles,
-                       int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s) {
-  MOE_LAUNCH(k_plan, dim3(1), dim3(1024), 0, s, offsets, E, min_rows, items_per, tiles, n_tiles, items,
-                     n_items);
+                       int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s, int tile_rows) {
+  MOE_LAUNCH(k_plan, dim3(1), dim3(1024), 0, s, offsets, E, min_rows, items_per, tile_rows > 0 ? tile_rows : GBM,
+             tiles, n_tiles, items, n_items);
   return hipGetLastError();
 }
 

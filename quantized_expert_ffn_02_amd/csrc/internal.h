@@ -178,12 +178,20 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates = nullptr,
                           uint16_t* y16 = nullptr);
+// skinny MFMA GEMMs (gemm_skinny.hip): 32-row chunks x 64 columns, K split over waves
+static constexpr int kSkinnyRows = 32;
+hipError_t launch_gemm_skinny(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
+                              const int32_t* chunks, const int32_t* n_chunks, int max_chunks,
+                              const int32_t* sorted_rows, int T, int k, const uint16_t* a_f16, void* out,
+                              hipStream_t s);
+hipError_t launch_router_skinny(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
+                                float* logits, hipStream_t s);
 // out[t] = sum over the token's entries of the gate-scaled fp16 rows y16 (rank
 // order, then the shared expert) (+ residual), fp32, optional bf16 copy
 hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,
                             const uint16_t* residual, float* out, uint16_t* out_bf16, hipStream_t s);
 hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_per, int32_t* tiles,
-                       int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s);
+                       int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s, int tile_rows = 0);
 int gemm_tile_rows();
 // shapes the grouped GEMM covers (column tiles of 128 gate/up and 256 down rows)
 bool gemm_shape_ok(int H, int I);

@@ -426,7 +426,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   }
   if (T > kDecodeDirectMaxTokens && T < 1024 && L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter)) {
     // many-sequence verify batch: skinny router, top-k, permutation, 32-row
-    // chunks of every group on the skinny MFMA GEMMs, combine
+    // tiles of every group on the grouped MFMA GEMM, combine
     int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
     if (rc) return rc;
     MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
@@ -443,11 +443,12 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     float* y = at<float>(ws, lay.y);
     MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
     MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
-      return launch_gemm_skinny(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf,
-                                s);
+      return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
+                            nullptr, nullptr, kSkinnyRows);
     }));
     MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
-      return launch_gemm_skinny(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s);
+      return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
+                            nullptr, nullptr, kSkinnyRows);
     }));
     MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
     return MOE_OK;

@@ -165,27 +165,28 @@ struct GemmArgs {
   const float* row_gate;  // LDS: gate of each of the tile's rows (y16 only)
 };
 
-// MAXNMI = 32-row fragments per wave (tile height 32 MAXNMI); NMI <= MAXNMI the
-// fragments this tile's rows need.  As holds three LDS buffers of the A tile.
-template <bool GATEUP, int NMI, int MAXNMI>
+// MAXNMI = 32-row fragments per wave (tile height 32 MAXNMI: 32, 64 or 128
+// rows); NMI <= MAXNMI the fragments this tile's rows need.  As holds three LDS
+// buffers of the A tile.
+template <bool GATEUP, int NMI, int MAXNMI, int DEPTH>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, uint16_t* As) {
   constexpr int BMX = 32 * MAXNMI;          // tile rows
-  constexpr int RPT = MAXNMI / 4;           // A rows staged per thread (256 threads, 2 per row)
+  constexpr int TPR = 256 / BMX;            // threads staging one A row (2, 4 or 8)
+  constexpr int NV = 8 / TPR;               // 16-byte A chunks per thread and step
   constexpr int ABUF = BMX * A_STRIDE;      // halves per LDS buffer
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = GATEUP ? g.H : g.I;
   const int nch = K / GBK;
 
-  // A staging: thread -> rows ra + 128 j (j < RPT), 32-half slice ha of the
-  // step.  Rows past the tile's rows load its first row (no lane-divergent
-  // branch around the loads; LDS rows past NMI * 32 are never read).
-  const int ra = tid >> 1, ha = tid & 1;
-  const u32x4* ag[RPT];
-#pragma unroll
-  for (int j = 0; j < RPT; ++j) {
-    const int rr = ra + 128 * j;
-    const int pa = t.m0 + (rr < t.rows ? rr : 0);
+  // A staging: thread -> (row ra = tid / TPR, slice ha = tid % TPR of NV
+  // 16-byte chunks) of the step.  Rows past the tile's rows load its first row
+  // (no lane-divergent branch around the loads; LDS rows past NMI * 32 are
+  // never read).
+  const int ra = tid / TPR, ha = tid % TPR;
+  const u32x4* ag[1];
+  {
+    const int pa = t.m0 + (ra < t.rows ? ra : 0);
     size_t arow;
     if (GATEUP) {
       const int r = g.sorted_rows[pa];
@@ -194,9 +195,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     } else {
       arow = (size_t)pa;
     }
-    ag[j] = reinterpret_cast<const u32x4*>(g.a_src + arow * K) + ha * 4;
+    ag[0] = reinterpret_cast<const u32x4*>(g.a_src + arow * K) + ha * NV;
   }
-  const int a_off = ra * A_STRIDE + ha * 32;
+  const int a_off = ra * A_STRIDE + ha * NV * 8;
 
   // B columns of this lane
   int n0, n1;
@@ -223,41 +224,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   // Loads past the last step re-load the last step (index clamped): every load
   // is unconditional, so the wait counts before each use stay exact.
   struct ARegs {
-    u32x4 a[RPT][4];
+    u32x4 a[NV];
   };
   auto load_a = [&](int kc, ARegs& R) {
     kc = kc < nch ? kc : nch - 1;
 #pragma unroll
-    for (int j = 0; j < RPT; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) R.a[j][q] = ag[j][kc * 8 + q];
+    for (int q = 0; q < NV; ++q) R.a[q] = ag[0][kc * 8 + q];
   };
   auto store_a = [&](const ARegs& R, int buf) {
+    u32x4* d = reinterpret_cast<u32x4*>(As + buf * ABUF + a_off);
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      u32x4* d = reinterpret_cast<u32x4*>(As + buf * ABUF + a_off + 128 * j * A_STRIDE);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = R.a[j][q];
-    }
+    for (int q = 0; q < NV; ++q) d[q] = R.a[q];
   };
   auto load_bc = [&](int kc, BRegs& R) { load_b(B0, B1, kc < nch ? kc : nch - 1, R); };
 
-  // The loop is unrolled by three so that every rotating resource has a static
-  // name.  Step m computes from LDS buffer m % 3 and B register set m % 3; it
-  // first writes A of step m + 1 (register set (m + 1) % 3, loaded two steps
-  // earlier) into LDS buffer (m + 1) % 3, then issues the loads of A for step
-  // m + 3 and of B for step m + 2.  Both operands get two steps of latency
-  // cover; the scheduling barrier keeps the loads at the top of the step.
-  ARegs AX, AY, AZ;
-  BRegs BX, BY, BZ;
-  load_a(0, AX);
-  load_bc(0, BX);
-  load_a(1, AY);
-  load_bc(1, BY);
-  load_a(2, AZ);
-  store_a(AX, 0);
-  __syncthreads();
-#define MOE_GEMM_STEP(J, ACUR1, ANEW, BCUR, BNEW)                    \
+  if constexpr (DEPTH == 2) {
+    // Three register sets with static names (the loop is unrolled by three).
+    // Step m computes from LDS buffer m % 3 and B set m % 3; it first writes A
+    // of step m + 1 (set (m + 1) % 3, loaded two steps earlier) into LDS buffer
+    // (m + 1) % 3, then issues the loads of A for step m + 3 and of B for step
+    // m + 2.  The scheduling barrier keeps the loads at the top of the step.
+    ARegs AX, AY, AZ;
+    BRegs BX, BY, BZ;
+    load_a(0, AX);
+    load_bc(0, BX);
+    load_a(1, AY);
+    load_bc(1, BY);
+    load_a(2, AZ);
+    store_a(AX, 0);
+    __syncthreads();
+#define MOE_GEMM_STEP3(J, ACUR1, ANEW, BCUR, BNEW)                   \
   {                                                                  \
     store_a(ACUR1, (J + 1) % 3);                                     \
     load_a(kc + J + 3, ANEW);                                        \
@@ -267,17 +263,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     wave_step<NMI, MAXNMI>(As + J * ABUF, BCUR, shift, bc, acc);     \
     __syncthreads();                                                 \
   }
-  // whole groups of three steps with no branch inside (exact wait counts),
-  // then the remaining zero, one or two steps
-  int kc = 0;
-  for (; kc + 3 <= nch; kc += 3) {
-    MOE_GEMM_STEP(0, AY, AX, BX, BZ)
-    MOE_GEMM_STEP(1, AZ, AY, BY, BX)
-    MOE_GEMM_STEP(2, AX, AZ, BZ, BY)
+    // whole groups of three steps with no branch inside (exact wait counts),
+    // then the remaining zero, one or two steps
+    int kc = 0;
+    for (; kc + 3 <= nch; kc += 3) {
+      MOE_GEMM_STEP3(0, AY, AX, BX, BZ)
+      MOE_GEMM_STEP3(1, AZ, AY, BY, BX)
+      MOE_GEMM_STEP3(2, AX, AZ, BZ, BY)
+    }
+    if (kc < nch) MOE_GEMM_STEP3(0, AY, AX, BX, BZ)
+    if (kc + 1 < nch) MOE_GEMM_STEP3(1, AZ, AY, BY, BX)
+#undef MOE_GEMM_STEP3
+  } else {
+  // Register rings of R = DEPTH + 1 sets for A and B and three LDS buffers for
+  // A.  Step m computes from LDS buffer m % 3 and B set m % R; it first writes
+  // A of step m + 1 (set (m + 1) % R, loaded DEPTH steps earlier) into LDS
+  // buffer (m + 1) % 3, then issues the loads of A for step m + DEPTH + 1 and
+  // of B for step m + DEPTH.  The loop is unrolled by lcm(R, 3) so every ring
+  // index is a compile-time constant (the sets stay in registers); the
+  // scheduling barrier keeps the loads at the top of the step.
+  constexpr int R = DEPTH + 1;
+  constexpr int U = R % 3 == 0 ? R : 3 * R;
+  ARegs Ar[R];
+  BRegs Br[R];
+#pragma unroll
+  for (int i = 0; i <= DEPTH; ++i) load_a(i, Ar[i]);
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) load_bc(i, Br[i]);
+  store_a(Ar[0], 0);
+  __syncthreads();
+#define MOE_GEMM_STEP(J)                                                       \
+  {                                                                            \
+    store_a(Ar[(J + 1) % R], (J + 1) % 3);                                     \
+    load_a(kc + J + DEPTH + 1, Ar[J % R]);                                     \
+    load_bc(kc + J + DEPTH, Br[(J + DEPTH) % R]);                              \
+    __builtin_amdgcn_sched_barrier(0);                                         \
+    pin_b(Br[J % R]);                                                          \
+    wave_step<NMI, MAXNMI>(As + (J % 3) * ABUF, Br[J % R], shift, bc, acc);    \
+    __syncthreads();                                                           \
   }
-  if (kc < nch) MOE_GEMM_STEP(0, AY, AX, BX, BZ)
-  if (kc + 1 < nch) MOE_GEMM_STEP(1, AZ, AY, BY, BX)
+  // whole groups of U steps with no branch inside (exact wait counts), then
+  // the remaining steps
+  int kc = 0;
+  for (; kc + U <= nch; kc += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) MOE_GEMM_STEP(j)
+  }
+#pragma unroll
+  for (int j = 0; j < U - 1; ++j)
+    if (kc + j < nch) MOE_GEMM_STEP(j)
 #undef MOE_GEMM_STEP
+  }
 
   if (GATEUP) {
     // h = SiLU(gate) * up, fp16, stored at the pair-order position of its column
@@ -319,11 +355,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   }
 }
 
-// One kernel per projection and tile height: MAXNMI = 4 (128-row tiles, two
-// blocks per CU) or 8 (256-row tiles, one block of four waves per CU, twice the
-// MFMAs per dequantised B fragment, accumulators in AGPRs).
+// One kernel per projection and tile height: MAXNMI = 4 (128-row tiles, for
+// prompt chunks) or 1 (32-row tiles, for verify batches of many sequences,
+// whose experts have a few to a few dozen rows).
 template <bool GATEUP, int MAXNMI>
-__global__ __launch_bounds__(256, MAXNMI == 4 ? 2 : 1) void k_gemm_q2(
+__global__ __launch_bounds__(256, MAXNMI == 4 ? 2 : 3) void k_gemm_q2(
     const uint8_t* __restrict__ r_codes, const uint16_t* __restrict__ r_scales, const uint8_t* __restrict__ s_codes,
     const uint16_t* __restrict__ s_scales, size_t code_stride, size_t scale_stride, int H, int I, int E,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ sorted_rows,
@@ -356,30 +392,26 @@ __global__ __launch_bounds__(256, MAXNMI == 4 ? 2 : 1) void k_gemm_q2(
   g.y_out = y_out;
   g.y16 = y16;
   g.row_gate = row_gate;
+  // prefetch depth: two steps for 128-row tiles (register budget), five for
+  // 32-row tiles (few rows: latency, not the matrix cores, sets the pace)
+  constexpr int D = MAXNMI == 4 ? 2 : 5;
   const int nmi = __builtin_amdgcn_readfirstlane((t.rows + 31) >> 5);
-  if (MAXNMI == 4) {
-    switch (nmi) {
-      case 1: gemm_tile<GATEUP, 1, MAXNMI>(g, t, As); break;
-      case 2: gemm_tile<GATEUP, 2, MAXNMI>(g, t, As); break;
-      case 3: gemm_tile<GATEUP, 3, MAXNMI>(g, t, As); break;
-      default: gemm_tile<GATEUP, MAXNMI, MAXNMI>(g, t, As); break;
-    }
+  if (MAXNMI == 1 || nmi == 1) {
+    gemm_tile<GATEUP, 1, MAXNMI, D>(g, t, As);
+  } else if (MAXNMI == 2 || nmi == 2) {
+    gemm_tile<GATEUP, (MAXNMI >= 2 ? 2 : 1), MAXNMI, D>(g, t, As);
+  } else if (nmi == 3) {
+    gemm_tile<GATEUP, (MAXNMI >= 4 ? 3 : 1), MAXNMI, D>(g, t, As);
   } else {
-    switch ((nmi + 1) >> 1) {
-      case 1: gemm_tile<GATEUP, 2, MAXNMI>(g, t, As); break;
-      case 2: gemm_tile<GATEUP, 4, MAXNMI>(g, t, As); break;
-      case 3: gemm_tile<GATEUP, 6, MAXNMI>(g, t, As); break;
-      default: gemm_tile<GATEUP, MAXNMI, MAXNMI>(g, t, As); break;
-    }
+    gemm_tile<GATEUP, MAXNMI, MAXNMI, D>(g, t, As);
   }
 }
 
-hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
-                          const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
-                          int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
-                          uint16_t* y16) {
-  if (max_tiles <= 0) return hipSuccess;
-  constexpr int MAXNMI = GBM / 32;
+template <int MAXNMI>
+static hipError_t launch_gemm_q2_t(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
+                                   const int32_t* tiles, const int32_t* n_tiles, int max_tiles,
+                                   const int32_t* sorted_rows, int T, int k, const uint16_t* a_f16, void* out,
+                                   hipStream_t s, const float* gates, uint16_t* y16) {
   if (kind == GemvKind::GateUp) {
     MOE_LAUNCH((k_gemm_q2<true, MAXNMI>), dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
                shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
@@ -392,6 +424,18 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                y16);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
+                          const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
+                          int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
+                          uint16_t* y16, int tile_rows) {
+  if (max_tiles <= 0) return hipSuccess;
+  if (tile_rows == 32)
+    return launch_gemm_q2_t<1>(kind, routed, shared, H, I, E, tiles, n_tiles, max_tiles, sorted_rows, T, k, a_f16,
+                               out, s, gates, y16);
+  return launch_gemm_q2_t<GBM / 32>(kind, routed, shared, H, I, E, tiles, n_tiles, max_tiles, sorted_rows, T, k,
+                                    a_f16, out, s, gates, y16);
 }
 
 // ---------------------------------------------------------------------------

@@ -28,6 +28,34 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+# HBM traffic of the decode gate/up kernel (T = 4, 44 x 10 blocks) from two
+# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; command and figures in the
+# profiles/ counter summary), each scaled by what the counter reads for a plain
+# 256 MiB device copy: FETCH_SIZE reads 131,084.5 KiB for 262,144 KiB read
+# (factor 2.0), WRITE_SIZE 262,144 KiB for 262,144 KiB written (factor 1.0).
+# Reported only while the kernel's sources are the ones that were counted.
+GATEUP_TRAFFIC = {
+    "sources": ["decode_ffn.hip", "device.h", "table.h", "topk.h"],
+    "sha256": "b2324372ac4b8b080b2d7bb3a3a08fcb6af3d5b11f730c767b0cd10a30137eca",
+    "fetch_kib": 22274.7, "fetch_scale": 262144.0 / 131084.5,
+    "write_kib": 118.9, "write_scale": 1.0,
+    "tokens": 4,
+}
+
+
+def counted_traffic(entry, T):
+    """Bytes per launch from the stored counter runs, or None if the kernel changed or T differs."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_expert_ffn_02_amd", "csrc")
+    for f in entry["sources"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != entry["sha256"] or T != entry["tokens"]:
+        return None
+    return 1024.0 * (entry["fetch_kib"] * entry["fetch_scale"] + entry["write_kib"] * entry["write_scale"])
+
+
 def q2_expert_bytes(H, I):
     """Bytes of one 2-bit expert: 3*H*I codes at 2 bits + one fp16 scale per 32 weights."""
     w = 3 * H * I
@@ -296,6 +324,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--cache-steps", type=int, default=5)
     ap.add_argument("--no-cache", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run 10 plain device copies of BYTES bytes (a known-size reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -311,6 +341,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     B.lib()
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch scale the
+        # counters of the kernels above to bytes
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = synth.CONFIGS["decode"]
     s = wl.shape
     H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
@@ -420,7 +459,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": counted_traffic(GATEUP_TRAFFIC, T),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": gu_bytes,
             "avg_launch_us": gu_ms * 1e3,
         },

@@ -361,6 +361,48 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
                                out_bf16, (hipStream_t)stream));
 }
 
+// Batches beyond a decode step on the grouped MFMA GEMM with 32-row tiles
+// (2-bit below a prompt chunk, 3-bit at any size): router, top-k, permutation,
+// tile plan, x -> fp16 pair order, gate/up, down, combine.  In expert-cache
+// mode ``routed`` is the slot pool and ``slot_map`` maps routed groups to pool
+// slots (-1: a miss, whose rows contribute zero).
+static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int32_t* slot_map, const uint16_t* x,
+                       int32_t T, const uint16_t* residual, float* out, uint16_t* out_bf16, int32_t* ids,
+                       float* gates, float* margin, void* ws, const Layout& lay, hipStream_t s) {
+  const int k = L->top_k, E = L->n_experts, H = L->hidden, I = L->inter;
+  const int with_shared = has_shared(L) ? 1 : 0;
+  const int n = T * k + (with_shared ? T : 0);
+  int32_t* offsets = at<int32_t>(ws, lay.offsets);
+  int32_t* srt = at<int32_t>(ws, lay.sorted_rows);
+  int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
+  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
+  if (rc) return rc;
+  MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                         at<int32_t>(ws, lay.base), s));
+  int32_t* chunks = at<int32_t>(ws, lay.tiles);
+  int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
+  MOE_TRY(launch_plan(offsets, E, 1, 1, chunks, n_chunks, at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items),
+                      s, kSkinnyRows));
+  const int max_chunks = n / kSkinnyRows + std::min(E + 1, n) + 1;
+  const bool q3 = routed.fmt == MOE_FMT_Q3;
+  const MatRef r13 = mat_w13(routed), r2 = mat_w2(routed);
+  const MatRef s13 = with_shared ? mat_w13(L->shared) : MatRef(), s2 = with_shared ? mat_w2(L->shared) : MatRef();
+  uint16_t* xf = at<uint16_t>(ws, lay.xf16);
+  uint16_t* hf = at<uint16_t>(ws, lay.hf16);
+  float* y = at<float>(ws, lay.y);
+  MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
+  MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
+    return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
+                          nullptr, nullptr, kSkinnyRows, q3, slot_map);
+  }));
+  MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
+    return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
+                          nullptr, nullptr, kSkinnyRows, q3, slot_map);
+  }));
+  MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
+  return MOE_OK;
+}
+
 static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
                               float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
                               void* ws, const Layout& lay, hipStream_t s) {
@@ -424,35 +466,9 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     MOE_TRY(launch_decode_combine(d, s));
     return MOE_OK;
   }
-  if (T > kDecodeDirectMaxTokens && T < 1024 && L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter)) {
-    // many-sequence verify batch: skinny router, top-k, permutation, 32-row
-    // tiles of every group on the grouped MFMA GEMM, combine
-    int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
-    if (rc) return rc;
-    MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
-                           at<int32_t>(ws, lay.base), s));
-    int32_t* chunks = at<int32_t>(ws, lay.tiles);
-    int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
-    MOE_TRY(launch_plan(offsets, E, 1, 1, chunks, n_chunks, items, n_items, s, kSkinnyRows));
-    const int H = L->hidden, I = L->inter;
-    const int max_chunks = n / kSkinnyRows + std::min(E + 1, n) + 1;
-    const MatRef r13 = mat_w13(L->routed), r2 = mat_w2(L->routed);
-    const MatRef s13 = with_shared ? mat_w13(L->shared) : MatRef(), s2 = with_shared ? mat_w2(L->shared) : MatRef();
-    uint16_t* xf = at<uint16_t>(ws, lay.xf16);
-    uint16_t* hf = at<uint16_t>(ws, lay.hf16);
-    float* y = at<float>(ws, lay.y);
-    MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
-    MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
-      return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
-                            nullptr, nullptr, kSkinnyRows);
-    }));
-    MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
-      return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
-                            nullptr, nullptr, kSkinnyRows);
-    }));
-    MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
-    return MOE_OK;
-  }
+  if (T > kDecodeDirectMaxTokens && gemm_shape_ok(L->hidden, L->inter) &&
+      ((L->routed.fmt == MOE_FMT_Q2 && T < 1024) || L->routed.fmt == MOE_FMT_Q3))
+    return medium_path(L, L->routed, nullptr, x, T, residual, out, out_bf16, ids, gates, margin, ws, lay, s);
   if (n <= kSmallRouteMaxEntries) {
     // decode / MTP-verify batch: router, activation table, top-k and permutation in one launch
     SmallRouteArgs a;
@@ -578,6 +594,13 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
   int32_t* items = at<int32_t>(ws, lay.items);
   int32_t* n_items = at<int32_t>(ws, lay.n_items);
+  const int32_t* slot_map = slot_of + (size_t)layer_idx * E;
+  if (T > kDecodeDirectMaxTokens && gemm_shape_ok(L->hidden, L->inter)) {
+    rc = medium_path(&Lc, *slot_pool, slot_map, x, T, nullptr, out, nullptr, ids, gates, nullptr, ws, lay, s);
+    if (rc) return rc;
+    MOE_TRY(launch_miss_list(ids, T * k, slot_map, miss_rows, n_miss, s));
+    return MOE_OK;
+  }
   bool x_table_ready = false;
   if (n <= kSmallRouteMaxEntries) {
     SmallRouteArgs a;

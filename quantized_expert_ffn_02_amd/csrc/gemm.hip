@@ -27,6 +27,8 @@
 // columns, so SwiGLU is applied in registers.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 #include "mfma.h"
@@ -88,23 +90,36 @@ static constexpr int A_STRIDE = GBK + 8;     // halves per LDS row
 static constexpr int GCOLS = 256;            // weight rows per block (4 waves x 64)
 
 // One K step of a wave: 4 x (2 B fragments, NMI A fragments, 2 NMI MFMAs);
-// NMI = number of 32-row fragments the tile's rows need.
-template <int NMI, int MAXNMI>
-__device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const BRegs& R, int shift,
-                                          const BConst& bc, f16x_t acc[MAXNMI][2]) {
+// NMI = number of 32-row fragments the tile's rows need.  3-bit weights add the
+// high-bit fragment of each column and a second MFMA into the same accumulator.
+template <int NMI, int MAXNMI, bool Q3, typename BR>
+__device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const BR& R, int shift, int hshift,
+                                          const BConst& bc, const BConstHi& bch, f16x_t acc[MAXNMI][2]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, kh = (lane >> 5) * 8;
   const uint32_t cw0[4] = {R.c0.x, R.c0.y, R.c0.z, R.c0.w};
   const uint32_t cw1[4] = {R.c1.x, R.c1.y, R.c1.z, R.c1.w};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const h8_t b0 = b_frag(cw0[s] >> shift, scale_pair(R.s0, s >= 2), bc);
-    const h8_t b1 = b_frag(cw1[s] >> shift, scale_pair(R.s1, s >= 2), bc);
+    const h2_t s20 = scale_pair(R.s0, s >= 2), s21 = scale_pair(R.s1, s >= 2);
+    const h8_t b0 = b_frag(cw0[s] >> shift, s20, bc);
+    const h8_t b1 = b_frag(cw1[s] >> shift, s21, bc);
+    h8_t bh0, bh1;
+    if constexpr (Q3) {
+      const h2_t m2 = h2_t{(_Float16)-2.0f, (_Float16)-2.0f};
+      const int hs = hshift + 8 * (s & 1);
+      bh0 = b_frag_hi((s < 2 ? R.h0.x : R.h0.y) >> hs, s20, s20 * m2, bch, bc.magic);
+      bh1 = b_frag_hi((s < 2 ? R.h1.x : R.h1.y) >> hs, s21, s21 * m2, bch, bc.magic);
+    }
 #pragma unroll
     for (int mi = 0; mi < NMI; ++mi) {
       const h8_t a = *reinterpret_cast<const h8_t*>(As + (mi * 32 + r) * A_STRIDE + s * 16 + kh);
       acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[mi][0], 0, 0, 0);
       acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[mi][1], 0, 0, 0);
+      if constexpr (Q3) {
+        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh0, acc[mi][0], 0, 0, 0);
+        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh1, acc[mi][1], 0, 0, 0);
+      }
     }
   }
 }
@@ -156,6 +171,7 @@ __device__ __forceinline__ bool load_tile(const int32_t* __restrict__ tiles, con
 struct GemmArgs {
   const uint8_t* codes;
   const uint16_t* scales;
+  const uint8_t* hi;      // 3-bit weights: high-bit plane
   int H, I, T, k;
   const int32_t* sorted_rows;
   const uint16_t* a_src;
@@ -168,8 +184,9 @@ struct GemmArgs {
 // MAXNMI = 32-row fragments per wave (tile height 32 MAXNMI: 32, 64 or 128
 // rows); NMI <= MAXNMI the fragments this tile's rows need.  As holds three LDS
 // buffers of the A tile.
-template <bool GATEUP, int NMI, int MAXNMI, int DEPTH>
+template <bool GATEUP, int NMI, int MAXNMI, int DEPTH, bool Q3>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, uint16_t* As) {
+  typedef typename std::conditional<Q3, BRegs3, BRegs>::type BRegs;
   constexpr int BMX = 32 * MAXNMI;          // tile rows
   constexpr int TPR = 256 / BMX;            // threads staging one A row (2, 4 or 8)
   constexpr int NV = 8 / TPR;               // 16-byte A chunks per thread and step
@@ -208,10 +225,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     n0 = t.n * GCOLS + wv * 64 + (lane & 31);
     n1 = n0 + 32;
   }
-  const BCol B0 = b_column(g.codes, g.scales, n0, K);
-  const BCol B1 = b_column(g.codes, g.scales, n1, K);
-  const int shift = (lane >> 5) * 8;
+  const BCol B0 = b_column(g.codes, g.scales, n0, K, Q3 ? g.hi : nullptr);
+  const BCol B1 = b_column(g.codes, g.scales, n1, K, Q3 ? g.hi : nullptr);
+  const int shift = (lane >> 5) * 8, hshift = (lane >> 5) * 4;
   const BConst bc = bconst();
+  BConstHi bch;
+  if constexpr (Q3) bch = bconst_hi();
 
   f16x_t acc[MAXNMI][2];
 #pragma unroll
@@ -260,7 +279,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     load_bc(kc + J + 2, BNEW);                                       \
     __builtin_amdgcn_sched_barrier(0);                               \
     pin_b(BCUR);                                                     \
-    wave_step<NMI, MAXNMI>(As + J * ABUF, BCUR, shift, bc, acc);     \
+    wave_step<NMI, MAXNMI, Q3>(As + J * ABUF, BCUR, shift, hshift, bc, bch, acc); \
     __syncthreads();                                                 \
   }
     // whole groups of three steps with no branch inside (exact wait counts),
@@ -299,7 +318,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     load_bc(kc + J + DEPTH, Br[(J + DEPTH) % R]);                              \
     __builtin_amdgcn_sched_barrier(0);                                         \
     pin_b(Br[J % R]);                                                          \
-    wave_step<NMI, MAXNMI>(As + (J % 3) * ABUF, Br[J % R], shift, bc, acc);    \
+    wave_step<NMI, MAXNMI, Q3>(As + (J % 3) * ABUF, Br[J % R], shift, hshift, bc, bch, acc); \
     __syncthreads();                                                           \
   }
   // whole groups of U steps with no branch inside (exact wait counts), then
@@ -355,73 +374,91 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   }
 }
 
-// One kernel per projection and tile height: MAXNMI = 4 (128-row tiles, for
-// prompt chunks) or 1 (32-row tiles, for verify batches of many sequences,
-// whose experts have a few to a few dozen rows).
-template <bool GATEUP, int MAXNMI>
-__global__ __launch_bounds__(256, MAXNMI == 4 ? 2 : 3) void k_gemm_q2(
-    const uint8_t* __restrict__ r_codes, const uint16_t* __restrict__ r_scales, const uint8_t* __restrict__ s_codes,
-    const uint16_t* __restrict__ s_scales, size_t code_stride, size_t scale_stride, int H, int I, int E,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ sorted_rows,
-    int T, int k, const uint16_t* __restrict__ a_src, uint16_t* __restrict__ h_out, float* __restrict__ y_out,
-    const float* __restrict__ gates, uint16_t* __restrict__ y16) {
+struct GemmKArgs {
+  MatRef routed, shared;
+  int H, I, E, T, k;
+  const int32_t* tiles;
+  const int32_t* n_tiles;
+  const int32_t* sorted_rows;
+  const uint16_t* a_src;
+  uint16_t* h_out;
+  float* y_out;
+  const float* gates;
+  uint16_t* y16;
+  const int32_t* slot_map;   // expert-cache mode: pool slot of routed group g, or -1 (a miss)
+};
+
+// One kernel per projection, tile height and format: MAXNMI = 4 (128-row
+// tiles, 2-bit, for prompt chunks) or 1 (32-row tiles, for verify batches of
+// many sequences, whose experts have a few to a few dozen rows; 2- or 3-bit).
+// In expert-cache mode a tile whose group has no slot computes nothing: the
+// down projection writes zero rows, so the combine adds nothing for it.
+template <bool GATEUP, int MAXNMI, bool Q3>
+__global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(GemmKArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[3 * 32 * MAXNMI * A_STRIDE];
   __shared__ float row_gate[32 * MAXNMI];
   GemmTile t;
-  if (!load_tile(tiles, n_tiles, t)) return;
-  if (!GATEUP && y16) {
+  if (!load_tile(a.tiles, a.n_tiles, t)) return;
+  const bool sh = t.g == a.E;
+  int slot = t.g;
+  if (a.slot_map && !sh) {
+    slot = a.slot_map[t.g];
+    if (slot < 0) {
+      if (!GATEUP) {
+        for (int i = threadIdx.x; i < t.rows * GCOLS; i += blockDim.x)
+          a.y_out[(size_t)(t.m0 + i / GCOLS) * a.H + t.n * GCOLS + i % GCOLS] = 0.0f;
+      }
+      return;
+    }
+  }
+  if (!GATEUP && a.y16) {
     // gate of every row of the tile (1 for the shared expert), read in the
     // epilogue after the K loop's barriers
     for (int i = threadIdx.x; i < t.rows; i += blockDim.x) {
-      const int r = sorted_rows[t.m0 + i];
-      row_gate[i] = r < T * k ? gates[r] : 1.0f;
+      const int r = a.sorted_rows[t.m0 + i];
+      row_gate[i] = r < a.T * a.k ? a.gates[r] : 1.0f;
     }
   }
-  const bool sh = t.g == E;
-  const size_t eidx = sh ? 0 : (size_t)t.g;
+  const MatRef& M = sh ? a.shared : a.routed;
+  const size_t eidx = sh ? 0 : (size_t)slot;
   GemmArgs g;
-  g.codes = (sh ? s_codes : r_codes) + eidx * code_stride;
-  g.scales = (sh ? s_scales : r_scales) + eidx * scale_stride;
-  g.H = H;
-  g.I = I;
-  g.T = T;
-  g.k = k;
-  g.sorted_rows = sorted_rows;
-  g.a_src = a_src;
-  g.h_out = h_out;
-  g.y_out = y_out;
-  g.y16 = y16;
+  g.codes = M.codes + eidx * M.code_stride;
+  g.scales = M.scales + eidx * M.scale_stride;
+  g.hi = Q3 ? M.hi + eidx * M.hi_stride : nullptr;
+  g.H = a.H;
+  g.I = a.I;
+  g.T = a.T;
+  g.k = a.k;
+  g.sorted_rows = a.sorted_rows;
+  g.a_src = a.a_src;
+  g.h_out = a.h_out;
+  g.y_out = a.y_out;
+  g.y16 = a.y16;
   g.row_gate = row_gate;
   // prefetch depth: two steps for 128-row tiles (register budget), five for
-  // 32-row tiles (few rows: latency, not the matrix cores, sets the pace)
-  constexpr int D = MAXNMI == 4 ? 2 : 5;
+  // 32-row tiles (few rows: latency, not the matrix cores, sets the pace),
+  // three with the 3-bit high-bit planes
+  constexpr int D = MAXNMI == 4 ? 2 : (Q3 ? 3 : 5);
   const int nmi = __builtin_amdgcn_readfirstlane((t.rows + 31) >> 5);
   if (MAXNMI == 1 || nmi == 1) {
-    gemm_tile<GATEUP, 1, MAXNMI, D>(g, t, As);
+    gemm_tile<GATEUP, 1, MAXNMI, D, Q3>(g, t, As);
   } else if (MAXNMI == 2 || nmi == 2) {
-    gemm_tile<GATEUP, (MAXNMI >= 2 ? 2 : 1), MAXNMI, D>(g, t, As);
+    gemm_tile<GATEUP, (MAXNMI >= 2 ? 2 : 1), MAXNMI, D, Q3>(g, t, As);
   } else if (nmi == 3) {
-    gemm_tile<GATEUP, (MAXNMI >= 4 ? 3 : 1), MAXNMI, D>(g, t, As);
+    gemm_tile<GATEUP, (MAXNMI >= 4 ? 3 : 1), MAXNMI, D, Q3>(g, t, As);
   } else {
-    gemm_tile<GATEUP, MAXNMI, MAXNMI, D>(g, t, As);
+    gemm_tile<GATEUP, MAXNMI, MAXNMI, D, Q3>(g, t, As);
   }
 }
 
-template <int MAXNMI>
-static hipError_t launch_gemm_q2_t(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
-                                   const int32_t* tiles, const int32_t* n_tiles, int max_tiles,
-                                   const int32_t* sorted_rows, int T, int k, const uint16_t* a_f16, void* out,
-                                   hipStream_t s, const float* gates, uint16_t* y16) {
+template <int MAXNMI, bool Q3>
+static hipError_t launch_gemm_q2_t(GemvKind kind, GemmKArgs a, int max_tiles, void* out, hipStream_t s) {
   if (kind == GemvKind::GateUp) {
-    MOE_LAUNCH((k_gemm_q2<true, MAXNMI>), dim3(max_tiles, I / 128), dim3(256), 0, s, routed.codes, routed.scales,
-               shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles, n_tiles,
-               sorted_rows, T, k, a_f16, (uint16_t*)out, (float*)nullptr, (const float*)nullptr,
-               (uint16_t*)nullptr);
+    a.h_out = (uint16_t*)out;
+    MOE_LAUNCH((k_gemm_q2<true, MAXNMI, Q3>), dim3(max_tiles, a.I / 128), dim3(256), 0, s, a);
   } else {
-    MOE_LAUNCH((k_gemm_q2<false, MAXNMI>), dim3(max_tiles, H / GCOLS), dim3(256), 0, s, routed.codes,
-               routed.scales, shared.codes, shared.scales, routed.code_stride, routed.scale_stride, H, I, E, tiles,
-               n_tiles, sorted_rows, T, k, a_f16, (uint16_t*)nullptr, y16 ? (float*)nullptr : (float*)out, gates,
-               y16);
+    a.y_out = a.y16 ? nullptr : (float*)out;
+    MOE_LAUNCH((k_gemm_q2<false, MAXNMI, Q3>), dim3(max_tiles, a.H / GCOLS), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -429,13 +466,31 @@ static hipError_t launch_gemm_q2_t(GemvKind kind, const MatRef& routed, const Ma
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
-                          uint16_t* y16, int tile_rows) {
+                          uint16_t* y16, int tile_rows, bool q3, const int32_t* slot_map) {
   if (max_tiles <= 0) return hipSuccess;
-  if (tile_rows == 32)
-    return launch_gemm_q2_t<1>(kind, routed, shared, H, I, E, tiles, n_tiles, max_tiles, sorted_rows, T, k, a_f16,
-                               out, s, gates, y16);
-  return launch_gemm_q2_t<GBM / 32>(kind, routed, shared, H, I, E, tiles, n_tiles, max_tiles, sorted_rows, T, k,
-                                    a_f16, out, s, gates, y16);
+  GemmKArgs a = {};
+  a.routed = routed;
+  a.shared = shared;
+  a.H = H;
+  a.I = I;
+  a.E = E;
+  a.T = T;
+  a.k = k;
+  a.tiles = tiles;
+  a.n_tiles = n_tiles;
+  a.sorted_rows = sorted_rows;
+  a.a_src = a_f16;
+  a.gates = gates;
+  a.y16 = y16;
+  a.slot_map = slot_map;
+  if (q3) {
+    // 3-bit weights run on 32-row tiles only (the 128-row kernel's registers
+    // have no room for the high-bit planes); y16 is not used with them
+    if (tile_rows != 32 || y16) return hipErrorInvalidValue;
+    return launch_gemm_q2_t<1, true>(kind, a, max_tiles, out, s);
+  }
+  if (tile_rows == 32) return launch_gemm_q2_t<1, false>(kind, a, max_tiles, out, s);
+  return launch_gemm_q2_t<GBM / 32, false>(kind, a, max_tiles, out, s);
 }
 
 // ---------------------------------------------------------------------------

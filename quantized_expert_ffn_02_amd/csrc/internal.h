@@ -177,7 +177,8 @@ hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out,
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates = nullptr,
-                          uint16_t* y16 = nullptr, int tile_rows = 128);
+                          uint16_t* y16 = nullptr, int tile_rows = 128, bool q3 = false,
+                          const int32_t* slot_map = nullptr);
 // skinny MFMA GEMMs (gemm_skinny.hip): 32-row chunks x 64 columns, K split over waves
 static constexpr int kSkinnyRows = 32;
 hipError_t launch_gemm_skinny(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,

@@ -96,7 +96,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xf32 = take(dense ? T * H * 4 : 0);
   o.xf16 = take(dense ? 0 : T * H * 2);
   o.hf16 = take(dense ? 0 : n * I * 2);
-  o.tiles = take((n / kSkinnyRows + E + 2) * 3 * 4);   // GEMM tiles or skinny chunks
+  o.tiles = take((n / kSmallTileRows + E + 2) * 3 * 4);   // GEMM tiles (128 or 32 rows)
   o.n_tiles = take(4);
   o.h = take(n * I * 4);
   o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
@@ -172,7 +172,7 @@ int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float
     // prompt chunks: 128 x 128 MFMA tiles; verify batches: 32-token chunks with K
     // split over waves; a decode step: one wave per expert row
     if (T >= 1024) return launch_router_mfma(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
-    if (T > 16) return launch_router_skinny(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+    if (T > 16) return launch_router_split(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
     return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
   }));
   MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
@@ -382,8 +382,8 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   int32_t* chunks = at<int32_t>(ws, lay.tiles);
   int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
   MOE_TRY(launch_plan(offsets, E, 1, 1, chunks, n_chunks, at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items),
-                      s, kSkinnyRows));
-  const int max_chunks = n / kSkinnyRows + std::min(E + 1, n) + 1;
+                      s, kSmallTileRows));
+  const int max_chunks = n / kSmallTileRows + std::min(E + 1, n) + 1;
   const bool q3 = routed.fmt == MOE_FMT_Q3;
   const MatRef r13 = mat_w13(routed), r2 = mat_w2(routed);
   const MatRef s13 = with_shared ? mat_w13(L->shared) : MatRef(), s2 = with_shared ? mat_w2(L->shared) : MatRef();
@@ -393,11 +393,11 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
-                          nullptr, nullptr, kSkinnyRows, q3, slot_map);
+                          nullptr, nullptr, kSmallTileRows, q3, slot_map);
   }));
   MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
-                          nullptr, nullptr, kSkinnyRows, q3, slot_map);
+                          nullptr, nullptr, kSmallTileRows, q3, slot_map);
   }));
   MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
   return MOE_OK;

@@ -1,30 +1,26 @@
-// MFMA grouped GEMMs for prefill chunks and large token groups, and the MFMA
-// router GEMM.
+// MFMA grouped GEMMs over the quantized experts, and the MFMA router GEMM of
+// prompt chunks.
 //
 // A prompt is read in chunks of up to 8,192 tokens (page "Strata Runs a
 // 125-Billion-Parameter Qwen Model on a 12 GB Gaming GPU at up to 93 Tokens per
-// Second"); for such a chunk every expert that a few dozen or more tokens chose
-// is a dense [M_e x 2560] x [2560 x 1280] product followed by [M_e x 640] x
-// [640 x 2560], which belongs on the matrix cores.
+// Second"); for such a chunk, and for verify batches of many sequences, every
+// expert chosen by a few or more tokens is a dense [M_e x 2560] x [2560 x 1280]
+// product followed by [M_e x 640] x [640 x 2560], which belongs on the matrix
+// cores.
 //
-// Precision: the weights are dequantised EXACTLY into fp16 (s * (c - 2) with an
-// fp16 scale and c - 2 in {-2, -1, 0, 1} is an fp16 value), activations enter as
-// fp16 (bf16 -> fp16 is exact for |x| >= 2^-17 and below 65504), products are
-// exact and accumulate in fp32 (v_mfma_f32_32x32x16_f16); h = SiLU(gate) * up is
-// carried in fp16 between the two GEMMs and the output is fp32.
+// Precision: the weights are dequantised EXACTLY into fp16 (mfma.h: s (c - 2)
+// with an fp16 scale and c - 2 in {-2, -1, 0, 1} is an fp16 value; 3-bit
+// weights as two exact fragments), activations enter as fp16 (bf16 -> fp16 is
+// exact for normal values below 65504), products are exact and accumulate in
+// fp32 (v_mfma_f32_32x32x16_f16); h = SiLU(gate) * up is carried in fp16
+// between the two GEMMs.  The down projection writes fp32 rows, or, for a
+// prompt chunk, fp16 rows already multiplied by their gate.
 //
 // Operand order: the 2-bit unpacking yields weights in "pair order" -- inside
 // each aligned group of 16 columns the order is (0, 8, 1, 9, ..., 7, 15).  The
 // MFMA sums over K in any order as long as both operands agree, so the fp16
 // activations (x, and h from the gate/up epilogue) are stored in the same order
 // and no operand is ever permuted inside the GEMM.
-//
-// Tiles: a block computes 128 rows (sorted positions of one expert) x 128
-// columns with 4 waves of 64 x 64 (2 x 2 MFMA 32x32 tiles); the K loop steps by
-// 64 with double-buffered LDS: the next step's global loads are in flight while
-// the current step's MFMAs run, and the dequantisation happens on the way into
-// LDS.  The gate/up kernel's 128 columns are 64 gate + the 64 matching up
-// columns, so SwiGLU is applied in registers.
 #include <math.h>
 
 #include <type_traits>
@@ -71,18 +67,17 @@ hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out,
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM over the 2-bit experts.
+// Grouped GEMM over the quantized experts.
 //
-// A block owns one M-tile (up to GBM = 128 sorted rows of one expert group) and
+// A block owns one M-tile (up to 128 or 32 sorted rows of one expert group) and
 // 4 x 64 weight rows ("columns" of the product); each of its 4 waves computes
-// all 128 rows x its own 64 columns as 4 x 2 MFMA 32x32x16 tiles.  The
-// activations A are shared by the 4 waves and go through LDS (double-buffered,
+// all the tile's rows x its own 64 columns as 32x32x16 MFMA tiles.  The
+// activations A are shared by the 4 waves and go through LDS (three buffers,
 // rows padded to 72 halves so that the fragment reads are free of bank
 // conflicts).  The weights B are used by exactly one wave, so each wave reads
-// its 2-bit codes straight from global memory into registers and dequantises
-// them there into MFMA B fragments: no LDS traffic and no duplicated work for B.
-//
-// The B fragments are dequantised exactly into fp16 (mfma.h).
+// its codes straight from global memory into registers and dequantises them
+// there into MFMA B fragments (mfma.h): no LDS traffic and no duplicated work
+// for B.  Loads run DEPTH K-steps ahead through rings of register sets.
 // ---------------------------------------------------------------------------
 static constexpr int GBM = 128;              // rows per M-tile (32 x fragments per wave)
 static constexpr int GBK = 64;               // K per pipeline step

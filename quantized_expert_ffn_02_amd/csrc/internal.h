@@ -179,14 +179,11 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates = nullptr,
                           uint16_t* y16 = nullptr, int tile_rows = 128, bool q3 = false,
                           const int32_t* slot_map = nullptr);
-// skinny MFMA GEMMs (gemm_skinny.hip): 32-row chunks x 64 columns, K split over waves
-static constexpr int kSkinnyRows = 32;
-hipError_t launch_gemm_skinny(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
-                              const int32_t* chunks, const int32_t* n_chunks, int max_chunks,
-                              const int32_t* sorted_rows, int T, int k, const uint16_t* a_f16, void* out,
-                              hipStream_t s);
-hipError_t launch_router_skinny(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
-                                float* logits, hipStream_t s);
+// rows per tile of the grouped GEMM for batches beyond a decode step and below a prompt chunk
+static constexpr int kSmallTileRows = 32;
+// router of such batches (router_split.hip): 32 tokens x 64 experts per block, K split over waves
+hipError_t launch_router_split(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
+                               float* logits, hipStream_t s);
 // out[t] = sum over the token's entries of the gate-scaled fp16 rows y16 (rank
 // order, then the shared expert) (+ residual), fp32, optional bf16 copy
 hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,

@@ -87,7 +87,19 @@ static constexpr int GCOLS = 256;            // weight rows per block (4 waves x
 // One K step of a wave: 4 x (2 B fragments, NMI A fragments, 2 NMI MFMAs);
 // NMI = number of 32-row fragments the tile's rows need.  3-bit weights add the
 // high-bit fragment of each column and a second MFMA into the same accumulator.
-template <int NMI, int MAXNMI, bool Q3, typename BR>
+//
+// TR (128-row tiles): the weights enter as the MFMA's first operand and the
+// activations as its second, so the accumulator holds C^T: lane l has token
+// row 32 mi + l % 32 and, in registers 4 q .. 4 q + 3, four consecutive output
+// columns 8 q + 4 (l / 32) + (0..3) -- the epilogue stores rows in 8- and
+// 16-byte pieces instead of 2-byte scatters.
+template <bool TR>
+__device__ __forceinline__ f16x_t mfma_op(h8_t a, h8_t b, f16x_t c) {
+  return TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0)
+            : __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+template <int NMI, int MAXNMI, bool Q3, bool TR, typename BR>
 __device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const BR& R, int shift, int hshift,
                                           const BConst& bc, const BConstHi& bch, f16x_t acc[MAXNMI][2]) {
   const int lane = threadIdx.x & 63;
@@ -109,11 +121,11 @@ __device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const
 #pragma unroll
     for (int mi = 0; mi < NMI; ++mi) {
       const h8_t a = *reinterpret_cast<const h8_t*>(As + (mi * 32 + r) * A_STRIDE + s * 16 + kh);
-      acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[mi][0], 0, 0, 0);
-      acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[mi][1], 0, 0, 0);
+      acc[mi][0] = mfma_op<TR>(a, b0, acc[mi][0]);
+      acc[mi][1] = mfma_op<TR>(a, b1, acc[mi][1]);
       if constexpr (Q3) {
-        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh0, acc[mi][0], 0, 0, 0);
-        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh1, acc[mi][1], 0, 0, 0);
+        acc[mi][0] = mfma_op<TR>(a, bh0, acc[mi][0]);
+        acc[mi][1] = mfma_op<TR>(a, bh1, acc[mi][1]);
       }
     }
   }
@@ -174,47 +186,64 @@ struct GemmArgs {
   float* y_out;           // down, fp32 rows (NULL when y16 is used)
   uint16_t* y16;          // down, fp16 rows already multiplied by their entry's gate
   const float* row_gate;  // LDS: gate of each of the tile's rows (y16 only)
+  uint32_t a_bytes;       // bytes of a_src, code and scale bytes of this expert
+  uint32_t code_bytes, scale_bytes;
 };
+
+// Raw buffer resource (gfx9 layout, stride 0) over `bytes` bytes from `base`:
+// loads take a 32-bit per-lane offset and a wave-uniform scalar offset, and
+// return zero past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // MAXNMI = 32-row fragments per wave (tile height 32 MAXNMI: 32, 64 or 128
 // rows); NMI <= MAXNMI the fragments this tile's rows need.  As holds three LDS
-// buffers of the A tile.
+// buffers of the A tile.  128-row tiles run with the transposed accumulator
+// (TR, see mfma_op).
 template <bool GATEUP, int NMI, int MAXNMI, int DEPTH, bool Q3>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, uint16_t* As) {
   typedef typename std::conditional<Q3, BRegs3, BRegs>::type BRegs;
+  constexpr bool TR = MAXNMI == 4;
   constexpr int BMX = 32 * MAXNMI;          // tile rows
-  constexpr int TPR = 256 / BMX;            // threads staging one A row (2, 4 or 8)
-  constexpr int NV = 8 / TPR;               // 16-byte A chunks per thread and step
+  constexpr int NV = BMX / 32;              // 16-byte A chunks per thread and step
   constexpr int ABUF = BMX * A_STRIDE;      // halves per LDS buffer
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = GATEUP ? g.H : g.I;
   const int nch = K / GBK;
 
-  // A staging: thread -> (row ra = tid / TPR, slice ha = tid % TPR of NV
-  // 16-byte chunks) of the step.  Rows past the tile's rows load its first row
-  // (no lane-divergent branch around the loads; LDS rows past NMI * 32 are
-  // never read).
-  const int ra = tid / TPR, ha = tid % TPR;
-  const u32x4* ag[1];
-  {
-    const int pa = t.m0 + (ra < t.rows ? ra : 0);
-    size_t arow;
+  // A staging: a step's tile is BMX rows x 8 chunks of 16 bytes; chunk
+  // q * 256 + tid (row 32 q + tid / 8, chunk tid % 8) is this thread's q-th, so
+  // every load instruction of a wave covers eight whole 128-byte row segments.
+  // Rows past the tile's rows load its first row (no lane-divergent branch
+  // around the loads; LDS rows past NMI * 32 are never read).
+  const __amdgpu_buffer_rsrc_t a_rsrc = buffer_rsrc(g.a_src, g.a_bytes);
+  uint32_t a_voff[NV];
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int rr = 32 * q + (tid >> 3);
+    const int pa = t.m0 + (rr < t.rows ? rr : 0);
+    uint32_t arow;
     if (GATEUP) {
       const int r = g.sorted_rows[pa];
       const int Tk = g.T * g.k;
-      arow = (size_t)(r < Tk ? r / g.k : r - Tk);
+      arow = (uint32_t)(r < Tk ? r / g.k : r - Tk);
     } else {
-      arow = (size_t)pa;
+      arow = (uint32_t)pa;
     }
-    ag[0] = reinterpret_cast<const u32x4*>(g.a_src + arow * K) + ha * NV;
+    a_voff[q] = (arow * (uint32_t)K + (uint32_t)(tid & 7) * 8u) * 2u;
   }
-  const int a_off = ra * A_STRIDE + ha * NV * 8;
+  const int a_off = (tid >> 3) * A_STRIDE + (tid & 7) * 8;
 
-  // B columns of this lane
+  // B columns of this lane.  Gate/up with TR: lane m of the wave's 32 loads the
+  // column whose pair-order position is m (position 2 j <- column j, 2 j + 1 <-
+  // column 8 + j inside each 16-group), so accumulator rows come out in pair
+  // order and h is stored as it is laid out.
   int n0, n1;
   if (GATEUP) {
-    n0 = t.n * 128 + wv * 32 + (lane & 31);
+    const int m = lane & 31, j = m & 15;
+    n0 = t.n * 128 + wv * 32 + (TR ? ((m & 16) | ((j & 1) ? 8 + (j >> 1) : (j >> 1))) : m);
     n1 = g.I + n0;
   } else {
     n0 = t.n * GCOLS + wv * 64 + (lane & 31);
@@ -222,6 +251,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   }
   const BCol B0 = b_column(g.codes, g.scales, n0, K, Q3 ? g.hi : nullptr);
   const BCol B1 = b_column(g.codes, g.scales, n1, K, Q3 ? g.hi : nullptr);
+  // 2-bit codes and scales through buffer loads: per-lane byte offsets of
+  // column n0 (16 code bytes per step; 8 scale bytes per 128 K, the layout of
+  // b_column) and the wave-uniform distance to column n1
+  const __amdgpu_buffer_rsrc_t c_rsrc = buffer_rsrc(g.codes, g.code_bytes);
+  const __amdgpu_buffer_rsrc_t s_rsrc = buffer_rsrc(g.scales, g.scale_bytes);
+  const uint32_t c_voff = (uint32_t)((((n0 >> 6) * (K / 64)) * 64 + (n0 & 63)) * 16);
+  const uint32_t s_voff = (uint32_t)((((n0 >> 6) * (K / 128)) * 64 + (n0 & 63)) * 8);
+  const uint32_t c_d1 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)((((n1 >> 6) * (K / 64)) * 64 + (n1 & 63)) * 16) - c_voff);
+  const uint32_t s_d1 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)((((n1 >> 6) * (K / 128)) * 64 + (n1 & 63)) * 8) - s_voff);
   const int shift = (lane >> 5) * 8, hshift = (lane >> 5) * 4;
   const BConst bc = bconst();
   BConstHi bch;
@@ -243,14 +283,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   auto load_a = [&](int kc, ARegs& R) {
     kc = kc < nch ? kc : nch - 1;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) R.a[q] = ag[0][kc * 8 + q];
+    for (int q = 0; q < NV; ++q) R.a[q] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_voff[q], kc * 128, 0);
   };
   auto store_a = [&](const ARegs& R, int buf) {
-    u32x4* d = reinterpret_cast<u32x4*>(As + buf * ABUF + a_off);
 #pragma unroll
-    for (int q = 0; q < NV; ++q) d[q] = R.a[q];
+    for (int q = 0; q < NV; ++q) *reinterpret_cast<u32x4*>(As + buf * ABUF + a_off + 32 * q * A_STRIDE) = R.a[q];
   };
-  auto load_bc = [&](int kc, BRegs& R) { load_b(B0, B1, kc < nch ? kc : nch - 1, R); };
+  auto load_bc = [&](int kc, BRegs& R) {
+    kc = kc < nch ? kc : nch - 1;
+    if constexpr (Q3) {
+      load_b(B0, B1, kc, R);
+    } else {
+      // codes: 1024 bytes per step; scales: blocks 2 kc, 2 kc + 1 at dword
+      // (kc / 2) * 128 + kc % 2
+      const int so = (kc >> 1) * 512 + (kc & 1) * 4;
+      R.c0 = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff, kc * 1024, 0);
+      R.s0 = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so, 0);
+      R.c1 = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff, kc * 1024 + c_d1, 0);
+      R.s1 = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so + s_d1, 0);
+    }
+  };
 
   if constexpr (DEPTH == 2) {
     // Three register sets with static names (the loop is unrolled by three).
@@ -274,7 +326,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     load_bc(kc + J + 2, BNEW);                                       \
     __builtin_amdgcn_sched_barrier(0);                               \
     pin_b(BCUR);                                                     \
-    wave_step<NMI, MAXNMI, Q3>(As + J * ABUF, BCUR, shift, hshift, bc, bch, acc); \
+    wave_step<NMI, MAXNMI, Q3, TR>(As + J * ABUF, BCUR, shift, hshift, bc, bch, acc); \
     __syncthreads();                                                 \
   }
     // whole groups of three steps with no branch inside (exact wait counts),
@@ -313,7 +365,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     load_bc(kc + J + DEPTH, Br[(J + DEPTH) % R]);                              \
     __builtin_amdgcn_sched_barrier(0);                                         \
     pin_b(Br[J % R]);                                                          \
-    wave_step<NMI, MAXNMI, Q3>(As + (J % 3) * ABUF, Br[J % R], shift, hshift, bc, bch, acc); \
+    wave_step<NMI, MAXNMI, Q3, TR>(As + (J % 3) * ABUF, Br[J % R], shift, hshift, bc, bch, acc); \
     __syncthreads();                                                           \
   }
   // whole groups of U steps with no branch inside (exact wait counts), then
@@ -329,6 +381,92 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
 #undef MOE_GEMM_STEP
   }
 
+  if constexpr (TR) {
+    // lane: token row 32 mi + l % 32; registers 4 q .. 4 q + 3: columns
+    // 8 q + 4 (l / 32) + (0..3) of the wave's 32 (gate/up, pair-order
+    // positions) or of each of its two 32-column halves f (down)
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const int l32 = lane & 31, c4 = 4 * (lane >> 5);
+    auto pack2 = [](float a, float b) {
+      return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    };
+    if (GATEUP) {
+      // h = SiLU(gate) * up in fp16, 8-byte stores
+      const int hb = t.n * 128 + wv * 32 + c4;
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) {
+        const int row = mi * 32 + l32;
+        if (row < t.rows) {
+          uint16_t* dst = g.h_out + (size_t)(t.m0 + row) * g.I + hb;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float hv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float gv = acc[mi][0][4 * q + j], uv = acc[mi][1][4 * q + j];
+              hv[j] = gv / (1.0f + expf(-gv)) * uv;
+            }
+            *reinterpret_cast<u2v*>(dst + 8 * q) = u2v{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
+          }
+        }
+      }
+    } else if (g.y16) {
+      // gate-scaled fp16 rows through LDS (the A buffers are free after the K
+      // loop's last barrier): each wave writes its own 64 rows x 64 columns
+      // region in 8-byte pieces, reads it back as 16-byte row chunks and
+      // stores whole 128-byte row segments; two rounds of 64 rows.  Rows of 68
+      // halves keep both LDS passes free of bank conflicts.
+      constexpr int RS = 68;
+      static_assert(4 * 64 * RS <= 3 * ABUF, "epilogue staging exceeds the A buffers");
+      uint16_t* W = As + wv * (64 * RS);
+      const int cb = t.n * GCOLS + wv * 64;
+#pragma unroll
+      for (int hr = 0; hr < (NMI + 1) / 2; ++hr) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const int mi = 2 * hr + mm;
+          if (mi < NMI) {
+            const float gt = g.row_gate[mi * 32 + l32];
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f16x_t& c = acc[mi][f];
+                *reinterpret_cast<u2v*>(W + (mm * 32 + l32) * RS + f * 32 + 8 * q + c4) =
+                    u2v{pack2(gt * c[4 * q], gt * c[4 * q + 1]), pack2(gt * c[4 * q + 2], gt * c[4 * q + 3])};
+              }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = i * 64 + lane, rl = idx >> 3, ch = idx & 7, row = hr * 64 + rl;
+          const u2v lo = *reinterpret_cast<const u2v*>(W + rl * RS + ch * 8);
+          const u2v hi = *reinterpret_cast<const u2v*>(W + rl * RS + ch * 8 + 4);
+          if (row < t.rows)
+            *reinterpret_cast<u32x4*>(g.y16 + (size_t)(t.m0 + row) * g.H + cb + ch * 8) = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+    } else {
+      // fp32 rows, 16-byte stores
+      const int cb = t.n * GCOLS + wv * 64 + c4;
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) {
+        const int row = mi * 32 + l32;
+        if (row < t.rows) {
+          float* dst = g.y_out + (size_t)(t.m0 + row) * g.H + cb;
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<f4v*>(dst + 32 * f + 8 * q) =
+                  f4v{acc[mi][f][4 * q], acc[mi][f][4 * q + 1], acc[mi][f][4 * q + 2], acc[mi][f][4 * q + 3]};
+        }
+      }
+    }
+    return;
+  }
   if (GATEUP) {
     // h = SiLU(gate) * up, fp16, stored at the pair-order position of its column
     const int col = t.n * 128 + wv * 32 + (lane & 31);
@@ -430,6 +568,10 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(Ge
   g.y_out = a.y_out;
   g.y16 = a.y16;
   g.row_gate = row_gate;
+  // byte sizes of the buffer resources (the host checks that they fit 31 bits)
+  g.a_bytes = GATEUP ? (uint32_t)a.T * (uint32_t)a.H * 2u : (uint32_t)(a.T * a.k + a.T) * (uint32_t)a.I * 2u;
+  g.code_bytes = (uint32_t)M.code_stride;
+  g.scale_bytes = (uint32_t)(M.scale_stride * 2);
   // prefetch depth: two steps for 128-row tiles (register budget), five for
   // 32-row tiles (few rows: latency, not the matrix cores, sets the pace),
   // three with the 3-bit high-bit planes
@@ -463,6 +605,11 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
                           uint16_t* y16, int tile_rows, bool q3, const int32_t* slot_map) {
   if (max_tiles <= 0) return hipSuccess;
+  // the kernels address activations and one expert's weights with 32-bit
+  // buffer offsets
+  const uint64_t a_bytes = kind == GemvKind::GateUp ? (uint64_t)T * H * 2 : (uint64_t)T * (k + 1) * I * 2;
+  if (a_bytes > 0x7FFFFFFFu || routed.code_stride > 0x7FFFFFFFu || shared.code_stride > 0x7FFFFFFFu)
+    return hipErrorInvalidValue;
   GemmKArgs a = {};
   a.routed = routed;
   a.shared = shared;

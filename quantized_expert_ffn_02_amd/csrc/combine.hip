@@ -11,6 +11,11 @@
 
 namespace moe {
 
+// Loads are issued a batch of kCombineBatch entries at a time (indices clamped
+// to the last entry, extra values dropped) and then added in entry order, so a
+// thread waits for one memory round trip per batch instead of one per entry.
+static constexpr int kCombineBatch = 12;
+
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_sorted,
                                                  const int32_t* __restrict__ row_to_sorted,
                                                  const float* __restrict__ gates, int T, int k, int H,
@@ -20,30 +25,40 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_sor
   const int q = blockIdx.x * blockDim.x + threadIdx.x;   // index of 4 consecutive outputs
   if (q * 4 >= H) return;
   const size_t H4 = H / 4;
+  uint2 rb = make_uint2(0u, 0u);
+  if (residual) rb = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[q];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = 0; i < k; ++i) {
-    const float g = gates[(size_t)t * k + i];
-    const size_t p = (size_t)row_to_sorted[(size_t)t * k + i];
-    const float4 y = reinterpret_cast<const float4*>(y_sorted)[p * H4 + q];
-    acc.x = fmaf(g, y.x, acc.x);
-    acc.y = fmaf(g, y.y, acc.y);
-    acc.z = fmaf(g, y.z, acc.z);
-    acc.w = fmaf(g, y.w, acc.w);
-  }
-  if (with_shared) {
-    const size_t p = (size_t)row_to_sorted[(size_t)T * k + t];
-    const float4 y = reinterpret_cast<const float4*>(y_sorted)[p * H4 + q];
-    acc.x += y.x;
-    acc.y += y.y;
-    acc.z += y.z;
-    acc.w += y.w;
+  const int n = k + (with_shared ? 1 : 0);
+  for (int i0 = 0; i0 < n; i0 += kCombineBatch) {
+    float4 y[kCombineBatch];
+    float g[kCombineBatch];
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const int i = i0 + j < n ? i0 + j : n - 1;
+      const size_t r = i < k ? (size_t)t * k + i : (size_t)T * k + t;
+      g[j] = i < k ? gates[r] : 1.0f;
+      y[j] = reinterpret_cast<const float4*>(y_sorted)[(size_t)row_to_sorted[r] * H4 + q];
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (i0 + j < k) {
+        acc.x = fmaf(g[j], y[j].x, acc.x);
+        acc.y = fmaf(g[j], y[j].y, acc.y);
+        acc.z = fmaf(g[j], y[j].z, acc.z);
+        acc.w = fmaf(g[j], y[j].w, acc.w);
+      } else if (i0 + j < n) {   // the shared expert, weight 1
+        acc.x += y[j].x;
+        acc.y += y[j].y;
+        acc.z += y[j].z;
+        acc.w += y[j].w;
+      }
+    }
   }
   if (residual) {
-    const uint2 r = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[q];
-    acc.x += bf16_to_f32(r.x & 0xFFFFu);
-    acc.y += bf16_to_f32(r.x >> 16);
-    acc.z += bf16_to_f32(r.y & 0xFFFFu);
-    acc.w += bf16_to_f32(r.y >> 16);
+    acc.x += bf16_to_f32(rb.x & 0xFFFFu);
+    acc.y += bf16_to_f32(rb.x >> 16);
+    acc.z += bf16_to_f32(rb.y & 0xFFFFu);
+    acc.w += bf16_to_f32(rb.y >> 16);
   }
   reinterpret_cast<float4*>(out)[(size_t)t * H4 + q] = acc;
   if (out_bf16) {
@@ -79,20 +94,30 @@ __global__ __launch_bounds__(256) void k_combine16(const uint16_t* __restrict__ 
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  uint4 rb = make_uint4(0u, 0u, 0u, 0u);
+  if (residual) rb = reinterpret_cast<const uint4*>(residual + (size_t)t * H)[q];
   const int n = k + (with_shared ? 1 : 0);
-  for (int i = 0; i < n; ++i) {
-    const size_t r = i < k ? (size_t)t * k + i : (size_t)T * k + t;
-    const size_t p = (size_t)row_to_sorted[r];
-    const uint4 v = reinterpret_cast<const uint4*>(y16)[p * H8 + q];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int i0 = 0; i0 < n; i0 += kCombineBatch) {
+    uint4 v[kCombineBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] += fp16_to_f32(w[j] & 0xFFFFu);
-      acc[2 * j + 1] += fp16_to_f32(w[j] >> 16);
+    for (int j = 0; j < kCombineBatch; ++j) {
+      const int i = i0 + j < n ? i0 + j : n - 1;
+      const size_t r = i < k ? (size_t)t * k + i : (size_t)T * k + t;
+      v[j] = reinterpret_cast<const uint4*>(y16)[(size_t)row_to_sorted[r] * H8 + q];
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (i0 + j < n) {
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] += fp16_to_f32(w[h] & 0xFFFFu);
+          acc[2 * h + 1] += fp16_to_f32(w[h] >> 16);
+        }
+      }
     }
   }
   if (residual) {
-    const uint4 rb = reinterpret_cast<const uint4*>(residual + (size_t)t * H)[q];
     const uint32_t w[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

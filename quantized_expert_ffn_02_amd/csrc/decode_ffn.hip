@@ -216,32 +216,41 @@ __global__ __launch_bounds__(W * 64) void k_decode_down(
 }
 
 // out[t] = sum_{i<k} (g y)[t k + i] + y[T k + t] (+ residual[t]), fixed order;
-// optional bf16 copy.  Four consecutive outputs per thread.
+// optional bf16 copy.  Four consecutive outputs per thread; the token's rows
+// are loaded kBatch at a time before they are added (one memory round trip
+// per batch, not per row).
 __global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ y, int T, int k, int H,
                                                         int with_shared, const uint16_t* __restrict__ residual,
                                                         float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+  constexpr int kBatch = 12;
   const int t = blockIdx.y;
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
   if (q * 4 >= H) return;
   const size_t H4 = H / 4;
   const float4* __restrict__ y4 = reinterpret_cast<const float4*>(y);
+  uint2 rb = make_uint2(0u, 0u);
+  if (residual) rb = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[q];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = 0; i < k; ++i) {
-    const float4 v = y4[((size_t)t * k + i) * H4 + q];
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  if (with_shared) {
-    const float4 v = y4[((size_t)T * k + t) * H4 + q];
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+  const int n = k + (with_shared ? 1 : 0);
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j < n ? i0 + j : n - 1;
+      const size_t r = i < k ? (size_t)t * k + i : (size_t)T * k + t;
+      v[j] = y4[r * H4 + q];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (i0 + j < n) {
+        acc.x += v[j].x;
+        acc.y += v[j].y;
+        acc.z += v[j].z;
+        acc.w += v[j].w;
+      }
+    }
   }
   if (residual) {
-    const uint2 rb = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[q];
     acc.x += bf16_to_f32(rb.x & 0xFFFFu);
     acc.y += bf16_to_f32(rb.x >> 16);
     acc.z += bf16_to_f32(rb.y & 0xFFFFu);

@@ -149,6 +149,46 @@ hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, i
 
 // Parameter-free RMSNorm of each bf16 row: bf16(x / sqrt(mean(x^2) + eps)), one
 // block per row, fixed-order fp32 reduction (the input of every layer of a stack).
+// Rows whose width is a multiple of 8 and at most 8,192: one 16-byte chunk per
+// thread (blockDim = H / 8 rounded up to whole waves), loaded once and kept in
+// registers for the scaling pass.  Other widths: one element per thread and
+// step.
+__device__ __forceinline__ float block_sum_fixed(float v, float* part, int nw) {
+  v = wave_sum(v);
+  const int tid = threadIdx.x;
+  if ((tid & 63) == 0) part[tid >> 6] = v;
+  __syncthreads();
+  float tot = 0.0f;
+  for (int i = 0; i < nw; ++i) tot += part[i];
+  return tot;
+}
+
+__global__ __launch_bounds__(1024) void k_rmsnorm_bf16_v8(const uint16_t* __restrict__ x, int H, float eps,
+                                                          uint16_t* __restrict__ out) {
+  __shared__ float part[16];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int nc = H / 8;
+  const uint4* __restrict__ xr = reinterpret_cast<const uint4*>(x + (size_t)row * H);
+  const uint4 v = tid < nc ? xr[tid] : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8], ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+    f[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = fmaf(f[j], f[j], ss);
+  const float tot = block_sum_fixed(ss, part, (int)(blockDim.x >> 6));
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  if (tid < nc) {
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_rne(f[2 * j] * inv) | (f32_to_bf16_rne(f[2 * j + 1] * inv) << 16);
+    reinterpret_cast<uint4*>(out + (size_t)row * H)[tid] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const uint16_t* __restrict__ x, int H, float eps,
                                                       uint16_t* __restrict__ out) {
   __shared__ float part[4];
@@ -159,17 +199,19 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const uint16_t* __restrict
     const float v = bf16_to_f32(xr[h]);
     ss = fmaf(v, v, ss);
   }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float tot = block_sum_fixed(ss, part, 4);
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
   for (int h = tid; h < H; h += 256) out[(size_t)row * H + h] = f32_to_bf16_rne(bf16_to_f32(xr[h]) * inv);
 }
 
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  MOE_LAUNCH(k_rmsnorm_bf16, dim3(T), dim3(256), 0, s, x, H, eps, out);
+  if (H % 8 == 0 && H <= 8192) {
+    const int threads = ((H / 8 + 63) / 64) * 64;
+    MOE_LAUNCH(k_rmsnorm_bf16_v8, dim3(T), dim3(threads), 0, s, x, H, eps, out);
+  } else {
+    MOE_LAUNCH(k_rmsnorm_bf16, dim3(T), dim3(256), 0, s, x, H, eps, out);
+  }
   return hipGetLastError();
 }
 

@@ -638,37 +638,68 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
 // ---------------------------------------------------------------------------
 // Router GEMM (bf16 MFMA): logits[t, e] = x_t . Wr[e] + b[e] for 128 x 128 tiles.
 // Both operands are bf16 in natural column order; products are exact in fp32.
+//
+// A prompt chunk has few tiles (8,192 tokens x 512 experts is one tile per
+// compute unit), so a block cannot count on a second block to hide memory
+// latency: it runs alone (launch bound 1) and keeps RDEPTH K-steps of both
+// operands in flight in registers.  Step m: write step m + 1 (loaded RDEPTH - 1
+// steps earlier) into the other LDS buffer, issue the loads of step m + RDEPTH
+// into the register set just freed, then 4 x 4 MFMAs per wave from LDS.  The
+// loop is unrolled by RDEPTH so that every register set has a static name.
+// Tile (m, n) is block n + 4 m of a linear order whose neighbours share one
+// XCD, so the expert tiles of a token tile read its rows from one L2.
 // ---------------------------------------------------------------------------
+static constexpr int RDEPTH = 6;
+
 __device__ __forceinline__ b8_t lds_frag_b(const uint16_t* base, int row, int k) {
   return *reinterpret_cast<const b8_t*>(base + row * LDS_STRIDE + k);
 }
 
-__global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restrict__ x, int T,
+__global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restrict__ x, int T,
                                                         const uint16_t* __restrict__ wr,
                                                         const float* __restrict__ bias, int E, int H,
                                                         float* __restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  const int ra = tid >> 1, ha = tid & 1;
-  const int arow_i = min(m0 + ra, T - 1), brow_i = min(n0 + ra, E - 1);
-  const u32x4* __restrict__ arow = reinterpret_cast<const u32x4*>(x + (size_t)arow_i * H) + ha * 4;
-  const u32x4* __restrict__ brow = reinterpret_cast<const u32x4*>(wr + (size_t)brow_i * H) + ha * 4;
-  const int nch = H / 64;
-  u32x4 pa[4], pb[4];
-  auto load_step = [&](int kc) {
+  const int ntn = (E + BN - 1) / BN, ntm = (T + BM - 1) / BM;
+  const int n_valid = ntm * ntn;
+  const int lin = blockIdx.x;
+  if (lin >= n_valid) return;
+  const int per = (n_valid + 7) / 8, xcd = lin & 7, slot = lin >> 3;
+  const int full = n_valid - 8 * (per - 1);
+  const int id = xcd < full ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
+  const int m0 = (id / ntn) * BM, n0 = (id % ntn) * BN;
+  // staging: chunk q * 256 + tid of a step is row 32 q + tid / 8, 16-byte chunk
+  // tid % 8 (whole 128-byte row segments per load instruction); rows past T or
+  // E load the last row and are never stored
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * (uint32_t)H * 2u);
+  const __amdgpu_buffer_rsrc_t wrr = buffer_rsrc(wr, (uint32_t)E * (uint32_t)H * 2u);
+  uint32_t xo[4], wo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = 32 * q + (tid >> 3);
+    xo[q] = ((uint32_t)min(m0 + rr, T - 1) * (uint32_t)H + (uint32_t)(tid & 7) * 8u) * 2u;
+    wo[q] = ((uint32_t)min(n0 + rr, E - 1) * (uint32_t)H + (uint32_t)(tid & 7) * 8u) * 2u;
+  }
+  const int st_off = (tid >> 3) * LDS_STRIDE + (tid & 7) * 8;
+  const int nch = H / BK;
+  struct Stage {
+    u32x4 a[4], b[4];
+  };
+  auto load = [&](int kc, Stage& S) {
+    kc = kc < nch ? kc : nch - 1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      pa[q] = arow[kc * 8 + q];
-      pb[q] = brow[kc * 8 + q];
+      S.a[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[q], kc * 128, 0);
+      S.b[q] = __builtin_amdgcn_raw_buffer_load_b128(wrr, wo[q], kc * 128, 0);
     }
   };
-  auto store_step = [&](int buf) {
+  auto store = [&](const Stage& S, int buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      reinterpret_cast<u32x4*>(&As[buf][ra * LDS_STRIDE + ha * 32])[q] = pa[q];
-      reinterpret_cast<u32x4*>(&Bs[buf][ra * LDS_STRIDE + ha * 32])[q] = pb[q];
+      *reinterpret_cast<u32x4*>(&As[buf][st_off + 32 * q * LDS_STRIDE]) = S.a[q];
+      *reinterpret_cast<u32x4*>(&Bs[buf][st_off + 32 * q * LDS_STRIDE]) = S.b[q];
     }
   };
   f16x_t acc[2][2];
@@ -680,25 +711,49 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const int a0 = (wv >> 1) * 64, b0 = (wv & 1) * 64;
   const int r32 = lane & 31, kh = (lane >> 5) * 8;
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-  for (int kc = 0; kc < nch; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nch) load_step(kc + 1);
+  // all 16 fragments of the step are read before the first MFMA: one LDS
+  // round trip per step instead of one per 16 K
+  auto compute = [&](int buf) {
+    b8_t fa[4][2], fb[4][2];
 #pragma unroll
-    for (int k16 = 0; k16 < BK; k16 += 16) {
-      const b8_t fa0 = lds_frag_b(As[buf], a0 + r32, k16 + kh);
-      const b8_t fa1 = lds_frag_b(As[buf], a0 + 32 + r32, k16 + kh);
-      const b8_t fb0 = lds_frag_b(Bs[buf], b0 + r32, k16 + kh);
-      const b8_t fb1 = lds_frag_b(Bs[buf], b0 + 32 + r32, k16 + kh);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0, fb1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1, fb1, acc[1][1], 0, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      fa[k][0] = lds_frag_b(As[buf], a0 + r32, 16 * k + kh);
+      fa[k][1] = lds_frag_b(As[buf], a0 + 32 + r32, 16 * k + kh);
+      fb[k][0] = lds_frag_b(Bs[buf], b0 + r32, 16 * k + kh);
+      fb[k][1] = lds_frag_b(Bs[buf], b0 + 32 + r32, 16 * k + kh);
     }
-    if (kc + 1 < nch) store_step(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k][i], fb[k][j], acc[i][j], 0, 0, 0);
+  };
+  Stage S[RDEPTH];
+#pragma unroll
+  for (int i = 0; i < RDEPTH; ++i) load(i, S[i]);
+  store(S[0], 0);
+  __syncthreads();
+  // step kc + J uses LDS buffer J % 2 and, for its successor, register set (J + 1) % RDEPTH
+  int kc = 0;
+  for (; kc + RDEPTH <= nch; kc += RDEPTH) {
+#pragma unroll
+    for (int J = 0; J < RDEPTH; ++J) {
+      store(S[(J + 1) % RDEPTH], (kc + J + 1) & 1);
+      load(kc + J + RDEPTH, S[J]);
+      compute((kc + J) & 1);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int J = 0; J < RDEPTH - 1; ++J) {
+    if (kc + J < nch) {
+      store(S[(J + 1) % RDEPTH], (kc + J + 1) & 1);
+      compute((kc + J) & 1);
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
@@ -714,8 +769,9 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const uint16_t* __restri
 
 hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s) {
-  dim3 grid((T + BM - 1) / BM, (E + BN - 1) / BN);
-  MOE_LAUNCH(k_router_mfma, grid, dim3(256), 0, s, x, T, wr, bias, E, H, logits);
+  if ((uint64_t)T * H * 2 > 0x7FFFFFFFu || (uint64_t)E * H * 2 > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  const int tiles = ((T + BM - 1) / BM) * ((E + BN - 1) / BN);
+  MOE_LAUNCH(k_router_mfma, dim3(tiles), dim3(256), 0, s, x, T, wr, bias, E, H, logits);
   return hipGetLastError();
 }
 

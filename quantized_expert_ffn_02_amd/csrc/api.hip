@@ -58,7 +58,7 @@ bool has_shared(const moe_layer_t* L) { return L->shared.fmt != MOE_FMT_NONE; }
 
 // Workspace layout of every call for a layer shape and up to T tokens.
 struct Layout {
-  size_t logits, ids, gates, margin;
+  size_t logits, rparts, ids, gates, margin;
   size_t counts, base, offsets, sorted_rows, row_to_sorted, items, n_items;
   size_t xtab_pairs, xtab_init, xf32, xf16, hf16, tiles, n_tiles;
   size_t h, htab_pairs, htab_init, y;
@@ -81,6 +81,8 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
     return at;
   };
   o.logits = take(T * E * 4);
+  const int rp = router_parts((int)T, (int)E, (int)H);
+  o.rparts = take(rp > 1 ? (size_t)rp * T * E * 4 : 0);   // K-split router partial planes
   o.ids = take(T * k * 4);
   o.gates = take(T * k * 4);
   o.margin = take(T * 4);
@@ -168,14 +170,22 @@ int mfma_min_rows(int T);
 int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float* gates, float* margin, void* ws,
              const Layout& lay, hipStream_t s) {
   float* logits = at<float>(ws, lay.logits);
+  // split-K router partial planes (16 < T < 1024)
+  const int parts = T > 16 && T < 1024 ? router_parts(T, L->n_experts, L->hidden) : 1;
+  float* rparts = at<float>(ws, lay.rparts);
   MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] {
     // prompt chunks: 128 x 128 MFMA tiles; verify batches: 32-token chunks with K
     // split over waves; a decode step: one wave per expert row
     if (T >= 1024) return launch_router_mfma(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
-    if (T > 16) return launch_router_split(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
+    if (T > 16)
+      return launch_router_split(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden,
+                                 parts > 1 ? rparts : logits, parts, s);
     return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
   }));
-  MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
+  if (parts > 1)
+    MOE_TRY(launch_topk(rparts, T, L->n_experts, L->top_k, ids, gates, margin, s, parts, L->router_bias));
+  else
+    MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
   return MOE_OK;
 }
 
@@ -377,12 +387,11 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
   int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
   if (rc) return rc;
-  MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
-                         at<int32_t>(ws, lay.base), s));
   int32_t* chunks = at<int32_t>(ws, lay.tiles);
   int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
-  MOE_TRY(launch_plan(offsets, E, 1, 1, chunks, n_chunks, at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items),
-                      s, kSmallTileRows));
+  MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                              at<int32_t>(ws, lay.base), 1, 1, kSmallTileRows, chunks, n_chunks,
+                              at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items), s));
   const int max_chunks = n / kSmallTileRows + std::min(E + 1, n) + 1;
   const bool q3 = routed.fmt == MOE_FMT_Q3;
   const MatRef r13 = mat_w13(routed), r2 = mat_w2(routed);
@@ -498,11 +507,11 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   } else {
     int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
     if (rc) return rc;
-    MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
-                           at<int32_t>(ws, lay.base), s));
     gemm = L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter);
-    MOE_TRY(launch_plan(offsets, E, gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T), at<int32_t>(ws, lay.tiles),
-                        at<int32_t>(ws, lay.n_tiles), items, n_items, s));
+    MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                                at<int32_t>(ws, lay.base), gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T),
+                                gemm_tile_rows(), at<int32_t>(ws, lay.tiles), at<int32_t>(ws, lay.n_tiles), items,
+                                n_items, s));
   }
   PermRef perm;
   perm.offsets = offsets;
@@ -630,10 +639,9 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   } else {
     rc = do_route(L, x, T, ids, gates, nullptr, ws, lay, s);
     if (rc) return rc;
-    MOE_TRY(launch_permute(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
-                           at<int32_t>(ws, lay.base), s));
-    MOE_TRY(launch_plan(offsets, E, 0x7FFFFFFF, items_per_for(T), at<int32_t>(ws, lay.tiles),
-                        at<int32_t>(ws, lay.n_tiles), items, n_items, s));
+    MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
+                                at<int32_t>(ws, lay.base), 0x7FFFFFFF, items_per_for(T), gemm_tile_rows(),
+                                at<int32_t>(ws, lay.tiles), at<int32_t>(ws, lay.n_tiles), items, n_items, s));
   }
   PermRef perm;
   perm.offsets = offsets;

@@ -143,14 +143,22 @@ hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, cons
 hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s);
 // router logits + activation table only (the first launch of launch_route_small)
 hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s);
+// parts > 1: ``logits`` holds ``parts`` partial planes [T][E] to be added in
+// plane order, then ``bias`` (launch_router_split with parts > 1)
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
-                       hipStream_t s);
+                       hipStream_t s, int parts = 1, const float* bias = nullptr);
 
 // permutation: counts/base are [n_chunks][E + 2] int32 scratch
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
                           int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
                           hipStream_t s);
 int permute_chunks(int n_entries);
+// permutation followed by the plan (launch_plan); batches of up to 16,384 entries
+// in one single-block launch
+hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
+                               int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
+                               int min_rows, int items_per, int tile_rows, int32_t* tiles, int32_t* n_tiles,
+                               int32_t* items, int32_t* n_items, hipStream_t s);
 // work items of a permutation (see PermRef), from its offsets
 hipError_t launch_items_from_offsets(const int32_t* offsets, int E, int items_per, int32_t* items,
                                      int32_t* n_items, hipStream_t s);
@@ -181,9 +189,12 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           const int32_t* slot_map = nullptr);
 // rows per tile of the grouped GEMM for batches beyond a decode step and below a prompt chunk
 static constexpr int kSmallTileRows = 32;
-// router of such batches (router_split.hip): 32 tokens x 64 experts per block, K split over waves
+// router of such batches (router_split.hip): 32 tokens x 64 experts per unit, K split over
+// ``parts`` blocks (router_parts) and over the 4 waves of each; parts == 1 writes logits (with
+// the bias), parts > 1 writes partial planes [parts][T][E] (without it) for launch_topk
+int router_parts(int T, int E, int H);
 hipError_t launch_router_split(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
-                               float* logits, hipStream_t s);
+                               float* out, int parts, hipStream_t s);
 // out[t] = sum over the token's entries of the gate-scaled fp16 rows y16 (rank
 // order, then the shared expert) (+ residual), fp32, optional bf16 copy
 hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,

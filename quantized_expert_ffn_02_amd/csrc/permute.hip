@@ -137,6 +137,124 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shar
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Permutation and plan of a batch of up to kPermSmallMax entries in ONE block
+// of 16 waves (the four launches above cost more than the work at these
+// sizes).  Wave w owns the contiguous entries [w P, (w + 1) P): per-wave
+// group counts in LDS, a block scan gives the offsets and then each wave's
+// base per group (waves in order), and every wave scatters its own entries in
+// ascending r, 64 at a time, ranking equal groups inside a batch with ballots
+// over the group bits -- the same stable order as the multi-block path.  The
+// plan (tiles of groups with at least min_rows entries, work items of the
+// rest) follows from the offsets, as k_plan computes it.
+// ---------------------------------------------------------------------------
+static constexpr int kPermSmallMax = 16384;
+
+__global__ __launch_bounds__(1024) void k_perm_plan_small(const int32_t* __restrict__ ids, int Tk, int n, int E,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_rows,
+                                                          int32_t* __restrict__ row_to_sorted, int min_rows,
+                                                          int items_per, int tile_rows, int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ n_tiles, int32_t* __restrict__ items,
+                                                          int32_t* __restrict__ n_items) {
+  __shared__ int hw[16][1024];
+  __shared__ int s_off[1025];
+  const int G = E + 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < 16 * 1024; i += 1024) (&hw[0][0])[i] = 0;
+  __syncthreads();
+  const int per = (n + 15) / 16;
+  const int r0 = min(n, w * per), r1 = min(n, r0 + per);
+  for (int r = r0 + lane; r < r1; r += 64) {
+    const int g = group_of(ids, r, Tk, E);
+    if ((unsigned)g <= (unsigned)E) atomicAdd(&hw[w][g], 1);   // out-of-range ids are dropped
+  }
+  __syncthreads();
+  int tot = 0;
+  if (tid < G)
+    for (int i = 0; i < 16; ++i) tot += hw[i][tid];
+  int n_all = 0;
+  const int off = block_exclusive_scan_1024(tid < G ? tot : 0, &n_all);
+  if (tid < G) {
+    offsets[tid] = off;
+    s_off[tid] = off;
+    int run = off;
+    for (int i = 0; i < 16; ++i) {
+      const int c = hw[i][tid];
+      hw[i][tid] = run;
+      run += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[G] = n_all;
+    s_off[G] = n_all;
+  }
+  __syncthreads();
+  // per-wave scatter (no block barrier inside: the waves' ranges differ in
+  // length; a wave's LDS reads of hw[w][g] precede its own update in order)
+  for (int b = r0; b < r1; b += 64) {
+    const int r = b + lane;
+    int g = r < r1 ? group_of(ids, r, Tk, E) : 0;
+    const bool valid = r < r1 && (unsigned)g <= (unsigned)E;
+    if (!valid) g = 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const bool on = (g >> bit) & 1;
+      const uint64_t m = __ballot(on);
+      peers &= on ? m : ~m;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(peers & below);
+    const int prior = valid ? hw[w][g] : 0;
+    if (valid) {
+      const int pos = prior + rank;
+      sorted_rows[pos] = r;
+      row_to_sorted[r] = pos;
+      if ((peers >> lane) == 1ull) hw[w][g] = prior + __popcll(peers);   // the group's highest lane
+    }
+  }
+  __syncthreads();
+  const int start = tid < G ? s_off[tid] : 0;
+  const int cnt = tid < G ? s_off[tid + 1] - start : 0;
+  const bool big = cnt >= min_rows;
+  const int nt = big ? (cnt + tile_rows - 1) / tile_rows : 0;
+  const int ni = big ? 0 : (cnt + items_per - 1) / items_per;
+  int tot_t = 0, tot_i = 0;
+  const int pt = block_exclusive_scan_1024(nt, &tot_t);
+  const int pi = block_exclusive_scan_1024(ni, &tot_i);
+  for (int i = 0; i < nt; ++i) {
+    tiles[3 * (pt + i)] = tid;
+    tiles[3 * (pt + i) + 1] = start + i * tile_rows;
+    tiles[3 * (pt + i) + 2] = min(tile_rows, cnt - i * tile_rows);
+  }
+  for (int i = 0; i < ni; ++i) {
+    items[3 * (pi + i)] = tid;
+    items[3 * (pi + i) + 1] = start + i * items_per;
+    items[3 * (pi + i) + 2] = min(items_per, cnt - i * items_per);
+  }
+  if (tid == 0) {
+    *n_tiles = tot_t;
+    *n_items = tot_i;
+  }
+}
+
+hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
+                               int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
+                               int min_rows, int items_per, int tile_rows, int32_t* tiles, int32_t* n_tiles,
+                               int32_t* items, int32_t* n_items, hipStream_t s) {
+  const int Tk = T * k;
+  const int n = Tk + (with_shared ? T : 0);
+  if (n <= kPermSmallMax && E + 1 <= 1024) {
+    MOE_LAUNCH(k_perm_plan_small, dim3(1), dim3(1024), 0, s, ids, Tk, n, E, offsets, sorted_rows, row_to_sorted,
+               min_rows, items_per, tile_rows, tiles, n_tiles, items, n_items);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_permute(ids, T, k, E, with_shared, offsets, sorted_rows, row_to_sorted, counts, base, s);
+  if (e != hipSuccess) return e;
+  return launch_plan(offsets, E, min_rows, items_per, tiles, n_tiles, items, n_items, s, tile_rows);
+}
+
 // Work items from offsets: group g yields ceil(count / items_per) items, placed
 // after the items of every lower group.
 __global__ __launch_bounds__(1024) void k_items_from_offsets(const int32_t* __restrict__ offsets, int E,

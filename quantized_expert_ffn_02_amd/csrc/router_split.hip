@@ -2,14 +2,15 @@
 // (16 < T < 1,024 tokens: an MTP verify batch of many sequences).
 //
 // logits[t, e] = x_t . Wr[e] (+ b[e]): bf16 operands, exact products, fp32
-// accumulation (v_mfma_f32_32x32x16_bf16).  At these sizes the 128 x 128 tile
-// kernel has a handful of blocks that each walk K = 2,560 serially, bound by
-// memory latency.  Here a block takes 32 tokens x 64 experts and its W waves
-// split K: wave w owns K steps [w UPW, (w + 1) UPW) of 64, loads its A (x) and B
-// (router rows) fragments straight into registers two steps ahead of use, and
-// runs 2 MFMAs per 16 K; the W partial tiles are summed in LDS in wave order
-// (deterministic) and written with the bias.  Blocks walk the (token chunk,
-// expert tile) space grid-stride, expert tile fastest.
+// accumulation (v_mfma_f32_32x32x16_bf16).  A unit is 32 tokens x 64 experts;
+// at these sizes there are only (T / 32) x (E / 64) units, so K is also split
+// over KS blocks (router_parts) to put a block on every compute unit.  Block
+// (unit, ks) covers K range ks of KS; its 4 waves each take a quarter of that
+// range, load all their A (x) and B (router rows) fragments at once, run 2
+// MFMAs per 16 K, and the 4 partial tiles are summed in LDS in wave order.
+// With KS = 1 the block adds the bias and writes the logits; otherwise it
+// writes its partial sum to parts[ks] and the top-k kernel adds the KS parts
+// in ks order and then the bias (route.hip), so the result is deterministic.
 #include <math.h>
 
 #include "device.h"
@@ -22,120 +23,107 @@ struct RouterArgs {
   const uint16_t* x;     // bf16 [T][H]
   const uint16_t* wr;    // bf16 [E][H]
   const float* bias;     // fp32 [E] or NULL
-  float* logits;         // fp32 [T][E]
-  int T, E, H;
+  float* out;            // KS = 1: logits [T][E]; else parts [KS][T][E]
+  int T, E, H, KS;
 };
 
-template <int W, int UPW>
-__global__ __launch_bounds__(W * 64) void k_router_split(RouterArgs a) {
-  __shared__ float red[W][16][64];
+// A wave's K range is REPS x NK 16-K fragments; each group of NK is loaded at
+// once and then multiplied.
+template <int NK>
+__global__ __launch_bounds__(256) void k_router_split(RouterArgs a, int reps) {
+  __shared__ float red[4][2][16][64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = a.H, nch = K / 64;
+  const int K = a.H;
   const int ncol = (a.E + 63) / 64;
-  const int units = ((a.T + 31) / 32) * ncol;
+  const int unit = blockIdx.x / a.KS, ks = blockIdx.x - unit * a.KS;
+  const int chunk = unit / ncol, j = unit - chunk * ncol;
+  const int m0 = chunk * 32, rows = min(32, a.T - m0);
   const int r32 = lane & 31, kh = (lane >> 5) * 8;
-
-  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int chunk = unit / ncol, j = unit - chunk * ncol;
-    const int m0 = chunk * 32, rows = min(32, a.T - m0);
-    // token of this lane's A rows (rows past the chunk repeat its first token)
-    const int rr = r32 < rows ? r32 : 0;
-    const u32x4* __restrict__ ap = reinterpret_cast<const u32x4*>(a.x + (size_t)(m0 + rr) * K + kh);
-    const int e0 = 64 * j + r32, e1 = e0 + 32;
-    const u32x4* __restrict__ w0 = reinterpret_cast<const u32x4*>(a.wr + (size_t)min(e0, a.E - 1) * K + kh);
-    const u32x4* __restrict__ w1 = reinterpret_cast<const u32x4*>(a.wr + (size_t)min(e1, a.E - 1) * K + kh);
-
-    f16x_t acc0, acc1;
+  // this wave's K range: [k0, k0 + 16 NK reps)
+  const int k0 = (ks * 4 + wv) * 16 * NK * reps;
+  const int rr = r32 < rows ? r32 : 0;   // rows past the chunk repeat its first token
+  const u32x4* __restrict__ ap = reinterpret_cast<const u32x4*>(a.x + (size_t)(m0 + rr) * K + k0 + kh);
+  const int e0 = 64 * j + r32, e1 = e0 + 32;
+  const u32x4* __restrict__ w0 = reinterpret_cast<const u32x4*>(a.wr + (size_t)min(e0, a.E - 1) * K + k0 + kh);
+  const u32x4* __restrict__ w1 = reinterpret_cast<const u32x4*>(a.wr + (size_t)min(e1, a.E - 1) * K + k0 + kh);
+  f16x_t acc0, acc1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
-
-    // registers of the wave's UPW steps; loads issued two steps ahead of use
-    u32x4 A[UPW][4], B[UPW][8];
-    auto issue = [&](int u) {
-      const int step = min(wv * UPW + u, nch - 1);   // past the end: reload the last step, result unused
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
+  for (int g = 0; g < reps; ++g) {
+    u32x4 A[NK], B0[NK], B1[NK];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        A[u][s] = ap[step * 8 + 2 * s];
-        B[u][s] = w0[step * 8 + 2 * s];
-        B[u][4 + s] = w1[step * 8 + 2 * s];
-      }
-    };
-    auto compute = [&](int u) {
-      if (wv * UPW + u >= nch) return;   // wave-uniform
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const b8_t fa = __builtin_bit_cast(b8_t, A[u][s]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(b8_t, B[u][s]), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(b8_t, B[u][4 + s]), acc1, 0, 0, 0);
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < UPW + 2; ++u) {
-      if (u < UPW) issue(u);
-      __builtin_amdgcn_sched_barrier(0);
-      if (u >= 2) compute(u - 2);
-    }
-
-    // fixed-order reduction over the waves, one fragment at a time
-    constexpr int PER = (1024 + W * 64 - 1) / (W * 64);   // outputs per thread
-    float v0[PER], v1[PER];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[wv][r][lane] = f ? acc1[r] : acc0[r];
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const int e = threadIdx.x + q * W * 64;
-        float sum = 0.0f;
-        if (e < 1024)
-          for (int w = 0; w < W; ++w) sum += red[w][e >> 6][e & 63];
-        if (f)
-          v1[q] = sum;
-        else
-          v0[q] = sum;
-      }
-      __syncthreads();
+    for (int u = 0; u < NK; ++u) {
+      A[u] = ap[2 * (g * NK + u)];
+      B0[u] = w0[2 * (g * NK + u)];
+      B1[u] = w1[2 * (g * NK + u)];
     }
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int e = threadIdx.x + q * W * 64;
-      if (e >= 1024) continue;
-      const int r = e >> 6, l = e & 63;
-      const int row = acc_row(r, l), col = l & 31;
-      if (row >= rows) continue;
-      const int c0 = 64 * j + col, c1 = c0 + 32;
-      float* lr = a.logits + (size_t)(m0 + row) * a.E;
-      if (c0 < a.E) lr[c0] = v0[q] + (a.bias ? a.bias[c0] : 0.0f);
-      if (c1 < a.E) lr[c1] = v1[q] + (a.bias ? a.bias[c1] : 0.0f);
+    for (int u = 0; u < NK; ++u) {
+      const b8_t fa = __builtin_bit_cast(b8_t, A[u]);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(b8_t, B0[u]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(b8_t, B1[u]), acc1, 0, 0, 0);
     }
-    __syncthreads();   // red is reused by the next unit
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    red[wv][0][r][lane] = acc0[r];
+    red[wv][1][r][lane] = acc1[r];
+  }
+  __syncthreads();
+  // 2 x 16 x 64 outputs over 256 threads: 8 each, summed over the waves in order
+  const size_t plane = (size_t)a.T * a.E;
+  float* __restrict__ dst = a.out + (a.KS > 1 ? (size_t)ks * plane : 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int o = q * 256 + (int)threadIdx.x;   // o = f * 1024 + r * 64 + l
+    const int f = o >> 10, r = (o >> 6) & 15, l = o & 63;
+    const float sum = ((red[0][f][r][l] + red[1][f][r][l]) + red[2][f][r][l]) + red[3][f][r][l];
+    const int row = acc_row(r, l), col = 64 * j + 32 * f + (l & 31);
+    if (row < rows && col < a.E)
+      dst[(size_t)(m0 + row) * a.E + col] = a.KS > 1 ? sum : sum + (a.bias ? a.bias[col] : 0.0f);
   }
 }
 
+// K-split factor of the router for T tokens: enough blocks to cover the
+// compute units, with every wave's quarter of a block's K a whole number of
+// 16-K fragments (at most 8 parts).
+int router_parts(int T, int E, int H) {
+  if (T <= 16 || T >= 1024) return 1;
+  const int units = ((T + 31) / 32) * ((E + 63) / 64);
+  int ks = 1;
+  while (ks < 8 && units * ks < 256 && (H / 16) % (8 * ks) == 0) ks *= 2;
+  return ks;
+}
+
 hipError_t launch_router_split(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
-                               float* logits, hipStream_t s) {
+                               float* out, int parts, hipStream_t s) {
   RouterArgs a;
   a.x = x;
   a.wr = wr;
   a.bias = bias;
-  a.logits = logits;
+  a.out = out;
   a.T = T;
   a.E = E;
   a.H = H;
+  a.KS = parts;
   const int units = ((T + 31) / 32) * ((E + 63) / 64);
   if (units <= 0) return hipSuccess;
-  constexpr int W = 8;
-  const int nch = H / 64;
-  if (nch <= 2 * W)
-    MOE_LAUNCH((k_router_split<W, 2>), dim3(units), dim3(W * 64), 0, s, a);
-  else if (nch <= 5 * W)
-    MOE_LAUNCH((k_router_split<W, 5>), dim3(units), dim3(W * 64), 0, s, a);
-  else if (nch <= 8 * W)
-    MOE_LAUNCH((k_router_split<W, 8>), dim3(units), dim3(W * 64), 0, s, a);
+  if (parts < 1 || (H / 16) % (4 * parts)) return hipErrorInvalidValue;
+  const int nkw = H / 16 / (4 * parts);   // 16-K fragments per wave
+  dim3 grid(units * parts);
+  if (nkw % 10 == 0)
+    MOE_LAUNCH(k_router_split<10>, grid, dim3(256), 0, s, a, nkw / 10);
+  else if (nkw % 8 == 0)
+    MOE_LAUNCH(k_router_split<8>, grid, dim3(256), 0, s, a, nkw / 8);
+  else if (nkw % 5 == 0)
+    MOE_LAUNCH(k_router_split<5>, grid, dim3(256), 0, s, a, nkw / 5);
+  else if (nkw % 4 == 0)
+    MOE_LAUNCH(k_router_split<4>, grid, dim3(256), 0, s, a, nkw / 4);
+  else if (nkw % 2 == 0)
+    MOE_LAUNCH(k_router_split<2>, grid, dim3(256), 0, s, a, nkw / 2);
   else
-    return hipErrorInvalidValue;
+    MOE_LAUNCH(k_router_split<1>, grid, dim3(256), 0, s, a, nkw);
   return hipGetLastError();
 }
 

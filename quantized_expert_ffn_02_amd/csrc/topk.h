@@ -58,13 +58,29 @@ struct TopkKeys {
   uint64_t mine, last, next;
 };
 
-template <int VPL>
-__device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k) {
+// PARTS: the logits are the sum of np partial planes pstride floats apart
+// (added in plane order) plus bias (if not NULL), as a K-split router leaves them.
+template <int VPL, bool PARTS = false>
+__device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k, int np = 1, size_t pstride = 0,
+                                   const float* __restrict__ bias = nullptr) {
   const int lane = threadIdx.x & 63;
   // all VPL loads in flight at once (clamped index, no branch around a load)
   float v[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
+  if constexpr (PARTS) {
+    for (int p = 1; p < np; ++p) {
+      float w[VPL];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) w[j] = row[p * pstride + min(lane + 64 * j, E - 1)];
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) v[j] += w[j];
+    }
+    if (bias) {
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) v[j] += bias[min(lane + 64 * j, E - 1)];
+    }
+  }
   uint64_t key[VPL];
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
@@ -127,11 +143,12 @@ __device__ __forceinline__ void topk_write(const TopkKeys& r, int E, int k, int3
 }
 
 // Top-k of one token: logits row [E] -> ids[k], gates[k], margin.
-template <int VPL>
+template <int VPL, bool PARTS = false>
 __device__ void wave_topk_row(const float* __restrict__ row, int E, int k, int32_t* __restrict__ ids_out,
                               float* __restrict__ gates_out, float* __restrict__ margin_out,
-                              int32_t* __restrict__ ids_lds = nullptr) {
-  const TopkKeys r = wave_topk_keys<VPL>(row, E, k);
+                              int32_t* __restrict__ ids_lds = nullptr, int np = 1, size_t pstride = 0,
+                              const float* __restrict__ bias = nullptr) {
+  const TopkKeys r = wave_topk_keys<VPL, PARTS>(row, E, k, np, pstride, bias);
   topk_write(r, E, k, ids_out, gates_out, margin_out, ids_lds);
 }
 

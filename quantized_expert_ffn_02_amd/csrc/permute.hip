@@ -61,25 +61,77 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return base + incl - v;
 }
 
-// One block of 1024 threads, thread g = group: totals, offsets and per-chunk bases.
+// One block of 1024 threads, thread g = group: totals, offsets and per-chunk
+// bases.  A group's per-chunk counts are read kScanBatch at a time (indices
+// clamped, extra values dropped), so a thread waits for one memory round trip
+// per batch rather than per chunk.
+static constexpr int kScanBatch = 16;
+
+struct PlanOut {
+  int min_rows = 0, items_per = 1, tile_rows = 1;
+  int32_t *tiles = nullptr, *n_tiles = nullptr, *items = nullptr, *n_items = nullptr;
+};
+
+// Plan of the groups (as k_plan computes it) from thread g's group start and
+// count; every thread of the block calls it.
+__device__ void plan_groups(const PlanOut& P, int g, int start, int cnt) {
+  const bool big = cnt >= P.min_rows;
+  const int nt = big ? (cnt + P.tile_rows - 1) / P.tile_rows : 0;
+  const int ni = big ? 0 : (cnt + P.items_per - 1) / P.items_per;
+  int tot_t = 0, tot_i = 0;
+  const int pt = block_exclusive_scan_1024(nt, &tot_t);
+  const int pi = block_exclusive_scan_1024(ni, &tot_i);
+  for (int i = 0; i < nt; ++i) {
+    P.tiles[3 * (pt + i)] = g;
+    P.tiles[3 * (pt + i) + 1] = start + i * P.tile_rows;
+    P.tiles[3 * (pt + i) + 2] = min(P.tile_rows, cnt - i * P.tile_rows);
+  }
+  for (int i = 0; i < ni; ++i) {
+    P.items[3 * (pi + i)] = g;
+    P.items[3 * (pi + i) + 1] = start + i * P.items_per;
+    P.items[3 * (pi + i) + 2] = min(P.items_per, cnt - i * P.items_per);
+  }
+  if (g == 0) {
+    *P.n_tiles = tot_t;
+    *P.n_items = tot_i;
+  }
+}
+
+// P.tiles != NULL: the plan is made here too (the offsets are this block's).
 __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ counts, int n_chunks, int E,
-                                                    int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
+                                                    int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+                                                    PlanOut P) {
   const int G = E + 1;
   const int g = threadIdx.x;
+  const int gg = g < G ? g : 0;
   int tot = 0;
-  if (g < G)
-    for (int c = 0; c < n_chunks; ++c) tot += counts[(size_t)c * G + g];
+  for (int c0 = 0; c0 < n_chunks; c0 += kScanBatch) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) v[j] = counts[(size_t)min(c0 + j, n_chunks - 1) * G + gg];
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) tot += c0 + j < n_chunks ? v[j] : 0;
+  }
   int n_all = 0;
   const int off = block_exclusive_scan_1024(g < G ? tot : 0, &n_all);
   if (g < G) {
     offsets[g] = off;
     int run = off;
-    for (int c = 0; c < n_chunks; ++c) {
-      base[(size_t)c * G + g] = run;
-      run += counts[(size_t)c * G + g];
+    for (int c0 = 0; c0 < n_chunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = counts[(size_t)min(c0 + j, n_chunks - 1) * G + g];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (c0 + j < n_chunks) {
+          base[(size_t)(c0 + j) * G + g] = run;
+          run += v[j];
+        }
+      }
     }
   }
   if (g == 0) offsets[G] = n_all;
+  if (P.tiles) plan_groups(P, g, g < G ? off : 0, g < G ? tot : 0);
 }
 
 // One wave per chunk: entries in ascending r, 64 at a time; the rank of an
@@ -125,16 +177,22 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
   }
 }
 
-hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
-                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
-                          hipStream_t s) {
+static hipError_t permute_multi(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
+                                int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
+                                const PlanOut& plan, hipStream_t s) {
   const int Tk = T * k;
   const int n = Tk + (with_shared ? T : 0);
   const int nc = permute_chunks(n);
   MOE_LAUNCH(k_perm_hist, dim3(nc), dim3(256), 0, s, ids, Tk, n, E, counts);
-  MOE_LAUNCH(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets);
+  MOE_LAUNCH(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets, plan);
   MOE_LAUNCH(k_perm_scatter, dim3(nc), dim3(64), 0, s, ids, Tk, n, E, base, sorted_rows, row_to_sorted);
   return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
+                          int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
+                          hipStream_t s) {
+  return permute_multi(ids, T, k, E, with_shared, offsets, sorted_rows, row_to_sorted, counts, base, PlanOut(), s);
 }
 
 // ---------------------------------------------------------------------------
@@ -215,28 +273,16 @@ __global__ __launch_bounds__(1024) void k_perm_plan_small(const int32_t* __restr
     }
   }
   __syncthreads();
+  PlanOut P;
+  P.min_rows = min_rows;
+  P.items_per = items_per;
+  P.tile_rows = tile_rows;
+  P.tiles = tiles;
+  P.n_tiles = n_tiles;
+  P.items = items;
+  P.n_items = n_items;
   const int start = tid < G ? s_off[tid] : 0;
-  const int cnt = tid < G ? s_off[tid + 1] - start : 0;
-  const bool big = cnt >= min_rows;
-  const int nt = big ? (cnt + tile_rows - 1) / tile_rows : 0;
-  const int ni = big ? 0 : (cnt + items_per - 1) / items_per;
-  int tot_t = 0, tot_i = 0;
-  const int pt = block_exclusive_scan_1024(nt, &tot_t);
-  const int pi = block_exclusive_scan_1024(ni, &tot_i);
-  for (int i = 0; i < nt; ++i) {
-    tiles[3 * (pt + i)] = tid;
-    tiles[3 * (pt + i) + 1] = start + i * tile_rows;
-    tiles[3 * (pt + i) + 2] = min(tile_rows, cnt - i * tile_rows);
-  }
-  for (int i = 0; i < ni; ++i) {
-    items[3 * (pi + i)] = tid;
-    items[3 * (pi + i) + 1] = start + i * items_per;
-    items[3 * (pi + i) + 2] = min(items_per, cnt - i * items_per);
-  }
-  if (tid == 0) {
-    *n_tiles = tot_t;
-    *n_items = tot_i;
-  }
+  plan_groups(P, tid, start, tid < G ? s_off[tid + 1] - start : 0);
 }
 
 hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
@@ -250,9 +296,15 @@ hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with
                min_rows, items_per, tile_rows, tiles, n_tiles, items, n_items);
     return hipGetLastError();
   }
-  hipError_t e = launch_permute(ids, T, k, E, with_shared, offsets, sorted_rows, row_to_sorted, counts, base, s);
-  if (e != hipSuccess) return e;
-  return launch_plan(offsets, E, min_rows, items_per, tiles, n_tiles, items, n_items, s, tile_rows);
+  PlanOut P;
+  P.min_rows = min_rows;
+  P.items_per = items_per;
+  P.tile_rows = tile_rows;
+  P.tiles = tiles;
+  P.n_tiles = n_tiles;
+  P.items = items;
+  P.n_items = n_items;
+  return permute_multi(ids, T, k, E, with_shared, offsets, sorted_rows, row_to_sorted, counts, base, P, s);
 }
 
 // Work items from offsets: group g yields ceil(count / items_per) items, placed

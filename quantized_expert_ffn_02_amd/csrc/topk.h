@@ -58,8 +58,9 @@ struct TopkKeys {
   uint64_t mine, last, next;
 };
 
-// PARTS: the logits are the sum of np partial planes pstride floats apart
-// (added in plane order) plus bias (if not NULL), as a K-split router leaves them.
+// PARTS: the logits are the sum of np (<= 8) partial planes pstride floats
+// apart (added in plane order) plus bias (if not NULL), as a K-split router
+// leaves them.
 template <int VPL, bool PARTS = false>
 __device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k, int np = 1, size_t pstride = 0,
                                    const float* __restrict__ bias = nullptr) {
@@ -69,16 +70,24 @@ __device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k, 
 #pragma unroll
   for (int j = 0; j < VPL; ++j) v[j] = row[min(lane + 64 * j, E - 1)];
   if constexpr (PARTS) {
-    for (int p = 1; p < np; ++p) {
-      float w[VPL];
+    // planes 1 .. np - 1 (np <= 8), every load issued before the first add
+    // (plane index clamped; clamped planes are not added)
+    float w[7][VPL], bv[VPL];
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) w[j] = row[p * pstride + min(lane + 64 * j, E - 1)];
+    for (int p = 1; p < 8; ++p)
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) v[j] += w[j];
-    }
+      for (int j = 0; j < VPL; ++j) w[p - 1][j] = row[(size_t)min(p, np - 1) * pstride + min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) bv[j] = bias ? bias[min(lane + 64 * j, E - 1)] : 0.0f;
+#pragma unroll
+    for (int p = 1; p < 8; ++p)
+      if (p < np) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) v[j] += w[p - 1][j];
+      }
     if (bias) {
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) v[j] += bias[min(lane + 64 * j, E - 1)];
+      for (int j = 0; j < VPL; ++j) v[j] += bv[j];
     }
   }
   uint64_t key[VPL];

@@ -106,6 +106,41 @@ __device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const
   const int r = lane & 31, kh = (lane >> 5) * 8;
   const uint32_t cw0[4] = {R.c0.x, R.c0.y, R.c0.z, R.c0.w};
   const uint32_t cw1[4] = {R.c1.x, R.c1.y, R.c1.z, R.c1.w};
+  if constexpr (TR && !Q3) {
+    // Software pipeline over the 4 sub-steps: the dequant of sub-step s + 1
+    // is scheduled in slices between the MFMAs of sub-step s (scheduling
+    // groups: the A reads, then per MFMA a few VALU instructions), so the
+    // matrix core and the VALU work side by side within the wave.
+    h8_t c0 = b_frag(cw0[0] >> shift, scale_pair(R.s0, false), bc);
+    h8_t c1 = b_frag(cw1[0] >> shift, scale_pair(R.s1, false), bc);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8_t a[NMI];
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) a[mi] = *reinterpret_cast<const h8_t*>(As + (mi * 32 + r) * A_STRIDE + s * 16 + kh);
+      h8_t n0 = c0, n1 = c1;
+      if (s < 3) {
+        n0 = b_frag(cw0[s + 1] >> shift, scale_pair(R.s0, s + 1 >= 2), bc);
+        n1 = b_frag(cw1[s + 1] >> shift, scale_pair(R.s1, s + 1 >= 2), bc);
+      }
+#pragma unroll
+      for (int mi = 0; mi < NMI; ++mi) {
+        acc[mi][0] = mfma_op<TR>(a[mi], c0, acc[mi][0]);
+        acc[mi][1] = mfma_op<TR>(a[mi], c1, acc[mi][1]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, NMI, 0);   // LDS reads
+#pragma unroll
+      for (int j = 0; j < 2 * NMI; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x002, (28 + 2 * NMI - 1) / (2 * NMI), 0);   // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      c0 = n0;
+      c1 = n1;
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const h2_t s20 = scale_pair(R.s0, s >= 2), s21 = scale_pair(R.s1, s >= 2);

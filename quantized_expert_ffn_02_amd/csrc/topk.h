@@ -3,10 +3,11 @@
 // Order: logit descending, expert index ascending (so exactly equal logits go to
 // the lower index).  Each lane holds VPL logits (experts lane + 64 j), sorted once
 // per lane; then k + 1 rounds of a wave arg-max over the lanes' heads pick the
-// experts in order and the (k+1)-th logit for the margin.  The arg-max compares
-// one 64-bit key per lane with DPP moves (four steps inside each 16-lane row, two
-// row broadcasts across rows) and reads the winner from lane 63, instead of
-// LDS-routed shuffles.
+// experts in order and the (k+1)-th logit for the margin.  The arg-max takes the
+// 32-bit maximum of the heads' logit words with DPP moves (four steps inside
+// each 16-lane row, two row broadcasts across rows, the result read from lane
+// 63) and a ballot for its holder; only equal logits need a second maximum, over
+// the index words.
 #pragma once
 
 #include <math.h>
@@ -29,27 +30,24 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 }
 __device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
 
+// Lanes without a source (or in rows outside ROW_MASK) read 0, the identity of
+// an unsigned maximum, which lets the compiler fold the move into v_max_u32's
+// DPP form.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_step(uint64_t key) {
-  const int lo = (int)(uint32_t)key, hi = (int)(uint32_t)(key >> 32);
-  // rows outside ROW_MASK and lanes without a source keep their own key
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > key ? o : key;
+__device__ __forceinline__ uint32_t dpp_max_u32_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+  return o > v ? o : v;
 }
 
-// Wave-uniform maximum key over the 64 lanes.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
-  key = dpp_max_step<0xB1, 0xF>(key);    // quad_perm [1,0,3,2]
-  key = dpp_max_step<0x4E, 0xF>(key);    // quad_perm [2,3,0,1]
-  key = dpp_max_step<0x124, 0xF>(key);   // row_ror:4
-  key = dpp_max_step<0x128, 0xF>(key);   // row_ror:8  -> every lane holds its row's max
-  key = dpp_max_step<0x142, 0xA>(key);   // row_bcast:15 -> rows 1, 3 include rows 0, 2
-  key = dpp_max_step<0x143, 0xC>(key);   // row_bcast:31 -> rows 2, 3 include row 1 (lane 63 = all)
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+// Wave-uniform maximum of one 32-bit value per lane (the same DPP steps).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_u32_step<0xB1, 0xF>(v);
+  v = dpp_max_u32_step<0x4E, 0xF>(v);
+  v = dpp_max_u32_step<0x124, 0xF>(v);
+  v = dpp_max_u32_step<0x128, 0xF>(v);
+  v = dpp_max_u32_step<0x142, 0xA>(v);
+  v = dpp_max_u32_step<0x143, 0xC>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Keys of one token's top-k: lane r (< k) holds the key of rank r in ``mine``;
@@ -106,18 +104,38 @@ __device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k, 
         key[b] = key[b - 1];
         key[b - 1] = t;
       }
+  // Each round: the wave maximum of the heads' logit words; a single holder
+  // (the usual case) gives the key directly, equal logits fall back to the
+  // maximum of their index words (the lowest expert index).
+  uint32_t khi[VPL], klo[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    khi[j] = (uint32_t)(key[j] >> 32);
+    klo[j] = (uint32_t)key[j];
+  }
   TopkKeys r;
   r.mine = r.last = r.next = 0;
   const int rounds = k < E ? k + 1 : k;
   for (int q = 0; q < rounds; ++q) {
-    const uint64_t best = wave_max_key(key[0]);
+    const uint32_t mh = wave_max_u32(khi[0]);
+    const uint64_t tied = __ballot(khi[0] == mh);
+    uint32_t ml;
+    if (__popcll(tied) == 1)
+      ml = (uint32_t)__builtin_amdgcn_readlane((int)klo[0], (int)__builtin_ctzll(tied));
+    else
+      ml = wave_max_u32(khi[0] == mh ? klo[0] : 0u);
+    const uint64_t best = ((uint64_t)mh << 32) | ml;
     if (q < k) {
       if (lane == q) r.mine = best;
       r.last = best;
-      if (key[0] == best) {   // the lane holding it pops its head
+      if (khi[0] == mh && klo[0] == ml) {   // the lane holding it pops its head
 #pragma unroll
-        for (int j = 0; j + 1 < VPL; ++j) key[j] = key[j + 1];
-        key[VPL - 1] = 0ull;
+        for (int j = 0; j + 1 < VPL; ++j) {
+          khi[j] = khi[j + 1];
+          klo[j] = klo[j + 1];
+        }
+        khi[VPL - 1] = 0u;
+        klo[VPL - 1] = 0u;
       }
     } else {
       r.next = best;

@@ -4,9 +4,9 @@
 // on a 12GB Gaming GPU", section "How a 125B model fits in 12 GB") in two
 // launches.
 //
-// k_route_front: every block computes the logits of 4 experts (one wave per
-// bf16 router row, the row's and the tokens' 16-byte chunks all loaded before
-// any arithmetic) and a slice of the activation pair table.
+// k_route_front: the first blocks compute the logits of 4 experts each (one
+// wave per bf16 router row, the row's and the tokens' 16-byte chunks all loaded
+// before any arithmetic); the remaining blocks build the activation pair table.
 // k_route_select: one block runs top-k for every token (a wave per token) and a
 // stable counting sort of the T*k (+T shared) entries into offsets, sorted rows,
 // the inverse map and the GEMV work items.  (A single fused launch with a
@@ -90,21 +90,37 @@ hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, cons
   return hipGetLastError();
 }
 
+// The first (E + 3) / 4 blocks compute router rows; the blocks after them build
+// the activation table, so its loads run alongside the router's instead of
+// after them.
 __global__ __launch_bounds__(256) void k_route_front(SmallRouteArgs a) {
   const int tid = threadIdx.x, wv = tid >> 6;
-  const int e = blockIdx.x * 4 + wv;
-  if (e < a.E) {
-    const float b = a.bias ? a.bias[e] : 0.0f;
-    router_row_dispatch(a.x, a.T, a.wr, b, a.E, a.H, e, a.logits);
+  const int rblocks = (a.E + 3) / 4;
+  if ((int)blockIdx.x < rblocks) {
+    const int e = blockIdx.x * 4 + wv;
+    if (e < a.E) {
+      const float b = a.bias ? a.bias[e] : 0.0f;
+      router_row_dispatch(a.x, a.T, a.wr, b, a.E, a.H, e, a.logits);
+    }
+    return;
   }
   if (a.xpairs) {
     const int nblk = a.H / 32;
     const int items = a.T * nblk * 16;
-    for (int it = blockIdx.x * 256 + tid; it < items; it += gridDim.x * 256) {
+    const int tblocks = gridDim.x - rblocks;
+    for (int it = (blockIdx.x - rblocks) * 256 + tid; it < items; it += tblocks * 256) {
       const int row = it / (nblk * 16), rem = it % (nblk * 16);
       prep_x_item(a.x, row, a.H, rem >> 4, (rem >> 3) & 1, rem & 7, a.q3 != 0, a.xpairs, a.xinit);
     }
   }
+}
+
+static int route_front_blocks(const SmallRouteArgs& a) {
+  const int rblocks = (a.E + 3) / 4;
+  if (!a.xpairs) return rblocks;
+  const int items = a.T * (a.H / 32) * 16;
+  const int tblocks = (items + 255) / 256;
+  return rblocks + (tblocks < 64 ? tblocks : 64);
 }
 
 template <int VPL>
@@ -194,12 +210,12 @@ __global__ __launch_bounds__(256) void k_route_select(SmallRouteArgs a) {
 }
 
 hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s) {
-  MOE_LAUNCH(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  MOE_LAUNCH(k_route_front, dim3(route_front_blocks(a)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s) {
-  MOE_LAUNCH(k_route_front, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
+  MOE_LAUNCH(k_route_front, dim3(route_front_blocks(a)), dim3(256), 0, s, a);
   if (a.E <= 64)
     MOE_LAUNCH(k_route_select<1>, dim3(1), dim3(256), 0, s, a);
   else if (a.E <= 128)

@@ -33,12 +33,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # profiles/ counter summary), each scaled by what the counter reads for a plain
 # 256 MiB device copy: FETCH_SIZE reads 131,084.5 KiB for 262,144 KiB read
 # (factor 2.0), WRITE_SIZE 262,144 KiB for 262,144 KiB written (factor 1.0).
-# Reported only while the kernel's sources are the ones that were counted.
+# Reported only while the kernel's sources are the ones that were counted
+# (an empty hash: not counted for the current sources).
 GATEUP_TRAFFIC = {
-    "sources": ["decode_ffn.hip", "device.h", "table.h", "topk.h"],
-    "sha256": "eaa0e358e29003e8b2131c6e7d02c6aeb4a5bb70ee763cc6872bb1506a60154e",
-    "fetch_kib": 22275.5, "fetch_scale": 262144.0 / 131084.4,
-    "write_kib": 118.8, "write_scale": 1.0,
+    "sources": ["decode_mx.hip", "mx.h", "mfma.h", "device.h", "topk.h"],
+    "sha256": "",
+    "fetch_kib": 0.0, "fetch_scale": 262144.0 / 131084.4,
+    "write_kib": 0.0, "write_scale": 1.0,
     "tokens": 4,
 }
 
@@ -453,7 +454,7 @@ def main():
                    "layer_GBps": step_bytes1 / (ms1_step * 1e-3) / 1e9},
         },
         "roofline": {
-            "kernel": "k_decode_gateup (top-k, gate/up + SwiGLU 2-bit dequant-GEMV, down-table epilogue)",
+            "kernel": "k_decode_gateup_mx (top-k, gate/up + SwiGLU on the fp8 x fp4 matrix cores, down-table epilogue)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

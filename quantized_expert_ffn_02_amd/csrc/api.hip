@@ -6,6 +6,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "mx.h"
 
 using namespace moe;
 
@@ -62,6 +63,7 @@ struct Layout {
   size_t counts, base, offsets, sorted_rows, row_to_sorted, items, n_items;
   size_t xtab_pairs, xtab_init, xf32, xf16, hf16, tiles, n_tiles;
   size_t h, htab_pairs, htab_init, y;
+  size_t xmx_data, xmx_exps, hmx_data, hmx_exps;   // fp8-piece tables (mx.h)
   size_t out_f32, xa, xb, xn;     // stack ping-pong buffers and the normalised layer input
   size_t miss_flag;
   size_t total;
@@ -104,6 +106,14 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
   o.htab_init = take(dense ? 0 : n * (I / 32) * 4);
   o.y = take(n * H * 4);
+  // fp8-piece tables of the 2-bit decode batch (up to kDecodeDirectMaxTokens tokens)
+  const bool mx = decode_mx_ok((int)H, (int)I, L->routed.fmt == MOE_FMT_Q3 ? 1 : 0) && !dense;
+  const int64_t Tm = mx ? (T < kDecodeDirectMaxTokens ? T : kDecodeDirectMaxTokens) : 0;
+  const int64_t nm = Tm * k + Tm;
+  o.xmx_data = take(Tm * mx_data_bytes((int)H));
+  o.xmx_exps = take(Tm * mx_exps_bytes((int)H));
+  o.hmx_data = take(nm * mx_data_bytes((int)I));
+  o.hmx_exps = take(nm * mx_exps_bytes((int)I));
   o.out_f32 = take(T * H * 4);
   o.xa = take(T * H * 2);
   o.xb = take(T * H * 2);
@@ -441,6 +451,49 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     a.wr = L->w_router;
     a.bias = L->router_bias;
     a.logits = at<float>(ws, lay.logits);
+    if (decode_mx_ok(L->hidden, L->inter, a.q3)) {
+      // 2-bit weights: the fp8 x fp4 matrix-core kernels
+      a.xpairs = nullptr;
+      a.xinit = nullptr;
+      a.xmx_data = at<uint8_t>(ws, lay.xmx_data);
+      a.xmx_exps = at<uint8_t>(ws, lay.xmx_exps);
+      MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_front(a, s); }));
+      MxFfnArgs m;
+      m.r13 = mat_w13(L->routed);
+      m.r2 = mat_w2(L->routed);
+      if (with_shared) {
+        m.s13 = mat_w13(L->shared);
+        m.s2 = mat_w2(L->shared);
+      }
+      m.H = L->hidden;
+      m.I = L->inter;
+      m.T = T;
+      m.k = k;
+      m.E = E;
+      m.with_shared = with_shared;
+      m.logits = a.logits;
+      m.ids = ids;
+      m.gates = gates;
+      m.margin = margin;
+      m.xdata = a.xmx_data;
+      m.xexps = a.xmx_exps;
+      m.hdata = at<uint8_t>(ws, lay.hmx_data);
+      m.hexps = at<uint8_t>(ws, lay.hmx_exps);
+      m.y = at<float>(ws, lay.y);
+      MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] { return launch_decode_gateup_mx(m, s); }));
+      MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] { return launch_decode_down_mx(m, s); }));
+      DecodeFfnArgs d;
+      d.H = L->hidden;
+      d.T = T;
+      d.k = k;
+      d.with_shared = with_shared;
+      d.y = m.y;
+      d.residual = residual;
+      d.out = out;
+      d.out_bf16 = out_bf16;
+      MOE_TRY(launch_decode_combine(d, s));
+      return MOE_OK;
+    }
     a.xpairs = at<uint32_t>(ws, lay.xtab_pairs);
     a.xinit = at<float>(ws, lay.xtab_init);
     MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_front(a, s); }));

@@ -16,6 +16,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "mx.h"
 #include "table.h"
 #include "topk.h"
 
@@ -104,6 +105,24 @@ __global__ __launch_bounds__(256) void k_route_front(SmallRouteArgs a) {
     }
     return;
   }
+  if (a.xmx_data) {
+    // fp8-piece table (256-column form, read by the gate/up kernel): one
+    // element per thread, a half wave per 32-column block
+    // (T H is a multiple of 64, so every wave is whole); thread of position p
+    // reads the weight index at p
+    const int items = a.T * a.H;
+    const int tblocks = gridDim.x - rblocks;
+    for (int base = (blockIdx.x - rblocks) * 256; base < items; base += tblocks * 256) {
+      const int it = base + tid;
+      if (it < items) {
+        const int row = it / a.H, col = it - row * a.H;
+        const int B = col >> 5, p = col & 31;
+        const float v = bf16_to_f32(a.x[(size_t)row * a.H + 32 * B + mx_weight_at(p)]);
+        mx_emit(v, row, mx_slot256(B), p, a.H, a.xmx_data, a.xmx_exps);
+      }
+    }
+    return;
+  }
   if (a.xpairs) {
     const int nblk = a.H / 32;
     const int items = a.T * nblk * 16;
@@ -117,8 +136,8 @@ __global__ __launch_bounds__(256) void k_route_front(SmallRouteArgs a) {
 
 static int route_front_blocks(const SmallRouteArgs& a) {
   const int rblocks = (a.E + 3) / 4;
-  if (!a.xpairs) return rblocks;
-  const int items = a.T * (a.H / 32) * 16;
+  if (!a.xpairs && !a.xmx_data) return rblocks;
+  const int items = a.xmx_data ? a.T * a.H : a.T * (a.H / 32) * 16;
   const int tblocks = (items + 255) / 256;
   return rblocks + (tblocks < 64 ? tblocks : 64);
 }

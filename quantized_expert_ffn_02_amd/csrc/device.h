@@ -39,6 +39,13 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
   return r;
 }
 
+// Raw buffer resource (gfx9 layout, stride 0) over `bytes` bytes from `base`:
+// loads take a 32-bit per-lane offset and a wave-uniform scalar offset, and
+// return zero past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);

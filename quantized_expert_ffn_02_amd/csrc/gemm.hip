@@ -225,13 +225,6 @@ struct GemmArgs {
   uint32_t code_bytes, scale_bytes;
 };
 
-// Raw buffer resource (gfx9 layout, stride 0) over `bytes` bytes from `base`:
-// loads take a 32-bit per-lane offset and a wave-uniform scalar offset, and
-// return zero past the end.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // MAXNMI = 32-row fragments per wave (tile height 32 MAXNMI: 32, 64 or 128
 // rows); NMI <= MAXNMI the fragments this tile's rows need.  As holds three LDS
 // buffers of the A tile.  128-row tiles run with the transposed accumulator

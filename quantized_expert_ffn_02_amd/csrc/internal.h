@@ -95,6 +95,8 @@ struct SmallRouteArgs {
   float* logits;
   uint32_t* xpairs;    // activation table (NULL: not built)
   float* xinit;
+  uint8_t* xmx_data = nullptr;   // fp8-piece activation table (mx.h; NULL: not built)
+  uint8_t* xmx_exps = nullptr;
   int32_t* ids;
   float* gates;
   float* margin;       // may be NULL
@@ -129,6 +131,25 @@ struct DecodeFfnArgs {
   uint16_t* out_bf16 = nullptr;       // [T][H] or NULL
 };
 bool decode_direct_ok(int T, int k, int with_shared, int H, int I);
+
+// The same decode FFN with 2-bit weights on the fp8 x fp4 matrix cores
+// (decode_mx.hip, mx.h): activation tables of e4m3 pieces with block exponents.
+struct MxFfnArgs {
+  MatRef r13, s13, r2, s2;
+  int H = 0, I = 0, T = 0, k = 0, E = 0, with_shared = 0;
+  const float* logits = nullptr;      // [T][E] router logits
+  int32_t* ids = nullptr;             // [T][k] written by the gate/up launch
+  float* gates = nullptr;             // [T][k]
+  float* margin = nullptr;            // [T] or NULL
+  const uint8_t* xdata = nullptr;     // activation table of x, one row per token
+  const uint8_t* xexps = nullptr;
+  uint8_t* hdata = nullptr;           // table of h, one row per entry
+  uint8_t* hexps = nullptr;
+  float* y = nullptr;                 // [entries][H] gate-scaled expert outputs
+};
+bool decode_mx_ok(int H, int I, int q3);
+hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s);
+hipError_t launch_decode_down_mx(const MxFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_gateup(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);

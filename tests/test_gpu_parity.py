@@ -217,10 +217,14 @@ def test_steps_match_fused_layer():
     ref_out, *_ = hl.oracle_forward(x)
     assert OL.rel_max_err(host(out), ref_out) <= OUT_TOL
     # The fused layer addresses a decode batch's entries directly (top-k inside
-    # the gate/up launch, combine inside the down launch, one wave per entry);
-    # the steps sum the same products in another fixed order.
+    # the gate/up launch) and runs its 2-bit products on the fp8 x fp4 matrix
+    # cores: x and h enter as four fixed-point e4m3 pieces per 32-column block,
+    # exact to 2^-19 of the block's largest magnitude.  For h (largest / rms of
+    # a block about 4) that is about 2^-19 * 4 / sqrt(3) ~ 4e-6 relative per
+    # element; over 2,560 output rows the largest deviation is a few times
+    # that, so the two paths agree to well under 4e-5 (max |diff| / rms).
     out_f, *_ = run_layer(d, x, T)
-    assert OL.rel_max_err(host(out), out_f.astype(np.float64)) <= 1e-5
+    assert OL.rel_max_err(host(out), out_f.astype(np.float64)) <= 4e-5
 
 
 # ------------------------------------------------------------------ prefill (MFMA grouped GEMM)

@@ -7,13 +7,14 @@
 //
 // k_decode_gateup_mx: block (entry r, 64 rows of gate and of up).  Wave 0
 //   selects the token's top-k from the router logits; every wave reads its
-//   chunks of the token's activation table first (they do not depend on the
-//   expert), then its 16-row x 128-column weight fragments of the chosen
-//   expert, and runs one MFMA per fragment.  The partial sums of the waves and
-//   blocks are added in a fixed order, and the epilogue writes
+//   chunks of the token's activation table (they do not depend on the
+//   expert), then the chosen expert's 16-byte code lanes of its 256 columns
+//   (two 32-weight blocks each, two MFMAs per load).  The partial sums of the
+//   waves and lanes are added in a fixed order, and the epilogue writes
 //   h = SiLU(gate) * up as the down projection's activation table.
-// k_decode_down_mx: block (entry r, 64 NG output rows), the K = I columns split
-//   over the waves; the epilogue scales by the entry's gate.
+// k_decode_down_mx: block (entry r, 64 output rows), one wave per 256 columns
+//   of K = I and one for a 128-column tail; the epilogue scales by the
+//   entry's gate.
 //
 // The combine is k_decode_combine (decode_ffn.hip).
 #include <math.h>
@@ -26,33 +27,9 @@
 
 namespace moe {
 
-// Weight rows of one 64-row group ng of an expert matrix, decode layout: tile
-// (ng, c64) of 64 rows x 64 columns is 1,024 bytes, row-major by row, 16 bytes
-// per row (two 32-weight blocks of two u32 words); scales per (ng, 128-column
-// chunk) are 64 rows x 4 fp16.
-struct MxLanes {
-  uint32_t code[4];    // byte offset of this lane's 8 code bytes, subgroup s (16 rows), chunk 0
-  uint32_t scale[4];   // byte offset of its fp16 scale, subgroup s, chunk 0
-};
-
-__device__ __forceinline__ MxLanes mx_weight_lanes(int lane) {
-  const int n = lane & 15, G = lane >> 4;
-  MxLanes L;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    L.code[s] = (uint32_t)((((G >> 1) * 64 + 16 * s + n) * 16) + 8 * (G & 1));
-    L.scale[s] = (uint32_t)(((16 * s + n) * 4 + G) * 2);
-  }
-  return L;
-}
-
-// Scalar offsets of row group ng and chunk c (K columns).
-__device__ __forceinline__ uint32_t mx_code_soff(int ng, int c, int K) {
-  return (uint32_t)(((size_t)ng * (K / 64) + 2 * c) * 1024);
-}
-__device__ __forceinline__ uint32_t mx_scale_soff(int ng, int c, int K) {
-  return (uint32_t)(((size_t)ng * (K / 128) + c) * 512);
-}
+// Weight layout (decode form): rows in groups of 64; tile (group, 64-column
+// chunk) is 1,024 bytes, 16 bytes per row (two 32-weight blocks of two u32
+// words); scales per (group, 128-column chunk) are 64 rows x 4 fp16.
 
 // Activation operand of chunk c and this lane's scale byte.
 struct MxAct {
@@ -205,29 +182,33 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
       }
     const float hv = g / (1.0f + expf(-g)) * up;
     // h row lane of this block is column 64 rg + lane of the entry's h: block
-    // 2 rg + lane / 32 (128-column table form, read by the down kernel),
-    // weight index lane % 32
-    mx_emit(hv, r, mx_slot128(2 * rg + (lane >> 5)), mx_pos_of_weight(lane & 31), a.I, a.hdata, a.hexps);
+    // 2 rg + lane / 32 (mixed table form, read by the down kernel), weight
+    // index lane % 32
+    mx_emit(hv, r, mx_slot_mixed(2 * rg + (lane >> 5), a.I), mx_pos_of_weight(lane & 31), a.I, a.hdata, a.hexps);
   }
 }
 
-// NG 64-row output groups per block; K = I columns over W waves of CPW chunks.
-template <int W, int CPW, int NG>
-__global__ __launch_bounds__(W * 64) void k_decode_down_mx(MxFfnArgs a) {
-  __shared__ float red[W][4 * NG][64];
+// Down projection of entry r and 64 output rows; K = I = 256 NS + 128 TAIL
+// columns, one wave per 256 columns (16-byte code lanes, two MFMAs per load
+// as in the gate/up kernel) and one for a 128-column tail (8-byte code lanes,
+// one MFMA per load).  The epilogue scales by the entry's gate.
+template <int NS, int TAIL>
+__global__ __launch_bounds__((NS + TAIL) * 64) void k_decode_down_mx(MxFfnArgs a) {
+  constexpr int W = NS + TAIL;
+  __shared__ float red[W][4][64];
   const int r = blockIdx.x, rg = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int K = a.I, nc = K / 128;
+  const int K = a.I;
   const int Tk = a.T * a.k;
-  const int c0 = wv * CPW;
+  const bool tail = wv >= NS;   // wave-uniform
 
   const MxALane AL = mx_a_lane(lane);
   const __amdgpu_buffer_rsrc_t rhd = buffer_rsrc(a.hdata + (size_t)r * mx_data_bytes(K), (uint32_t)mx_data_bytes(K));
   const __amdgpu_buffer_rsrc_t rhe = buffer_rsrc(a.hexps + (size_t)r * mx_exps_bytes(K), (uint32_t)mx_exps_bytes(K));
-  MxAct X[CPW];
-#pragma unroll
-  for (int u = 0; u < CPW; ++u) X[u] = mx_load_act(rhd, rhe, AL, min(c0 + u, nc - 1));
+  // virtual chunks: 2 wv (even blocks), 2 wv + 1 (odd blocks); the tail wave's 128 columns are chunk 2 NS
+  MxAct X0 = mx_load_act(rhd, rhe, AL, tail ? 2 * NS : 2 * wv);
+  MxAct X1 = mx_load_act(rhd, rhe, AL, tail ? 2 * NS : 2 * wv + 1);
 
   const int grp = r < Tk ? __builtin_amdgcn_readfirstlane(a.ids[r]) : a.E;
   const bool is_shared = grp == a.E;
@@ -235,64 +216,70 @@ __global__ __launch_bounds__(W * 64) void k_decode_down_mx(MxFfnArgs a) {
   const size_t eidx = is_shared ? 0 : (size_t)grp;
   const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(M.codes + eidx * M.code_stride, (uint32_t)M.code_stride);
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(M.scales + eidx * M.scale_stride, (uint32_t)(M.scale_stride * 2));
-  const MxLanes WL = mx_weight_lanes(lane);
+  const int n = lane & 15, q = lane >> 4;
+  const int nch64 = K / 64, n128 = K / 128;
 
-  uint2 cw[CPW][NG][4];
-  uint32_t sc[CPW][NG][4];
+  u32x4 cw[4];
+  uint32_t sc[4];
+  if (!tail) {
+    const uint32_t cso = (uint32_t)(((size_t)rg * nch64 + 4 * wv) * 1024);
+    const uint32_t sso = (uint32_t)(((size_t)rg * n128 + 2 * wv) * 512);
 #pragma unroll
-  for (int u = 0; u < CPW; ++u) {
-    const int c = min(c0 + u, nc - 1);
+    for (int s = 0; s < 4; ++s) {
+      cw[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(q * 1024 + (16 * s + n) * 16), cso, 0);
+      sc[s] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(((q >> 1) * 64 + 16 * s + n) * 8 + (q & 1) * 4), sso, 0);
+    }
+  } else {
+    // 128-column chunk c = 2 NS: lane (n, q) reads block q of row n (8 bytes) and its scale
+    const int c = 2 * NS;
+    const uint32_t cso = (uint32_t)(((size_t)rg * nch64 + 2 * c) * 1024);
+    const uint32_t sso = (uint32_t)(((size_t)rg * n128 + c) * 512);
 #pragma unroll
-    for (int gq = 0; gq < NG; ++gq) {
-      const int ngr = rg * NG + gq;
-      const uint32_t cso = mx_code_soff(ngr, c, K), sso = mx_scale_soff(ngr, c, K);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, WL.code[s], cso, 0);
-        cw[u][gq][s] = make_uint2(v[0], v[1]);
-        sc[u][gq][s] = __builtin_amdgcn_raw_buffer_load_b16(rs, WL.scale[s], sso, 0);
-      }
+    for (int s = 0; s < 4; ++s) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+          rc, (uint32_t)((((q >> 1) * 64 + 16 * s + n) * 16) + 8 * (q & 1)), cso, 0);
+      cw[s] = u32x4{v[0], v[1], 0u, 0u};
+      sc[s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(((16 * s + n) * 4 + q) * 2), sso, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first product
-  float y[NG][4];
+  const mx_v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  {
+    const mx_v8i A = mx_act_operand(X0);
+    const mx_v4f off = mx_mfma(A, mx_minus_one(), (int)X0.sa, zero);
 #pragma unroll
-  for (int gq = 0; gq < NG; ++gq)
+    for (int s = 0; s < 4; ++s) {
+      const mx_v4f o = mx_mfma(A, mx_weights(cw[s].x, cw[s].y), (int)X0.sa, off);
+      y[s] = mx_accumulate(o, sc[s] & 0xFFFFu, y[s]);
+    }
+  }
+  if (!tail) {
+    const mx_v8i A = mx_act_operand(X1);
+    const mx_v4f off = mx_mfma(A, mx_minus_one(), (int)X1.sa, zero);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) y[gq][s] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < CPW; ++u) {
-    const bool valid = c0 + u < nc;
-    const mx_v8i A = mx_act_operand(X[u]);
-    const mx_v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    const mx_v4f off = mx_mfma(A, mx_minus_one(), (int)X[u].sa, zero);   // -2 sum v per (piece, block)
-#pragma unroll
-    for (int gq = 0; gq < NG; ++gq)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const mx_v4f o = mx_mfma(A, mx_weights(cw[u][gq][s].x, cw[u][gq][s].y), (int)X[u].sa, off);
-        const float t = mx_accumulate(o, sc[u][gq][s], y[gq][s]);
-        y[gq][s] = valid ? t : y[gq][s];
-      }
+    for (int s = 0; s < 4; ++s) {
+      const mx_v4f o = mx_mfma(A, mx_weights(cw[s].z, cw[s].w), (int)X1.sa, off);
+      y[s] = mx_accumulate(o, sc[s] >> 16, y[s]);
+    }
   }
 #pragma unroll
-  for (int gq = 0; gq < NG; ++gq)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) red[wv][gq * 4 + s][lane] = y[gq][s];
+  for (int s = 0; s < 4; ++s) red[wv][s][lane] = y[s];
   __syncthreads();
   const int t = threadIdx.x;
-  if (t < 64 * NG) {
-    const int gq = t >> 6, s = (t >> 4) & 3, n = t & 15;
+  if (t < 64) {
+    const int s = t >> 4, nn = t & 15;
     float acc = 0.0f;
+#pragma unroll
     for (int w = 0; w < W; ++w)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc += red[w][gq * 4 + s][16 * q + n];
+      for (int qq = 0; qq < 4; ++qq) acc += red[w][s][16 * qq + nn];
     const float gate = r < Tk ? a.gates[r] : 1.0f;
-    a.y[(size_t)r * a.H + (size_t)rg * 64 * NG + t] = gate * acc;
+    a.y[(size_t)r * a.H + (size_t)rg * 64 + t] = gate * acc;
   }
 }
 
-bool decode_mx_ok(int H, int I, int q3) { return !q3 && H % 256 == 0 && I % 128 == 0 && H / 256 <= 20 && I / 128 <= 10; }
+bool decode_mx_ok(int H, int I, int q3) { return !q3 && H % 256 == 0 && I % 128 == 0 && H / 256 <= 20 && I <= 1024; }
 
 hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
   const int entries = a.T * a.k + (a.with_shared ? a.T : 0);
@@ -314,12 +301,22 @@ hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_down_mx(const MxFfnArgs& a, hipStream_t s) {
   const int entries = a.T * a.k + (a.with_shared ? a.T : 0);
-  const int nc = a.I / 128;
+  const int ns = a.I / 256, tail = (a.I % 256) ? 1 : 0;
   dim3 grid(entries, a.H / 64);
-  if (nc <= 5)
-    MOE_LAUNCH((k_decode_down_mx<5, 1, 1>), grid, dim3(320), 0, s, a);
-  else
-    MOE_LAUNCH((k_decode_down_mx<5, 2, 1>), grid, dim3(320), 0, s, a);
+#define MOE_DOWN_MX(NS, TL) MOE_LAUNCH((k_decode_down_mx<NS, TL>), grid, dim3((NS + TL) * 64), 0, s, a)
+  switch (ns * 2 + tail) {
+    case 1: MOE_DOWN_MX(0, 1); break;
+    case 2: MOE_DOWN_MX(1, 0); break;
+    case 3: MOE_DOWN_MX(1, 1); break;
+    case 4: MOE_DOWN_MX(2, 0); break;
+    case 5: MOE_DOWN_MX(2, 1); break;
+    case 6: MOE_DOWN_MX(3, 0); break;
+    case 7: MOE_DOWN_MX(3, 1); break;
+    case 8: MOE_DOWN_MX(4, 0); break;
+    case 9: MOE_DOWN_MX(4, 1); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DOWN_MX
   return hipGetLastError();
 }
 

@@ -162,6 +162,9 @@ __device__ __forceinline__ MxALane mx_a_lane(int lane) {
 // block B in chunk 2 (B / 8) + B % 2, block (B % 8) / 2 of it.
 __host__ __device__ constexpr int mx_slot128(int B) { return B; }
 __host__ __device__ constexpr int mx_slot256(int B) { return 4 * (2 * (B >> 3) + (B & 1)) + ((B & 7) >> 1); }
+// Mixed form for K = 256 ns + 128 t: the 256-column form for the first 256 ns
+// columns, a 128-column chunk for the rest.
+__host__ __device__ constexpr int mx_slot_mixed(int B, int K) { return B < (K / 256) * 8 ? mx_slot256(B) : B; }
 
 // Activation table of this lane's value v (this half wave holds the block in
 // table slot `slot`, this lane position p of the block) in row `row`: pieces

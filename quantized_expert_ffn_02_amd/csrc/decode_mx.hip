@@ -70,7 +70,7 @@ __device__ __forceinline__ float mx_accumulate(const mx_v4f& o, uint32_t scale16
 // takes the even blocks (words 0, 1), the second the odd ones (words 2, 3).
 template <int W, int SPW, int VPL>
 __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
-  __shared__ float red[W][8][64];
+  __shared__ __attribute__((aligned(16))) float red[W][8][64];
   __shared__ int s_expert;
   const int r = blockIdx.x, rg = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -100,9 +100,13 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
   if (select) {
     const int i = r - tok * a.k;
     if (wv == 0) {
-      const TopkKeys keys = wave_topk_keys<VPL>(a.logits + (size_t)tok * a.E, a.E, a.k);
+      // only the block that writes the token's ids, gates and margin needs all
+      // k + 1 ranks; the others stop at their own
+      const bool writer = i == 0 && rg == 0;
+      const TopkKeys keys =
+          wave_topk_keys<VPL>(a.logits + (size_t)tok * a.E, a.E, a.k, 1, 0, nullptr, writer ? 0x7FFFFFFF : i + 1);
       if (lane == 0) s_expert = topk_rank_id(keys, i);
-      if (i == 0 && rg == 0)
+      if (writer)
         topk_write(keys, a.E, a.k, a.ids + (size_t)tok * a.k, a.gates + (size_t)tok * a.k,
                    a.margin ? a.margin + tok : nullptr);
     }
@@ -164,22 +168,30 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
         }
     }
   }
+  // partial sums at [wave][m * 4 + s][row n][lane group q], so that each row's
+  // four lane groups are one 16-byte read
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) red[wv][m * 4 + s][lane] = y[m][s];
+    for (int s = 0; s < 4; ++s) red[wv][m * 4 + s][(lane & 15) * 4 + (lane >> 4)] = y[m][s];
   __syncthreads();
   if (wv == 0) {
     // row lane of the 64: subgroup s = lane / 16, row n = lane % 16 of it;
     // waves in order, then the four lane groups in order
     const int s = lane >> 4, nn = lane & 15;
     float g = 0.0f, up = 0.0f;
-    for (int w = 0; w < W; ++w)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        g += red[w][s][16 * qq + nn];
-        up += red[w][4 + s][16 * qq + nn];
-      }
+    for (int w = 0; w < W; ++w) {
+      const float4 gv = *reinterpret_cast<const float4*>(&red[w][s][nn * 4]);
+      const float4 uv = *reinterpret_cast<const float4*>(&red[w][4 + s][nn * 4]);
+      g += gv.x;
+      g += gv.y;
+      g += gv.z;
+      g += gv.w;
+      up += uv.x;
+      up += uv.y;
+      up += uv.z;
+      up += uv.w;
+    }
     const float hv = g / (1.0f + expf(-g)) * up;
     // h row lane of this block is column 64 rg + lane of the entry's h: block
     // 2 rg + lane / 32 (mixed table form, read by the down kernel), weight

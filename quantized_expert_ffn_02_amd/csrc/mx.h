@@ -91,13 +91,28 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
+// Largest |v| over each 32-lane half of the wave, in every lane of that half:
+// DPP steps inside each 16-lane row (magnitudes as unsigned words order like
+// the floats; moves from outside the row read 0), then the four row results.
+__device__ __forceinline__ float half_wave_max_abs(float v) {
+  uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, true));    // quad_perm 1,0,3,2
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, true));    // quad_perm 2,3,0,1
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xF, 0xF, true));   // row_ror 4
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, true));   // row_ror 8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)u, 48);
+  const int lane = threadIdx.x & 63;
+  return __uint_as_float(lane < 32 ? max(r0, r1) : max(r2, r3));
+}
+
 // Pieces of the value v held by this lane; the 32 lanes of each half wave form
 // one block (all 64 lanes must call).  p[j]: e4m3 bytes; sb[j]: E8M0 scale
 // bytes (127 + e_j + 1).
 __device__ __forceinline__ void mx_pieces(float v, uint32_t (&p)[kMxPieces], uint32_t (&sb)[kMxPieces]) {
-  float m = fabsf(v);
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float m = half_wave_max_abs(v);
   int e = (int)((__float_as_uint(m) >> 23) & 255u) - 134;   // floor(log2 m) - 7
   e = m > 0.0f ? (e < -113 ? -113 : e) : 0;                  // e - 15 stays a valid scale
   float r = v;

@@ -59,9 +59,11 @@ struct TopkKeys {
 // PARTS: the logits are the sum of np (<= 8) partial planes pstride floats
 // apart (added in plane order) plus bias (if not NULL), as a K-split router
 // leaves them.
+// max_rounds < k + 1 stops after that many ranks (wave-uniform): lanes below it
+// hold their ranks' keys, ``last`` and ``next`` are then not set.
 template <int VPL, bool PARTS = false>
 __device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k, int np = 1, size_t pstride = 0,
-                                   const float* __restrict__ bias = nullptr) {
+                                   const float* __restrict__ bias = nullptr, int max_rounds = 0x7FFFFFFF) {
   const int lane = threadIdx.x & 63;
   // all VPL loads in flight at once (clamped index, no branch around a load)
   float v[VPL];
@@ -115,7 +117,7 @@ __device__ TopkKeys wave_topk_keys(const float* __restrict__ row, int E, int k, 
   }
   TopkKeys r;
   r.mine = r.last = r.next = 0;
-  const int rounds = k < E ? k + 1 : k;
+  const int rounds = min(k < E ? k + 1 : k, max_rounds);
   for (int q = 0; q < rounds; ++q) {
     const uint32_t mh = wave_max_u32(khi[0]);
     const uint64_t tied = __ballot(khi[0] == mh);

@@ -149,7 +149,7 @@ def run_layer(d, x, T, residual=None):
     return host(out), host(out_bf), host(ids), host(gates), host(margin), ws
 
 
-@pytest.mark.parametrize("workload,T", [("tiny", 4), ("decode", 1), ("decode", 4), ("decode", 64),
+@pytest.mark.parametrize("workload,T", [("tiny", 4), ("decode", 1), ("decode", 4), ("decode", 16), ("decode", 64),
                                         ("decode", 100)])
 def test_layer_forward_parity(workload, T):
     hl = W.host_layer(workload)
@@ -164,6 +164,41 @@ def test_layer_forward_parity(workload, T):
     np.testing.assert_allclose(margin, m_r, rtol=0, atol=1e-5)
     # bf16 copy = RNE of the fp32 output
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
+def test_decode_extreme_activation_blocks():
+    # The 2-bit decode path carries each 32-column block of x (and of h) as
+    # fixed-point e4m3 pieces against the block's largest magnitude.  Blocks
+    # that are all zero, 2^-20 or 1e3 times the rest, one large value among
+    # tiny ones, or alternating magnitudes must still reach the oracle closely
+    # (represented values within 2^-19 of each block's largest magnitude).
+    from oracle import formats
+    hl = W.host_layer("decode")
+    T, H = 4, hl.H
+    x, _ = W.activations_with_margin(hl, T)
+    xf = formats.bf16_to_f64(x).astype(np.float32)
+
+    def blk(b):
+        return slice(32 * b, 32 * b + 32)
+
+    xf[0, blk(0)] = 0.0
+    xf[0, blk(5)] *= 1e-6
+    xf[0, blk(9)] *= 1e3
+    xf[1, blk(2)] *= 1e-5
+    xf[1, 64 + 7] = 100.0
+    xf[1, blk(7)] *= 2.0 ** -20
+    xf[2, blk(3)] = np.where(np.arange(32) % 2 == 0, 1e2, 1e-3).astype(np.float32)
+    x2 = synth.f32_to_bf16_bits(xf)
+    m = OL.topk_margin(OL.router_logits(x2, hl.wr, hl.bias), hl.shape.top_k)
+    assert (m >= 1e-4).all(), f"router margin of the crafted rows: {m}"
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x2, T)
+    ref, *_ = hl.oracle_forward(x2)
+    assert_route_matches(ids, gates, hl.logits(x2), hl.shape.top_k, "extreme blocks")
+    for t in range(T):
+        err = OL.rel_max_err(out[t], ref[t])
+        print(f"extreme blocks token {t}: max|err|/rms = {err:.3e}")
+        assert err <= 1e-4
 
 
 @pytest.mark.parametrize("workload,T", [("tiny", 4), ("decode", 4)])

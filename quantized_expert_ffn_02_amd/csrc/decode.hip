@@ -22,9 +22,26 @@
 
 namespace moe {
 
+// Sum over the 64 lanes in a fixed order (wave-uniform result): DPP adds
+// inside each 16-lane row (quad exchanges, then rotations by 4 and 8), then
+// the four row sums in row order.
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));    // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));    // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));   // row_ror 4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));   // row_ror 8
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 // logits of expert row e for tokens [t0, t0 + TB): the row's NC 16-byte chunks
 // per lane and the matching x chunks of all TB tokens are loaded before any
-// arithmetic (one memory round trip per call).
+// arithmetic (one memory round trip per call).  Loads past the row or past T
+// read a clamped address (no branch around a load); their products are zeroed
+// or not stored.
 template <int TB, int NC>
 __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T, int t0,
                                            const uint16_t* __restrict__ wr, float b, int E, int H, int e,
@@ -35,13 +52,14 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T
   uint4 w[NC], xv[TB][NC];
 #pragma unroll
   for (int u = 0; u < NC; ++u) {
-    const int c = lane + 64 * u;
-    w[u] = c < nch ? wrow[c] : make_uint4(0, 0, 0, 0);
+    const int c = min(lane + 64 * u, nch - 1);
+    w[u] = wrow[c];
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
-      xv[i][u] = (c < nch && t0 + i < T) ? reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H)[c]
-                                         : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < TB; ++i) xv[i][u] = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + i, T - 1) * H)[c];
   }
+#pragma unroll
+  for (int u = 0; u < NC; ++u)
+    if (lane + 64 * u >= nch) w[u] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     float a = 0.0f;
@@ -52,7 +70,7 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T
       a = dot2_bf16(w[u].z, xv[i][u].z, a);
       a = dot2_bf16(w[u].w, xv[i][u].w, a);
     }
-    const float sum = wave_sum(a);
+    const float sum = wave_sum_rows(a);
     if (lane == 0 && t0 + i < T) logits[(size_t)(t0 + i) * E + e] = sum + b;
   }
 }

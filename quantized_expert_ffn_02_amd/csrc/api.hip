@@ -481,6 +481,12 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
       m.hexps = at<uint8_t>(ws, lay.hmx_exps);
       m.y = at<float>(ws, lay.y);
       MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMV, s, [&] { return launch_decode_gateup_mx(m, s); }));
+      if (decode_down_combine_mx_ok(L->inter, k, with_shared)) {
+        // down projection and combine in one launch (a block per token and 64 rows)
+        MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s,
+                      [&] { return launch_decode_down_combine_mx(m, residual, out, out_bf16, s); }));
+        return MOE_OK;
+      }
       MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] { return launch_decode_down_mx(m, s); }));
       DecodeFfnArgs d;
       d.H = L->hidden;

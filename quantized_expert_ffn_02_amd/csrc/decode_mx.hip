@@ -291,6 +291,103 @@ __global__ __launch_bounds__((NS + TAIL) * 64) void k_decode_down_mx(MxFfnArgs a
   }
 }
 
+// Down projection and combine of token t and 64 output rows: wave i < k takes
+// routed entry t k + i, wave k the shared expert, each over all K = I columns
+// (256-column chunks, then the 128-column tail, in order); waves past the
+// token's entries only join the barrier.  The block then adds the entries'
+// gate-scaled rows in rank order, the shared expert's row and the residual.
+template <int W, int NS, int TAIL>
+__global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, const uint16_t* __restrict__ residual,
+                                                                  float* __restrict__ out,
+                                                                  uint16_t* __restrict__ out_bf16) {
+  constexpr int NV = 2 * NS + TAIL;   // activation chunks of K
+  __shared__ __attribute__((aligned(16))) float red[W][4][64];
+  const int tok = blockIdx.x, rg = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int K = a.I;
+  const int Tk = a.T * a.k;
+  const int n_ent = a.k + (a.with_shared ? 1 : 0);
+  if (wv < n_ent) {
+    const int r = wv < a.k ? tok * a.k + wv : Tk + tok;
+    const MxALane AL = mx_a_lane(lane);
+    const __amdgpu_buffer_rsrc_t rhd = buffer_rsrc(a.hdata + (size_t)r * mx_data_bytes(K), (uint32_t)mx_data_bytes(K));
+    const __amdgpu_buffer_rsrc_t rhe = buffer_rsrc(a.hexps + (size_t)r * mx_exps_bytes(K), (uint32_t)mx_exps_bytes(K));
+    MxAct X[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) X[v] = mx_load_act(rhd, rhe, AL, v);
+
+    const int grp = r < Tk ? __builtin_amdgcn_readfirstlane(a.ids[r]) : a.E;
+    const bool is_shared = grp == a.E;
+    const MatRef& M = is_shared ? a.s2 : a.r2;
+    const size_t eidx = is_shared ? 0 : (size_t)grp;
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(M.codes + eidx * M.code_stride, (uint32_t)M.code_stride);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(M.scales + eidx * M.scale_stride, (uint32_t)(M.scale_stride * 2));
+    const int n = lane & 15, q = lane >> 4;
+    const int nch64 = K / 64, n128 = K / 128;
+
+    u32x4 cw[NS + TAIL][4];
+    uint32_t sc[NS + TAIL][4];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      const uint32_t cso = (uint32_t)(((size_t)rg * nch64 + 4 * c) * 1024);
+      const uint32_t sso = (uint32_t)(((size_t)rg * n128 + 2 * c) * 512);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        cw[c][s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(q * 1024 + (16 * s + n) * 16), cso, 0);
+        sc[c][s] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, (uint32_t)(((q >> 1) * 64 + 16 * s + n) * 8 + (q & 1) * 4), sso, 0);
+      }
+    }
+    if (TAIL) {
+      const int c = 2 * NS;
+      const uint32_t cso = (uint32_t)(((size_t)rg * nch64 + 2 * c) * 1024);
+      const uint32_t sso = (uint32_t)(((size_t)rg * n128 + c) * 512);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+            rc, (uint32_t)((((q >> 1) * 64 + 16 * s + n) * 16) + 8 * (q & 1)), cso, 0);
+        cw[NS][s] = u32x4{v[0], v[1], 0u, 0u};
+        sc[NS][s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(((16 * s + n) * 4 + q) * 2), sso, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first product
+    const mx_v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = v >> 1, pi = v & 1;   // the tail chunk (v = 2 NS) reads words 0, 1 of its own loads
+      const mx_v8i A = mx_act_operand(X[v]);
+      const mx_v4f off = mx_mfma(A, mx_minus_one(), (int)X[v].sa, zero);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4& w = cw[c][s];
+        const mx_v4f o = mx_mfma(A, pi ? mx_weights(w.z, w.w) : mx_weights(w.x, w.y), (int)X[v].sa, off);
+        y[s] = mx_accumulate(o, pi ? sc[c][s] >> 16 : sc[c][s] & 0xFFFFu, y[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) red[wv][s][(lane & 15) * 4 + (lane >> 4)] = y[s];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 64) {
+    // row t: subgroup s = t / 16, row n = t % 16 of it; entries in rank order,
+    // then the shared expert, then the residual
+    const int s = t >> 4, nn = t & 15;
+    float acc = 0.0f;
+    for (int w = 0; w < n_ent; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(&red[w][s][nn * 4]);
+      const float e = ((v.x + v.y) + v.z) + v.w;
+      acc += (w < a.k ? a.gates[(size_t)tok * a.k + w] : 1.0f) * e;
+    }
+    const size_t o = (size_t)tok * a.H + (size_t)rg * 64 + t;
+    if (residual) acc += bf16_to_f32(residual[o]);
+    out[o] = acc;
+    if (out_bf16) out_bf16[o] = (uint16_t)f32_to_bf16_rne(acc);
+  }
+}
+
 bool decode_mx_ok(int H, int I, int q3) { return !q3 && H % 256 == 0 && I % 128 == 0 && H / 256 <= 20 && I <= 1024; }
 
 hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
@@ -309,6 +406,27 @@ hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
       MOE_LAUNCH((k_decode_gateup_mx<10, 2, 16>), grid, dim3(640), 0, s, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                                         hipStream_t s) {
+  const int n_ent = a.k + (a.with_shared ? 1 : 0);
+  dim3 grid(a.T, a.H / 64);
+  if (!decode_down_combine_mx_ok(a.I, a.k, a.with_shared)) return hipErrorInvalidValue;
+#define MOE_DC_MX(W, NS, TL) MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16)
+  const bool small = n_ent <= 11;
+  switch (a.I) {
+    case 512: if (small) MOE_DC_MX(11, 2, 0); else MOE_DC_MX(16, 2, 0); break;
+    case 640: if (small) MOE_DC_MX(11, 2, 1); else MOE_DC_MX(16, 2, 1); break;
+    case 768: if (small) MOE_DC_MX(11, 3, 0); else MOE_DC_MX(16, 3, 0); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DC_MX
+  return hipGetLastError();
+}
+
+bool decode_down_combine_mx_ok(int I, int k, int with_shared) {
+  return (I == 512 || I == 640 || I == 768) && k + (with_shared ? 1 : 0) <= 16;
 }
 
 hipError_t launch_decode_down_mx(const MxFfnArgs& a, hipStream_t s) {

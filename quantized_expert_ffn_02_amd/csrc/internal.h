@@ -150,6 +150,11 @@ struct MxFfnArgs {
 bool decode_mx_ok(int H, int I, int q3);
 hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_down_mx(const MxFfnArgs& a, hipStream_t s);
+// down projection and combine in one launch: a block per token and 64 output
+// rows, a wave per entry (I in {512, 640, 768}, k + 1 <= 16 entries per token)
+bool decode_down_combine_mx_ok(int I, int k, int with_shared);
+hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                                         hipStream_t s);
 hipError_t launch_decode_gateup(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);

@@ -68,9 +68,10 @@ __device__ __forceinline__ float mx_accumulate(const mx_v4f& o, uint32_t scale16
 // (n, q) = (lane % 16, lane / 16) loads the 16 code bytes of row n, 64-column
 // chunk q (blocks 2 q and 2 q + 1) and their two fp16 scales; the first MFMA
 // takes the even blocks (words 0, 1), the second the odd ones (words 2, 3).
-template <int W, int SPW, int VPL>
+template <int W, int SPW, int VPL, int RG = 64>
 __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[W][8][64];
+  constexpr int NSG = RG / 16;   // 16-row subgroups of gate (and of up) per block
+  __shared__ __attribute__((aligned(16))) float red[W][2 * NSG][64];
   __shared__ int s_expert;
   const int r = blockIdx.x, rg = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -122,12 +123,14 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
   const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(M.codes + eidx * M.code_stride, (uint32_t)M.code_stride);
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(M.scales + eidx * M.scale_stride, (uint32_t)(M.scale_stride * 2));
   const int n = lane & 15, q = lane >> 4;
-  const int ng[2] = {rg, rg + a.I / 64};   // gate rows, up rows
+  // this block's RG gate rows (and up rows) start at row ro of 64-row group ng
+  const int ng[2] = {(rg * RG) / 64, (rg * RG) / 64 + a.I / 64};   // gate rows, up rows
+  const int ro = (rg * RG) % 64;
   const int nch64 = K / 64, n128 = K / 128;
 
   // every weight load of this wave, then the products
-  u32x4 cw[SPW][2][4];
-  uint32_t sc[SPW][2][4];
+  u32x4 cw[SPW][2][NSG];
+  uint32_t sc[SPW][2][NSG];
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
     const int c = min(s0 + u, ns - 1);
@@ -136,19 +139,19 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
       const uint32_t cso = (uint32_t)(((size_t)ng[m] * nch64 + 4 * c) * 1024);
       const uint32_t sso = (uint32_t)(((size_t)ng[m] * n128 + 2 * c) * 512);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        cw[u][m][s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(q * 1024 + (16 * s + n) * 16), cso, 0);
+      for (int s = 0; s < NSG; ++s) {
+        cw[u][m][s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(q * 1024 + (ro + 16 * s + n) * 16), cso, 0);
         sc[u][m][s] = __builtin_amdgcn_raw_buffer_load_b32(
-            rs, (uint32_t)(((q >> 1) * 64 + 16 * s + n) * 8 + (q & 1) * 4), sso, 0);
+            rs, (uint32_t)(((q >> 1) * 64 + ro + 16 * s + n) * 8 + (q & 1) * 4), sso, 0);
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first product
-  float y[2][4];
+  float y[2][NSG];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) y[m][s] = 0.0f;
+    for (int s = 0; s < NSG; ++s) y[m][s] = 0.0f;
   const mx_v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < SPW; ++u) {
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NSG; ++s) {
           const u32x4& w = cw[u][m][s];
           const mx_v4f o = mx_mfma(A, pi ? mx_weights(w.z, w.w) : mx_weights(w.x, w.y), (int)X[u][pi].sa, off);
           const float t = mx_accumulate(o, pi ? sc[u][m][s] >> 16 : sc[u][m][s] & 0xFFFFu, y[m][s]);
@@ -173,16 +176,17 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) red[wv][m * 4 + s][(lane & 15) * 4 + (lane >> 4)] = y[m][s];
+    for (int s = 0; s < NSG; ++s) red[wv][m * NSG + s][(lane & 15) * 4 + (lane >> 4)] = y[m][s];
   __syncthreads();
   if (wv == 0) {
-    // row lane of the 64: subgroup s = lane / 16, row n = lane % 16 of it;
-    // waves in order, then the four lane groups in order
-    const int s = lane >> 4, nn = lane & 15;
+    // row lane of the RG: subgroup s = lane / 16, row n = lane % 16 of it;
+    // waves in order, then the four lane groups in order (lanes past RG
+    // repeat rows and store nothing)
+    const int s = (lane >> 4) & (NSG - 1), nn = lane & 15;
     float g = 0.0f, up = 0.0f;
     for (int w = 0; w < W; ++w) {
       const float4 gv = *reinterpret_cast<const float4*>(&red[w][s][nn * 4]);
-      const float4 uv = *reinterpret_cast<const float4*>(&red[w][4 + s][nn * 4]);
+      const float4 uv = *reinterpret_cast<const float4*>(&red[w][NSG + s][nn * 4]);
       g += gv.x;
       g += gv.y;
       g += gv.z;
@@ -193,10 +197,11 @@ __global__ __launch_bounds__(W * 64) void k_decode_gateup_mx(MxFfnArgs a) {
       up += uv.w;
     }
     const float hv = g / (1.0f + expf(-g)) * up;
-    // h row lane of this block is column 64 rg + lane of the entry's h: block
-    // 2 rg + lane / 32 (mixed table form, read by the down kernel), weight
+    // h row lane of this block is column RG rg + lane of the entry's h: block
+    // (RG rg + lane) / 32 (mixed table form, read by the down kernel), weight
     // index lane % 32
-    mx_emit(hv, r, mx_slot_mixed(2 * rg + (lane >> 5), a.I), mx_pos_of_weight(lane & 31), a.I, a.hdata, a.hexps);
+    mx_emit(hv, r, mx_slot_mixed((rg * RG + lane) >> 5, a.I), mx_pos_of_weight(lane & 31), a.I, a.hdata, a.hexps,
+            lane < RG);
   }
 }
 
@@ -390,21 +395,31 @@ __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, 
 
 bool decode_mx_ok(int H, int I, int q3) { return !q3 && H % 256 == 0 && I % 128 == 0 && H / 256 <= 20 && I <= 1024; }
 
+// 32-row blocks when 64-row blocks would leave compute units idle (T = 1, 2).
 hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
   const int entries = a.T * a.k + (a.with_shared ? a.T : 0);
   const int ns = a.H / 256;
-  dim3 grid(entries, a.I / 64);
+  const bool rows32 = entries * (a.I / 64) < 256;
+  dim3 grid(entries, a.I / (rows32 ? 32 : 64));
+#define MOE_GU_MX(SPW, VPL)                                                   \
+  do {                                                                        \
+    if (rows32)                                                               \
+      MOE_LAUNCH((k_decode_gateup_mx<10, SPW, VPL, 32>), grid, dim3(640), 0, s, a); \
+    else                                                                      \
+      MOE_LAUNCH((k_decode_gateup_mx<10, SPW, VPL, 64>), grid, dim3(640), 0, s, a); \
+  } while (0)
   if (ns <= 10) {
     if (a.E <= 512)
-      MOE_LAUNCH((k_decode_gateup_mx<10, 1, 8>), grid, dim3(640), 0, s, a);
+      MOE_GU_MX(1, 8);
     else
-      MOE_LAUNCH((k_decode_gateup_mx<10, 1, 16>), grid, dim3(640), 0, s, a);
+      MOE_GU_MX(1, 16);
   } else {
     if (a.E <= 512)
-      MOE_LAUNCH((k_decode_gateup_mx<10, 2, 8>), grid, dim3(640), 0, s, a);
+      MOE_GU_MX(2, 8);
     else
-      MOE_LAUNCH((k_decode_gateup_mx<10, 2, 16>), grid, dim3(640), 0, s, a);
+      MOE_GU_MX(2, 16);
   }
+#undef MOE_GU_MX
   return hipGetLastError();
 }
 

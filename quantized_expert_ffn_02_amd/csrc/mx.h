@@ -183,11 +183,13 @@ __host__ __device__ constexpr int mx_slot_mixed(int B, int K) { return B < (K / 
 
 // Activation table of this lane's value v (this half wave holds the block in
 // table slot `slot`, this lane position p of the block) in row `row`: pieces
-// and scale bytes.
+// and scale bytes.  Every lane takes part in the block maximum; only lanes
+// with `store` write.
 __device__ __forceinline__ void mx_emit(float v, int row, int slot, int p, int K, uint8_t* __restrict__ data,
-                                        uint8_t* __restrict__ exps) {
+                                        uint8_t* __restrict__ exps, bool store = true) {
   uint32_t pc[kMxPieces], sb[kMxPieces];
   mx_pieces(v, pc, sb);
+  if (!store) return;
   uint8_t* __restrict__ d =
       data + (size_t)row * mx_data_bytes(K) + (size_t)((slot * 2 + (p >> 4)) * kMxPieces) * 16 + (p & 15);
 #pragma unroll

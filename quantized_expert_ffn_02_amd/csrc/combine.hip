@@ -16,7 +16,7 @@ namespace moe {
 // thread waits for one memory round trip per batch instead of one per entry.
 static constexpr int kCombineBatch = 12;
 
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y_sorted,
+__global__ __launch_bounds__(1024) void k_combine(const float* __restrict__ y_sorted,
                                                  const int32_t* __restrict__ row_to_sorted,
                                                  const float* __restrict__ gates, int T, int k, int H,
                                                  int with_shared, const uint16_t* __restrict__ residual,
@@ -73,9 +73,12 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, c
                           int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  dim3 grid((H / 4 + 255) / 256, T);
-  MOE_LAUNCH(k_combine, grid, dim3(256), 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared,
-                     residual, out, out_bf16);
+  // one block per token row when it fits (no partly idle second block)
+  const int threads = ((H / 4 + 63) / 64) * 64;
+  const dim3 block(threads <= 1024 ? threads : 256);
+  dim3 grid((H / 4 + block.x - 1) / block.x, T);
+  MOE_LAUNCH(k_combine, grid, block, 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared, residual, out,
+             out_bf16);
   return hipGetLastError();
 }
 
@@ -83,7 +86,7 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, c
 // path's down GEMM writes them): out[t] = sum_i y16[row_to_sorted[t k + i]]
 // (i = 0..k-1) + y16[row_to_sorted[T k + t]] (+ residual), summed in fp32 in
 // that order.  Eight consecutive outputs per thread.
-__global__ __launch_bounds__(256) void k_combine16(const uint16_t* __restrict__ y16,
+__global__ __launch_bounds__(1024) void k_combine16(const uint16_t* __restrict__ y16,
                                                    const int32_t* __restrict__ row_to_sorted, int T, int k, int H,
                                                    int with_shared, const uint16_t* __restrict__ residual,
                                                    float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
@@ -141,9 +144,11 @@ __global__ __launch_bounds__(256) void k_combine16(const uint16_t* __restrict__ 
 hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,
                             const uint16_t* residual, float* out, uint16_t* out_bf16, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  dim3 grid((H / 8 + 255) / 256, T);
-  MOE_LAUNCH(k_combine16, grid, dim3(256), 0, s, y16, row_to_sorted, T, k, H, with_shared, residual, out,
-             out_bf16);
+  // one block per token row when it fits (no partly idle second block)
+  const int threads = ((H / 8 + 63) / 64) * 64;
+  const dim3 block(threads <= 1024 ? threads : 256);
+  dim3 grid((H / 8 + block.x - 1) / block.x, T);
+  MOE_LAUNCH(k_combine16, grid, block, 0, s, y16, row_to_sorted, T, k, H, with_shared, residual, out, out_bf16);
   return hipGetLastError();
 }
 

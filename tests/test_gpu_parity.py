@@ -166,6 +166,26 @@ def test_layer_forward_parity(workload, T):
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
 
 
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_decode_small_q2_shape(T):
+    # A 2-bit layer of another shape (H = 512, I = 256, 32 experts, top-4 +
+    # shared): the matrix-core gate/up with 32- and 64-row blocks, and the down
+    # projection and combine as two launches (the one-launch form covers
+    # I in {512, 640, 768}).
+    shape = synth.LayerShape(512, 32, 4, 256, True, "q2", None)
+    hl = W.host_layer("decode", shape=shape)
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+    assert_route_matches(ids, gates, hl.logits(x), shape.top_k, f"small q2 T={T}")
+    err = OL.rel_max_err(out, ref)
+    print(f"small q2 T={T}: max|err|/rms = {err:.3e}")
+    assert err <= 1e-4
+    np.testing.assert_allclose(margin, m_r, rtol=0, atol=1e-5)
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
 def test_decode_extreme_activation_blocks():
     # The 2-bit decode path carries each 32-column block of x (and of h) as
     # fixed-point e4m3 pieces against the block's largest magnitude.  Blocks

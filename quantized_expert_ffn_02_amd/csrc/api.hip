@@ -64,6 +64,7 @@ struct Layout {
   size_t xtab_pairs, xtab_init, xf32, xf16, hf16, tiles, n_tiles;
   size_t h, htab_pairs, htab_init, y;
   size_t xmx_data, xmx_exps, hmx_data, hmx_exps;   // fp8-piece tables (mx.h)
+  size_t norm_sq;                                   // partial sums of squares of a stack layer's output
   size_t out_f32, xa, xb, xn;     // stack ping-pong buffers and the normalised layer input
   size_t miss_flag;
   size_t total;
@@ -114,6 +115,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xmx_exps = take(Tm * mx_exps_bytes((int)H));
   o.hmx_data = take(nm * mx_data_bytes((int)I));
   o.hmx_exps = take(nm * mx_exps_bytes((int)I));
+  o.norm_sq = take(Tm * (H / 64) * 4);
   o.out_f32 = take(T * H * 4);
   o.xa = take(T * H * 2);
   o.xb = take(T * H * 2);
@@ -422,9 +424,24 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   return MOE_OK;
 }
 
+// A layer whose decode batch takes the fp8 x fp4 path with the one-launch down
+// and combine: its front end can apply the RMSNorm of its input, and its last
+// launch can leave the partial sums of squares of its output.
+static bool fused_norm_path(const moe_layer_t* L, int T) {
+  const int k = L->top_k, with_shared = has_shared(L) ? 1 : 0;
+  const int n = T * k + (with_shared ? T : 0);
+  return L->routed.fmt == MOE_FMT_Q2 && T <= kDecodeDirectMaxTokens && n <= kSmallRouteMaxEntries &&
+         decode_direct_ok(T, k, with_shared, L->hidden, L->inter) && decode_mx_ok(L->hidden, L->inter, 0) &&
+         decode_down_combine_mx_ok(L->inter, k, with_shared);
+}
+
+// norm_sq_in: x is the layer input before its RMSNorm, with its partial sums of
+// squares ([T][H / 64]); norm_sq_out: write those of out_bf16.  Both only on
+// the fused-norm decode path (fused_norm_path).
 static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
                               float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
-                              void* ws, const Layout& lay, hipStream_t s) {
+                              void* ws, const Layout& lay, hipStream_t s, const float* norm_sq_in = nullptr,
+                              float* norm_sq_out = nullptr) {
   const int k = L->top_k, E = L->n_experts;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
@@ -457,6 +474,8 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
       a.xinit = nullptr;
       a.xmx_data = at<uint8_t>(ws, lay.xmx_data);
       a.xmx_exps = at<uint8_t>(ws, lay.xmx_exps);
+      a.norm_sq = norm_sq_in;
+      a.norm_eps = MOE_RMS_EPS;
       MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_front(a, s); }));
       MxFfnArgs m;
       m.r13 = mat_w13(L->routed);
@@ -484,7 +503,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
       if (decode_down_combine_mx_ok(L->inter, k, with_shared)) {
         // down projection and combine in one launch (a block per token and 64 rows)
         MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s,
-                      [&] { return launch_decode_down_combine_mx(m, residual, out, out_bf16, s); }));
+                      [&] { return launch_decode_down_combine_mx(m, residual, out, out_bf16, norm_sq_out, s); }));
         return MOE_OK;
       }
       MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] { return launch_decode_down_mx(m, s); }));
@@ -618,14 +637,30 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
   if (!ws || reinterpret_cast<uintptr_t>(ws) % kAlign || ws_bytes < need) return MOE_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   const uint16_t* cur = x0;
+  // On the fused-norm decode path a layer leaves the partial sums of squares of
+  // its output, and the next layer's front end applies the RMSNorm as it loads
+  // x (no separate norm launch); otherwise the norm runs on its own.
+  bool have_sq = false;
+  size_t sq_off = 0;
   for (int l = 0; l < n_layers; ++l) {
     const Layout lay = make_layout(&layers[l], T);
     uint16_t* nxt = (l == n_layers - 1) ? x_out : at<uint16_t>(ws, (l % 2) ? lay.xb : lay.xa);
     float* of = (l == n_layers - 1 && out_last) ? out_last : at<float>(ws, lay.out_f32);
-    uint16_t* xn = at<uint16_t>(ws, lay.xn);
-    MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
-    rc = layer_forward_impl(&layers[l], xn, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s);
+    const bool fused = fused_norm_path(&layers[l], T);
+    const bool norm_in = have_sq && fused && lay.norm_sq == sq_off;
+    const bool norm_out = fused && l + 1 < n_layers;
+    float* sq = at<float>(ws, lay.norm_sq);
+    const uint16_t* lin = cur;
+    if (!norm_in) {
+      uint16_t* xn = at<uint16_t>(ws, lay.xn);
+      MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
+      lin = xn;
+    }
+    rc = layer_forward_impl(&layers[l], lin, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s,
+                            norm_in ? sq : nullptr, norm_out ? sq : nullptr);
     if (rc) return rc;
+    have_sq = norm_out;
+    sq_off = lay.norm_sq;
     cur = nxt;
   }
   return MOE_OK;

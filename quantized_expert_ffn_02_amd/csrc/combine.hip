@@ -168,6 +168,29 @@ __device__ __forceinline__ float block_sum_fixed(float v, float* part, int nw) {
   return tot;
 }
 
+// Rows of H = 64 G columns (G <= 64): one block per row, wave w takes the
+// 64-column groups w, w + W, ... (lane = column); group sums and the scale by
+// rms_group_sum / rms_inv_from_groups (device.h), the definition the fused
+// stack path uses; output rounded to bf16 (nearest even).
+__global__ __launch_bounds__(1024) void k_rmsnorm_bf16_g64(const uint16_t* __restrict__ x, int H, float eps,
+                                                           uint16_t* __restrict__ out) {
+  __shared__ float part[64];
+  const int row = blockIdx.x, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int G = H / 64;
+  const uint16_t* __restrict__ xr = x + (size_t)row * H;
+  for (int g = w; g < G; g += nw) {
+    const float s = rms_group_sum(bf16_to_f32(xr[64 * g + lane]));
+    if (lane == 0) part[g] = s;
+  }
+  __syncthreads();
+  const float inv = rms_inv_from_groups(lane < G ? part[lane] : 0.0f, H, eps);
+  for (int g = w; g < G; g += nw) {
+    const __bf16 o = (__bf16)(bf16_to_f32(xr[64 * g + lane]) * inv);
+    out[(size_t)row * H + 64 * g + lane] = __builtin_bit_cast(uint16_t, o);
+  }
+}
+
 __global__ __launch_bounds__(1024) void k_rmsnorm_bf16_v8(const uint16_t* __restrict__ x, int H, float eps,
                                                           uint16_t* __restrict__ out) {
   __shared__ float part[16];
@@ -211,7 +234,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const uint16_t* __restrict
 
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (H % 8 == 0 && H <= 8192) {
+  if (H % 64 == 0 && H / 64 <= 64) {
+    const int G = H / 64;
+    MOE_LAUNCH(k_rmsnorm_bf16_g64, dim3(T), dim3(64 * (G < 16 ? G : 16)), 0, s, x, H, eps, out);
+  } else if (H % 8 == 0 && H <= 8192) {
     const int threads = ((H / 8 + 63) / 64) * 64;
     MOE_LAUNCH(k_rmsnorm_bf16_v8, dim3(T), dim3(threads), 0, s, x, H, eps, out);
   } else {

@@ -22,30 +22,17 @@
 
 namespace moe {
 
-// Sum over the 64 lanes in a fixed order (wave-uniform result): DPP adds
-// inside each 16-lane row (quad exchanges, then rotations by 4 and 8), then
-// the four row sums in row order.
-__device__ __forceinline__ float wave_sum_rows(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));    // quad_perm 1,0,3,2
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));    // quad_perm 2,3,0,1
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));   // row_ror 4
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));   // row_ror 8
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return ((r0 + r1) + r2) + r3;
-}
-
 // logits of expert row e for tokens [t0, t0 + TB): the row's NC 16-byte chunks
 // per lane and the matching x chunks of all TB tokens are loaded before any
 // arithmetic (one memory round trip per call).  Loads past the row or past T
 // read a clamped address (no branch around a load); their products are zeroed
-// or not stored.
+// or not stored.  With norm_sq, x is the layer input before its RMSNorm: each
+// token's chunks are scaled by its row_inv_rms and rounded to bf16 first.
 template <int TB, int NC>
 __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T, int t0,
                                            const uint16_t* __restrict__ wr, float b, int E, int H, int e,
-                                           float* __restrict__ logits) {
+                                           float* __restrict__ logits, const float* __restrict__ norm_sq = nullptr,
+                                           float eps = 0.0f) {
   const int lane = threadIdx.x & 63;
   const uint4* __restrict__ wrow = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
   const int nch = H / 8;
@@ -60,6 +47,19 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T
 #pragma unroll
   for (int u = 0; u < NC; ++u)
     if (lane + 64 * u >= nch) w[u] = make_uint4(0u, 0u, 0u, 0u);
+  if (norm_sq) {
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const float inv = row_inv_rms(norm_sq, min(t0 + i, T - 1), H, eps);
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        xv[i][u].x = bf16x2_scale(xv[i][u].x, inv);
+        xv[i][u].y = bf16x2_scale(xv[i][u].y, inv);
+        xv[i][u].z = bf16x2_scale(xv[i][u].z, inv);
+        xv[i][u].w = bf16x2_scale(xv[i][u].w, inv);
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
     float a = 0.0f;
@@ -79,17 +79,19 @@ __device__ __forceinline__ void router_row(const uint16_t* __restrict__ x, int T
 template <int NC>
 __device__ __forceinline__ void router_row_all(const uint16_t* __restrict__ x, int T,
                                                const uint16_t* __restrict__ wr, float b, int E, int H, int e,
-                                               float* __restrict__ logits) {
-  for (int t0 = 0; t0 < T; t0 += 4) router_row<4, NC>(x, T, t0, wr, b, E, H, e, logits);
+                                               float* __restrict__ logits, const float* __restrict__ norm_sq,
+                                               float eps) {
+  for (int t0 = 0; t0 < T; t0 += 4) router_row<4, NC>(x, T, t0, wr, b, E, H, e, logits, norm_sq, eps);
 }
 
 __device__ __forceinline__ void router_row_dispatch(const uint16_t* __restrict__ x, int T,
                                                     const uint16_t* __restrict__ wr, float b, int E, int H, int e,
-                                                    float* __restrict__ logits) {
+                                                    float* __restrict__ logits,
+                                                    const float* __restrict__ norm_sq = nullptr, float eps = 0.0f) {
   if (H <= 2560)
-    router_row_all<5>(x, T, wr, b, E, H, e, logits);
+    router_row_all<5>(x, T, wr, b, E, H, e, logits, norm_sq, eps);
   else
-    router_row_all<8>(x, T, wr, b, E, H, e, logits);
+    router_row_all<8>(x, T, wr, b, E, H, e, logits, norm_sq, eps);
 }
 
 // Router GEMV for any T: one wave per expert row, tokens 4 at a time.
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void k_route_front(SmallRouteArgs a) {
     const int e = blockIdx.x * 4 + wv;
     if (e < a.E) {
       const float b = a.bias ? a.bias[e] : 0.0f;
-      router_row_dispatch(a.x, a.T, a.wr, b, a.E, a.H, e, a.logits);
+      router_row_dispatch(a.x, a.T, a.wr, b, a.E, a.H, e, a.logits, a.norm_sq, a.norm_eps);
     }
     return;
   }
@@ -133,9 +135,10 @@ __global__ __launch_bounds__(256) void k_route_front(SmallRouteArgs a) {
     for (int base = (blockIdx.x - rblocks) * 256; base < items; base += tblocks * 256) {
       const int it = base + tid;
       if (it < items) {
-        const int row = it / a.H, col = it - row * a.H;
+        const int row = it / a.H, col = it - row * a.H;   // a wave's 64 elements lie in one row
         const int B = col >> 5, p = col & 31;
-        const float v = bf16_to_f32(a.x[(size_t)row * a.H + 32 * B + mx_weight_at(p)]);
+        float v = bf16_to_f32(a.x[(size_t)row * a.H + 32 * B + mx_weight_at(p)]);
+        if (a.norm_sq) v = (float)(__bf16)(v * row_inv_rms(a.norm_sq, row, a.H, a.norm_eps));
         mx_emit(v, row, mx_slot256(B), p, a.H, a.xmx_data, a.xmx_exps);
       }
     }

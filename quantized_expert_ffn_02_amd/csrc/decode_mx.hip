@@ -304,7 +304,8 @@ __global__ __launch_bounds__((NS + TAIL) * 64) void k_decode_down_mx(MxFfnArgs a
 template <int W, int NS, int TAIL>
 __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, const uint16_t* __restrict__ residual,
                                                                   float* __restrict__ out,
-                                                                  uint16_t* __restrict__ out_bf16) {
+                                                                  uint16_t* __restrict__ out_bf16,
+                                                                  float* __restrict__ sq_out) {
   constexpr int NV = 2 * NS + TAIL;   // activation chunks of K
   __shared__ __attribute__((aligned(16))) float red[W][4][64];
   const int tok = blockIdx.x, rg = blockIdx.y;
@@ -389,7 +390,13 @@ __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, 
     const size_t o = (size_t)tok * a.H + (size_t)rg * 64 + t;
     if (residual) acc += bf16_to_f32(residual[o]);
     out[o] = acc;
-    if (out_bf16) out_bf16[o] = (uint16_t)f32_to_bf16_rne(acc);
+    const uint32_t ob = f32_to_bf16_rne(acc);
+    if (out_bf16) out_bf16[o] = (uint16_t)ob;
+    if (sq_out) {
+      // wave 0 holds the block's 64 rows: the sum of squares of their bf16 values
+      const float sq = rms_group_sum(bf16_to_f32(ob));
+      if (t == 0) sq_out[(size_t)tok * (a.H / 64) + rg] = sq;
+    }
   }
 }
 
@@ -424,11 +431,12 @@ hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
-                                         hipStream_t s) {
+                                         float* sq_out, hipStream_t s) {
   const int n_ent = a.k + (a.with_shared ? 1 : 0);
   dim3 grid(a.T, a.H / 64);
   if (!decode_down_combine_mx_ok(a.I, a.k, a.with_shared)) return hipErrorInvalidValue;
-#define MOE_DC_MX(W, NS, TL) MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16)
+#define MOE_DC_MX(W, NS, TL) \
+  MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16, sq_out)
   const bool small = n_ent <= 11;
   switch (a.I) {
     case 512: if (small) MOE_DC_MX(11, 2, 0); else MOE_DC_MX(16, 2, 0); break;

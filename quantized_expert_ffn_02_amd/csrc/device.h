@@ -52,6 +52,52 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over the 64 lanes in a fixed order (wave-uniform result): DPP adds
+// inside each 16-lane row (quad exchanges, then rotations by 4 and 8), then
+// the four row sums in row order.
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));    // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));    // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));   // row_ror 4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));   // row_ror 8
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+// RMSNorm of a bf16 row, one definition for every kernel that computes it:
+// the squares of a 64-column group (lane = column, rounded squares, no
+// contraction into the adds) summed by wave_sum_rows; the group sums
+// (lane = group, G = H / 64 <= 64) summed the same way; then
+// 1 / sqrt(sum / H + eps).  The fused stack path gets the same bits as the
+// standalone norm.
+__device__ __forceinline__ float rms_group_sum(float v) {
+#pragma clang fp contract(off)
+  const float sq = v * v;
+  return wave_sum_rows(sq);
+}
+__device__ __forceinline__ float rms_inv_from_groups(float group_sum_or_zero, int H, float eps) {
+#pragma clang fp contract(off)
+  return 1.0f / sqrtf(wave_sum_rows(group_sum_or_zero) / (float)H + eps);
+}
+
+// RMSNorm scale of row t from its group sums sq[t * G + g]; wave-uniform, every
+// lane must call.
+__device__ __forceinline__ float row_inv_rms(const float* __restrict__ sq, int t, int H, float eps) {
+  const int lane = threadIdx.x & 63, G = H / 64;
+  return rms_inv_from_groups(lane < G ? sq[(size_t)t * G + lane] : 0.0f, H, eps);
+}
+
+typedef __bf16 moe_bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two bf16 values (one u32) times s, rounded to bf16 (nearest even).
+__device__ __forceinline__ uint32_t bf16x2_scale(uint32_t w, float s) {
+  const moe_bf16x2_t r = {(__bf16)(bf16_to_f32(w & 0xFFFFu) * s), (__bf16)(bf16_to_f32(w >> 16) * s)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, MOE_WAVE);

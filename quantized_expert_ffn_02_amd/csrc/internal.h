@@ -97,6 +97,10 @@ struct SmallRouteArgs {
   float* xinit;
   uint8_t* xmx_data = nullptr;   // fp8-piece activation table (mx.h; NULL: not built)
   uint8_t* xmx_exps = nullptr;
+  // x before its RMSNorm: per-row partial sums of squares over 64-column groups
+  // ([T][H / 64]) and eps; every use of x applies the norm (NULL: x is used as is)
+  const float* norm_sq = nullptr;
+  float norm_eps = 0.0f;
   int32_t* ids;
   float* gates;
   float* margin;       // may be NULL
@@ -153,8 +157,10 @@ hipError_t launch_decode_down_mx(const MxFfnArgs& a, hipStream_t s);
 // down projection and combine in one launch: a block per token and 64 output
 // rows, a wave per entry (I in {512, 640, 768}, k + 1 <= 16 entries per token)
 bool decode_down_combine_mx_ok(int I, int k, int with_shared);
+// sq_out (may be NULL): partial sums of squares of the bf16 output per token and
+// 64 rows ([T][H / 64]), the next layer's RMSNorm input
 hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
-                                         hipStream_t s);
+                                         float* sq_out, hipStream_t s);
 hipError_t launch_decode_gateup(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);

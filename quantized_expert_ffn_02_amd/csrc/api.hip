@@ -388,9 +388,11 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
 // tile plan, x -> fp16 pair order, gate/up, down, combine.  In expert-cache
 // mode ``routed`` is the slot pool and ``slot_map`` maps routed groups to pool
 // slots (-1: a miss, whose rows contribute zero).
+// x_f16_ready: the workspace's fp16 pair-order copy of x is already written.
 static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int32_t* slot_map, const uint16_t* x,
                        int32_t T, const uint16_t* residual, float* out, uint16_t* out_bf16, int32_t* ids,
-                       float* gates, float* margin, void* ws, const Layout& lay, hipStream_t s) {
+                       float* gates, float* margin, void* ws, const Layout& lay, hipStream_t s,
+                       bool x_f16_ready = false) {
   const int k = L->top_k, E = L->n_experts, H = L->hidden, I = L->inter;
   const int with_shared = has_shared(L) ? 1 : 0;
   const int n = T * k + (with_shared ? T : 0);
@@ -411,7 +413,7 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   uint16_t* xf = at<uint16_t>(ws, lay.xf16);
   uint16_t* hf = at<uint16_t>(ws, lay.hf16);
   float* y = at<float>(ws, lay.y);
-  MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
+  if (!x_f16_ready) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
                           nullptr, nullptr, kSmallTileRows, q3, slot_map);
@@ -422,6 +424,12 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   }));
   MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
   return MOE_OK;
+}
+
+// A batch between a decode step and a prompt chunk on the 32-row grouped GEMM.
+static bool medium_path_taken(const moe_layer_t* L, int T) {
+  return T > kDecodeDirectMaxTokens && gemm_shape_ok(L->hidden, L->inter) &&
+         ((L->routed.fmt == MOE_FMT_Q2 && T < 1024) || L->routed.fmt == MOE_FMT_Q3);
 }
 
 // A layer whose decode batch takes the fp8 x fp4 path with the one-launch down
@@ -441,7 +449,7 @@ static bool fused_norm_path(const moe_layer_t* L, int T) {
 static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
                               float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
                               void* ws, const Layout& lay, hipStream_t s, const float* norm_sq_in = nullptr,
-                              float* norm_sq_out = nullptr) {
+                              float* norm_sq_out = nullptr, bool x_f16_ready = false) {
   const int k = L->top_k, E = L->n_experts;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
@@ -553,9 +561,9 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     MOE_TRY(launch_decode_combine(d, s));
     return MOE_OK;
   }
-  if (T > kDecodeDirectMaxTokens && gemm_shape_ok(L->hidden, L->inter) &&
-      ((L->routed.fmt == MOE_FMT_Q2 && T < 1024) || L->routed.fmt == MOE_FMT_Q3))
-    return medium_path(L, L->routed, nullptr, x, T, residual, out, out_bf16, ids, gates, margin, ws, lay, s);
+  if (medium_path_taken(L, T))
+    return medium_path(L, L->routed, nullptr, x, T, residual, out, out_bf16, ids, gates, margin, ws, lay, s,
+                       x_f16_ready);
   if (n <= kSmallRouteMaxEntries) {
     // decode / MTP-verify batch: router, activation table, top-k and permutation in one launch
     SmallRouteArgs a;
@@ -651,13 +659,19 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
     const bool norm_out = fused && l + 1 < n_layers;
     float* sq = at<float>(ws, lay.norm_sq);
     const uint16_t* lin = cur;
+    // on the 32-row GEMM path the norm also writes the GEMM's fp16 copy of its output
+    const bool f16 = !norm_in && medium_path_taken(&layers[l], T) && layers[l].routed.fmt != MOE_FMT_BF16 &&
+                     rmsnorm_f16_pairs_ok(layers[l].hidden);
     if (!norm_in) {
       uint16_t* xn = at<uint16_t>(ws, lay.xn);
-      MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
+      if (f16)
+        MOE_TRY(launch_rmsnorm_bf16_f16pairs(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, at<uint16_t>(ws, lay.xf16), s));
+      else
+        MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
       lin = xn;
     }
     rc = layer_forward_impl(&layers[l], lin, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s,
-                            norm_in ? sq : nullptr, norm_out ? sq : nullptr);
+                            norm_in ? sq : nullptr, norm_out ? sq : nullptr, f16);
     if (rc) return rc;
     have_sq = norm_out;
     sq_off = lay.norm_sq;

@@ -172,8 +172,10 @@ __device__ __forceinline__ float block_sum_fixed(float v, float* part, int nw) {
 // 64-column groups w, w + W, ... (lane = column); group sums and the scale by
 // rms_group_sum / rms_inv_from_groups (device.h), the definition the fused
 // stack path uses; output rounded to bf16 (nearest even).
+// f16p (may be NULL): also the fp16 copy of the output in pair order (u32 j of
+// each 16-column group = columns j and j + 8, the grouped GEMM's A layout).
 __global__ __launch_bounds__(1024) void k_rmsnorm_bf16_g64(const uint16_t* __restrict__ x, int H, float eps,
-                                                           uint16_t* __restrict__ out) {
+                                                           uint16_t* __restrict__ out, uint32_t* __restrict__ f16p) {
   __shared__ float part[64];
   const int row = blockIdx.x, lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -188,6 +190,12 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_bf16_g64(const uint16_t* __res
   for (int g = w; g < G; g += nw) {
     const __bf16 o = (__bf16)(bf16_to_f32(xr[64 * g + lane]) * inv);
     out[(size_t)row * H + 64 * g + lane] = __builtin_bit_cast(uint16_t, o);
+    if (f16p) {
+      // column + 8 of the same 16-column group: rotate the 16-lane row by 8
+      const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(float)o);
+      const uint32_t h8 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x128, 0xF, 0xF, true);
+      if ((lane & 15) < 8) f16p[((size_t)row * H + 64 * g + lane) / 16 * 8 + (lane & 7)] = h | (h8 << 16);
+    }
   }
 }
 
@@ -236,13 +244,26 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint1
   if (T <= 0) return hipSuccess;
   if (H % 64 == 0 && H / 64 <= 64) {
     const int G = H / 64;
-    MOE_LAUNCH(k_rmsnorm_bf16_g64, dim3(T), dim3(64 * (G < 16 ? G : 16)), 0, s, x, H, eps, out);
+    MOE_LAUNCH(k_rmsnorm_bf16_g64, dim3(T), dim3(64 * (G < 16 ? G : 16)), 0, s, x, H, eps, out,
+               (uint32_t*)nullptr);
   } else if (H % 8 == 0 && H <= 8192) {
     const int threads = ((H / 8 + 63) / 64) * 64;
     MOE_LAUNCH(k_rmsnorm_bf16_v8, dim3(T), dim3(threads), 0, s, x, H, eps, out);
   } else {
     MOE_LAUNCH(k_rmsnorm_bf16, dim3(T), dim3(256), 0, s, x, H, eps, out);
   }
+  return hipGetLastError();
+}
+
+bool rmsnorm_f16_pairs_ok(int H) { return H % 64 == 0 && H / 64 <= 64; }
+
+hipError_t launch_rmsnorm_bf16_f16pairs(const uint16_t* x, int T, int H, float eps, uint16_t* out, uint16_t* f16p,
+                                        hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!rmsnorm_f16_pairs_ok(H)) return hipErrorInvalidValue;
+  const int G = H / 64;
+  MOE_LAUNCH(k_rmsnorm_bf16_g64, dim3(T), dim3(64 * (G < 16 ? G : 16)), 0, s, x, H, eps, out,
+             reinterpret_cast<uint32_t*>(f16p));
   return hipGetLastError();
 }
 

@@ -167,6 +167,11 @@ hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);
 
 // ---- launchers (return hipGetLastError()) ----
 hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s);
+// RMSNorm that also writes the fp16 pair-order copy of its output (the grouped
+// GEMM's activation layout), for H = 64 G, G <= 64
+bool rmsnorm_f16_pairs_ok(int H);
+hipError_t launch_rmsnorm_bf16_f16pairs(const uint16_t* x, int T, int H, float eps, uint16_t* out, uint16_t* f16p,
+                                        hipStream_t s);
 
 hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s);

@@ -303,9 +303,90 @@ def bench_cache(steps):
            "layer_us": ms * 1e3, "tokens_per_s": T / (ms * 1e-3), "hit_rate": 1 - float(nm.mean()) / (T * k),
            "algorithmic_MB_per_call": gb / 1e6, "GBps": gb / (ms * 1e-3) / 1e9,
            "hbm_frac": gb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    res["tiered"] = bench_tiered(layers, pool, d_slot, xs, ws, wl)
     del layers, pool
     torch.cuda.empty_cache()
     return res
+
+
+def bench_tiered(layers, pool, d_slot, xs, ws, wl, rounds=25, tier_layers=(0, 12, 24, 36)):
+    """The cache workload's layers with the misses computed on the host (moe_layer_forward_tiered):
+    every routed expert of 4 layers held in host memory; the host kernel also timed alone on the
+    same miss lists.  Host wall-clock per call, each call ending in a stream synchronisation."""
+    import time
+
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    banks = {l: synth.bank(wl.seed, l, s.fmt, range(E), H, I) for l in tier_layers}
+    hb = {l: B.make_host_bank(s.fmt, E, H, I, banks[l]) for l in tier_layers}
+    out = torch.empty((wl.tokens[0], H), dtype=torch.float32, device="cuda")
+    res = {"host_layers": list(tier_layers), "host_bank_GB_per_layer": sum(v.nbytes for v in banks[0].values()) / 1e9,
+           "isa": {2: "avx512", 1: "avx2"}.get(B.cpu_isa(), "none"), "threads": min(16, os.cpu_count() or 1),
+           "cpu": _cpu_model()}
+    for T in (wl.tokens[0], 4):
+        xt = [x[:T].contiguous() for x in xs]
+        host_ws = torch.empty(B.tiered_host_bytes(layers[0].struct, T), dtype=torch.uint8, pin_memory=True)
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        miss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        nmiss = torch.empty(1, dtype=torch.int32, device="cuda")
+
+        def tiered(l, j):
+            B.layer_forward_tiered(layers[l].struct, l, wl.layers, d_slot, pool.struct, hb[l], xt[j % len(xt)], T,
+                                   out, ids, gates, miss, nmiss, ws, host_ws)
+
+        def cached(l, j):
+            B.layer_forward_cached(layers[l].struct, l, wl.layers, d_slot, pool.struct, xt[j % len(xt)], T, out,
+                                   ids, gates, miss, nmiss, ws)
+
+        # the miss lists of every (layer, batch) pair, for the host kernel alone
+        lists = []
+        for j, l in enumerate(tier_layers):
+            cached(l, j)
+            torch.cuda.synchronize()
+            nm = int(nmiss.cpu()[0])
+            lists.append((l, xt[j % len(xt)].cpu().numpy(), ids.cpu().numpy(), gates.cpu().numpy(),
+                          miss.cpu().numpy()[:nm].copy()))
+        timings = {}
+        for name, fn in (("tiered", tiered), ("cached", cached)):
+            for j, l in enumerate(tier_layers):
+                fn(l, j)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            n = 0
+            for _ in range(rounds):
+                for j, l in enumerate(tier_layers):
+                    fn(l, j)
+                    torch.cuda.synchronize()
+                    n += 1
+            timings[name] = (time.perf_counter() - t0) / n
+        y = np.empty((T, H), dtype=np.float32)
+        t0 = time.perf_counter()
+        for _ in range(rounds):
+            for (l, x, i_, g_, rows) in lists:
+                B.cpu_expert_ffn(hb[l], x, T, k, i_, g_, rows, len(rows), y)
+        cpu_s = (time.perf_counter() - t0) / (rounds * len(lists))
+        misses = float(np.mean([len(t[4]) for t in lists]))
+        res[f"T{T}"] = {"tiered_us": timings["tiered"] * 1e6, "cached_gpu_us": timings["cached"] * 1e6,
+                        "host_kernel_us": cpu_s * 1e6, "misses_per_call": misses,
+                        "host_Gweights_per_s": misses * 3 * H * I / cpu_s / 1e9 if misses else None}
+    return res
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():

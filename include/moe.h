@@ -192,6 +192,55 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                              int32_t* miss_rows, int32_t* n_miss,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Host miss tier (first page, section "How a 125B model fits in 12 GB": every expert
+ * is also held in system RAM, and the CPU computes a selected expert the GPU cache
+ * lacks at the same time as the GPU computes the cached ones; the aireport.net page
+ * names AVX-512 and AVX2 kernels for it).
+ *
+ * moe_cpu_expert_ffn takes HOST pointers only and makes no HIP call.  bank: a Q2 or
+ * Q3 bank (layout as above) in host memory.  x bf16 [T x H]; ids int32 [T*k] and
+ * gates fp32 [T*k] as the router writes them; rows int32 [n_rows]: entries
+ * r = t*k + i, strictly ascending, each below T*k (a miss list).  y fp32 [T x H] is
+ * overwritten: y[t] = sum over the listed entries r of token t, in ascending r, of
+ * gates[r] * FFN_{ids[r]}(x[t]); tokens with no listed entry get zero rows.
+ * n_threads: worker threads (0: the smaller of 16 and the host's hardware threads).
+ * Arithmetic: fp32 on AVX-512 where the CPU has AVX-512F/BW/VL/DQ, else AVX2 + FMA.
+ * The result does not depend on n_threads.  Blocks until done; concurrent calls
+ * are serialised.  MOE_EINVAL for bad arguments (unsorted rows, an id outside the
+ * bank), MOE_EUNSUPPORTED for a bf16 bank or a CPU without AVX2. */
+int moe_cpu_expert_ffn(const moe_bank_t* bank, const uint16_t* x, int32_t T, int32_t k,
+                       const int32_t* ids, const float* gates, const int32_t* rows, int32_t n_rows,
+                       float* y, int32_t n_threads);
+
+/* Instruction set moe_cpu_expert_ffn uses on this CPU: 2 AVX-512, 1 AVX2, 0 none. */
+int moe_cpu_isa(void);
+
+/* Host bytes of the staging area moe_layer_forward_tiered needs for T tokens
+ * (0 for invalid shapes). */
+size_t moe_tiered_host_bytes(const moe_layer_t* L, int32_t T);
+
+/* Tiered layer: the whole layer, with the cached experts on the GPU and the misses
+ * on the host CPU, overlapped (same passage as moe_cpu_expert_ffn).  Arguments as
+ * moe_layer_forward_cached, plus host_bank (all E routed experts of this layer in
+ * host memory, the format of slot_pool), host_ws (at least moe_tiered_host_bytes
+ * of pinned host memory, e.g. from hipHostMalloc) and n_threads (as above).
+ * Order of work: routing and the miss list on the GPU; their copy to host_ws; the
+ * cached experts, shared expert and combine on the GPU while the host computes the
+ * misses with moe_cpu_expert_ffn; the misses' sum copied back and added.  On return
+ * out (device, after the stream's work) = the full layer: every selected expert and
+ * the shared expert; miss_rows / n_miss hold the miss list as in
+ * moe_layer_forward_cached.  Blocks the calling thread until the miss sum has been
+ * computed and its upload and add are enqueued; not capturable into a graph.  The
+ * miss sum is staged in the workspace; host_ws must not be shared by overlapping
+ * calls. */
+int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers,
+                             const int32_t* slot_of, const moe_bank_t* slot_pool,
+                             const moe_bank_t* host_bank, const uint16_t* x, int32_t T, float* out,
+                             int32_t* topk_ids, float* topk_gates,
+                             int32_t* miss_rows, int32_t* n_miss,
+                             void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
+                             int32_t n_threads, void* stream);
+
 /* Measurement support.  Arms start_event / stop_event (hipEvent_t, created by
  * the caller) for the NEXT launch of the named kernel by any call above, then
  * forgets them (one-shot).  The events are attached to that kernel's dispatch

@@ -50,6 +50,12 @@ _SIGS = {
     "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_forward_cached": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank), _vp,
                                                 _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_cpu_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Bank), _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _i32]),
+    "moe_cpu_isa": (ctypes.c_int, []),
+    "moe_tiered_host_bytes": (_sz, [ctypes.POINTER(Layer), _i32]),
+    "moe_layer_forward_tiered": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank),
+                                                ctypes.POINTER(Bank), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                                _vp, _sz, _i32, _vp]),
     "moe_time_next_launch": (ctypes.c_int, [_i32, _vp, _vp]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -178,6 +184,46 @@ def layer_forward_cached(layer, layer_idx, n_layers, slot_of, slot_pool, x, T, o
         ctypes.byref(layer), int(layer_idx), int(n_layers), ptr(slot_of), ctypes.byref(slot_pool), ptr(x), int(T),
         ptr(out), ptr(topk_ids), ptr(topk_gates), ptr(miss_rows), ptr(n_miss), ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def hptr(a):
+    """Host address of a numpy array or CPU tensor, or None for None."""
+    if a is None:
+        return None
+    return a.ctypes.data if hasattr(a, "ctypes") else a.data_ptr()
+
+
+def make_host_bank(fmt, n_experts, hidden, inter, tensors):
+    """Bank struct over host arrays (dict with w13, w13_scale, w2, w2_scale and, for q3, w13_hi, w2_hi)."""
+    f = FMT_BY_NAME[fmt] if isinstance(fmt, str) else fmt
+    g = tensors.get
+    return Bank(f, n_experts, hidden, inter, hptr(g("w13")), hptr(g("w13_hi")), hptr(g("w13_scale")), hptr(g("w2")),
+                hptr(g("w2_hi")), hptr(g("w2_scale")))
+
+
+def cpu_isa():
+    return int(lib().moe_cpu_isa())
+
+
+def cpu_expert_ffn(bank, x, T, k, topk_ids, topk_gates, rows, n_rows, y, n_threads=0):
+    """Host call: every array is host memory (numpy or CPU tensor)."""
+    _check("moe_cpu_expert_ffn", lib().moe_cpu_expert_ffn(
+        ctypes.byref(bank), hptr(x), int(T), int(k), hptr(topk_ids), hptr(topk_gates), hptr(rows), int(n_rows),
+        hptr(y), int(n_threads)))
+
+
+def tiered_host_bytes(layer, T):
+    return int(lib().moe_tiered_host_bytes(ctypes.byref(layer), int(T)))
+
+
+def layer_forward_tiered(layer, layer_idx, n_layers, slot_of, slot_pool, host_bank, x, T, out, topk_ids, topk_gates,
+                         miss_rows, n_miss, ws, host_ws, n_threads=0, stream=None):
+    """host_ws: pinned CPU tensor of at least tiered_host_bytes(layer, T) bytes."""
+    _check("moe_layer_forward_tiered", lib().moe_layer_forward_tiered(
+        ctypes.byref(layer), int(layer_idx), int(n_layers), ptr(slot_of), ctypes.byref(slot_pool),
+        ctypes.byref(host_bank), ptr(x), int(T), ptr(out), ptr(topk_ids), ptr(topk_gates), ptr(miss_rows),
+        ptr(n_miss), ptr(ws), ws.numel() * ws.element_size(), hptr(host_ws),
+        host_ws.numel() * host_ws.element_size(), int(n_threads), _stream(stream)))
 
 
 def time_next_launch(kernel, start_event, stop_event):

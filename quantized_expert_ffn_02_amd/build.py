@@ -45,18 +45,56 @@ def _compile(src):
     return obj, noise
 
 
+# Host (CPU) sources, built with the host compiler.  host_ffn.cpp is built once per
+# instruction set; the library picks one at run time.
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-psabi", "-I", os.path.join(ROOT, "include")]
+HOST_ISAS = {
+    "avx512": ["-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512dq", "-mavx2", "-mfma", "-mf16c"],
+    "avx2": ["-mavx2", "-mfma", "-mf16c"],
+}
+
+
+def _cxx():
+    return os.environ.get("CXX") or "g++"
+
+
+def _compile_host(job):
+    src, isa = job
+    tag = os.path.basename(src) + (f".{isa}" if isa else "")
+    obj = os.path.join(OBJ, tag + ".o")
+    cmd = [_cxx()] + HOST_FLAGS + ["-pthread", "-c", src, "-o", obj]
+    if isa:
+        cmd[1:1] = HOST_ISAS[isa] + [f"-DMOE_HOST_ISA_NS={isa}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = [ln for ln in (r.stderr or "").splitlines() if ln.strip()]
+    if r.returncode != 0:
+        raise RuntimeError(f"{_cxx()} failed on {src}:\n" + "\n".join(noise))
+    return obj, noise
+
+
+def _host_jobs():
+    jobs = []
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
+        if os.path.basename(src) == "host_ffn.cpp":
+            jobs += [(src, isa) for isa in HOST_ISAS]
+        else:
+            jobs.append((src, None))
+    return jobs
+
+
 def build(verbose=False):
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
-        results = list(ex.map(_compile, srcs))
+        hosts = ex.map(_compile_host, _host_jobs())
+        results = list(ex.map(_compile, srcs)) + list(hosts)
     objs = []
     for obj, noise in results:
         objs.append(obj)
         if verbose and noise:
             print("\n".join(noise), file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

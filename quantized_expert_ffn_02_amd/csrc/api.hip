@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 
 #include "internal.h"
 #include "mx.h"
@@ -389,10 +390,11 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
 // mode ``routed`` is the slot pool and ``slot_map`` maps routed groups to pool
 // slots (-1: a miss, whose rows contribute zero).
 // x_f16_ready: the workspace's fp16 pair-order copy of x is already written.
+// after_route (optional) enqueues work that needs only the routing (ids, gates).
 static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int32_t* slot_map, const uint16_t* x,
                        int32_t T, const uint16_t* residual, float* out, uint16_t* out_bf16, int32_t* ids,
                        float* gates, float* margin, void* ws, const Layout& lay, hipStream_t s,
-                       bool x_f16_ready = false) {
+                       bool x_f16_ready = false, const std::function<int()>* after_route = nullptr) {
   const int k = L->top_k, E = L->n_experts, H = L->hidden, I = L->inter;
   const int with_shared = has_shared(L) ? 1 : 0;
   const int n = T * k + (with_shared ? T : 0);
@@ -401,6 +403,7 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
   int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
   if (rc) return rc;
+  if (after_route && (rc = (*after_route)())) return rc;
   int32_t* chunks = at<int32_t>(ws, lay.tiles);
   int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
   MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
@@ -680,10 +683,14 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
   return MOE_OK;
 }
 
-int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers, const int32_t* slot_of,
-                             const moe_bank_t* slot_pool, const uint16_t* x, int32_t T, float* out,
-                             int32_t* topk_ids, float* topk_gates, int32_t* miss_rows, int32_t* n_miss, void* ws,
-                             size_t ws_bytes, void* stream) {
+// Expert-cache layer.  The miss list is enqueued right after the routing, then
+// after_route (optional: the tiered layer's copy of the routing to the host), then
+// the cached experts, the shared expert and the combine.
+static int cached_layer(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers, const int32_t* slot_of,
+                        const moe_bank_t* slot_pool, const uint16_t* x, int32_t T, float* out, int32_t* topk_ids,
+                        float* topk_gates, int32_t* miss_rows, int32_t* n_miss, void* ws, size_t ws_bytes,
+                        hipStream_t s, const std::function<int()>* after_route, const int32_t** ids_out = nullptr,
+                        const float** gates_out = nullptr) {
   int rc = check_shape(L);
   if (rc) return rc;
   if (!L->w_router || !slot_of || !slot_pool || !x || !out || !miss_rows || !n_miss || T <= 0) return MOE_EINVAL;
@@ -700,10 +707,11 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   Lc.routed.n_experts = L->n_experts;
   const Layout lay = make_layout(&Lc, T);
   if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
-  hipStream_t s = (hipStream_t)stream;
   const int k = L->top_k, E = L->n_experts;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
+  if (ids_out) *ids_out = ids;
+  if (gates_out) *gates_out = gates;
   const int with_shared = has_shared(L) ? 1 : 0;
   const int n = T * k + (with_shared ? T : 0);
   int32_t* offsets = at<int32_t>(ws, lay.offsets);
@@ -712,12 +720,13 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   int32_t* items = at<int32_t>(ws, lay.items);
   int32_t* n_items = at<int32_t>(ws, lay.n_items);
   const int32_t* slot_map = slot_of + (size_t)layer_idx * E;
-  if (T > kDecodeDirectMaxTokens && gemm_shape_ok(L->hidden, L->inter)) {
-    rc = medium_path(&Lc, *slot_pool, slot_map, x, T, nullptr, out, nullptr, ids, gates, nullptr, ws, lay, s);
-    if (rc) return rc;
+  const std::function<int()> routed = [&]() -> int {
     MOE_TRY(launch_miss_list(ids, T * k, slot_map, miss_rows, n_miss, s));
-    return MOE_OK;
-  }
+    return after_route ? (*after_route)() : MOE_OK;
+  };
+  if (T > kDecodeDirectMaxTokens && gemm_shape_ok(L->hidden, L->inter))
+    return medium_path(&Lc, *slot_pool, slot_map, x, T, nullptr, out, nullptr, ids, gates, nullptr, ws, lay, s,
+                       false, &routed);
   bool x_table_ready = false;
   if (n <= kSmallRouteMaxEntries) {
     SmallRouteArgs a;
@@ -751,20 +760,116 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                                 at<int32_t>(ws, lay.base), 0x7FFFFFFF, items_per_for(T), gemm_tile_rows(),
                                 at<int32_t>(ws, lay.tiles), at<int32_t>(ws, lay.n_tiles), items, n_items, s));
   }
+  if ((rc = routed())) return rc;
   PermRef perm;
   perm.offsets = offsets;
   perm.sorted_rows = srt;
   perm.items = items;
   perm.n_items = n_items;
-  perm.slot_map = slot_of + (size_t)layer_idx * E;
+  perm.slot_map = slot_map;
   perm.T = T;
   perm.k = k;
   perm.E = E;
   float* y = at<float>(ws, lay.y);
   rc = do_expert_ffn(&Lc, x, T, perm, n, y, ws, lay, s, x_table_ready);
   if (rc) return rc;
-  MOE_TRY(launch_miss_list(ids, T * k, perm.slot_map, miss_rows, n_miss, s));
   MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, nullptr, out, nullptr, s));
+  return MOE_OK;
+}
+
+int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers, const int32_t* slot_of,
+                             const moe_bank_t* slot_pool, const uint16_t* x, int32_t T, float* out,
+                             int32_t* topk_ids, float* topk_gates, int32_t* miss_rows, int32_t* n_miss, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return cached_layer(L, layer_idx, n_layers, slot_of, slot_pool, x, T, out, topk_ids, topk_gates, miss_rows, n_miss,
+                      ws, ws_bytes, (hipStream_t)stream, nullptr);
+}
+
+// Host staging of the tiered layer: x, ids, gates, miss rows and count copied from
+// the device, then the miss sum computed on the host.
+struct HostStage {
+  size_t x, ids, gates, rows, n_rows, y, total;
+};
+
+static HostStage host_stage(const moe_layer_t* L, int64_t T) {
+  const int64_t k = L->top_k, H = L->hidden;
+  HostStage h;
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p = align_up(p + bytes);
+    return at;
+  };
+  h.x = take(T * H * 2);
+  h.ids = take(T * k * 4);
+  h.gates = take(T * k * 4);
+  h.rows = take(T * k * 4);
+  h.n_rows = take(4);
+  h.y = take(T * H * 4);
+  h.total = p;
+  return h;
+}
+
+size_t moe_tiered_host_bytes(const moe_layer_t* L, int32_t T) {
+  if (check_shape(L) || T <= 0) return 0;
+  return host_stage(L, T).total;
+}
+
+int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_layers, const int32_t* slot_of,
+                             const moe_bank_t* slot_pool, const moe_bank_t* host_bank, const uint16_t* x, int32_t T,
+                             float* out, int32_t* topk_ids, float* topk_gates, int32_t* miss_rows, int32_t* n_miss,
+                             void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes, int32_t n_threads,
+                             void* stream) {
+  int rc = check_shape(L);
+  if (rc) return rc;
+  if (!host_bank || !host_ws || T <= 0 || n_threads < 0) return MOE_EINVAL;
+  if (!slot_pool) return MOE_EINVAL;
+  if ((rc = check_bank(*host_bank, L->n_experts, L->hidden, L->inter))) return rc;
+  if (host_bank->fmt != slot_pool->fmt) return MOE_EUNSUPPORTED;
+  if (host_bank->fmt == MOE_FMT_BF16) return MOE_EUNSUPPORTED;
+  if (moe_cpu_isa() == 0) return MOE_EUNSUPPORTED;
+  const HostStage hs = host_stage(L, T);
+  if (host_ws_bytes < hs.total || ((uintptr_t)host_ws & (kAlign - 1))) return MOE_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = L->top_k, H = L->hidden;
+  char* hb = (char*)host_ws;
+  hipEvent_t routed_ev = nullptr;
+  const int32_t* ids = nullptr;
+  const float* gates = nullptr;
+  // after the routing and the miss list: their copy to the host, then an event the host waits on
+  const std::function<int()> to_host = [&]() -> int {
+    MOE_TRY(hipMemcpyAsync(hb + hs.x, x, (size_t)T * H * 2, hipMemcpyDeviceToHost, s));
+    MOE_TRY(hipMemcpyAsync(hb + hs.ids, ids, (size_t)T * k * 4, hipMemcpyDeviceToHost, s));
+    MOE_TRY(hipMemcpyAsync(hb + hs.gates, gates, (size_t)T * k * 4, hipMemcpyDeviceToHost, s));
+    MOE_TRY(hipMemcpyAsync(hb + hs.rows, miss_rows, (size_t)T * k * 4, hipMemcpyDeviceToHost, s));
+    MOE_TRY(hipMemcpyAsync(hb + hs.n_rows, n_miss, 4, hipMemcpyDeviceToHost, s));
+    MOE_TRY(hipEventCreateWithFlags(&routed_ev, hipEventDisableTiming));
+    MOE_TRY(hipEventRecord(routed_ev, s));
+    return MOE_OK;
+  };
+  rc = cached_layer(L, layer_idx, n_layers, slot_of, slot_pool, x, T, out, topk_ids, topk_gates, miss_rows, n_miss,
+                    ws, ws_bytes, s, &to_host, &ids, &gates);
+  if (rc) {
+    if (routed_ev) (void)hipEventDestroy(routed_ev);
+    return rc;
+  }
+  // the GPU runs the cached experts meanwhile
+  const hipError_t werr = hipEventSynchronize(routed_ev);
+  (void)hipEventDestroy(routed_ev);
+  if (werr != hipSuccess) return MOE_EHIP;
+  const int32_t nm = *(const int32_t*)(hb + hs.n_rows);
+  if (nm <= 0) return MOE_OK;
+  float* hy = (float*)(hb + hs.y);
+  rc = moe_cpu_expert_ffn(host_bank, (const uint16_t*)(hb + hs.x), T, k, (const int32_t*)(hb + hs.ids),
+                          (const float*)(hb + hs.gates), (const int32_t*)(hb + hs.rows), nm, hy, n_threads);
+  if (rc) return rc;
+  // stage the miss sum in the workspace's expert-output area (free once the combine has run)
+  moe_layer_t Lc = *L;
+  Lc.routed = *slot_pool;
+  Lc.routed.n_experts = L->n_experts;
+  float* dy = at<float>(ws, make_layout(&Lc, T).y);
+  MOE_TRY(hipMemcpyAsync(dy, hy, (size_t)T * H * 4, hipMemcpyHostToDevice, s));
+  MOE_TRY(launch_add_f32(out, dy, (size_t)T * H, s));
   return MOE_OK;
 }
 

@@ -6,6 +6,8 @@
 // the same on every run, the property the pages report for the engine's
 // releases (page "Strata: a 125B AI model on your gaming PC", section "What is
 // new in Strata 0.1.45": byte-identical answers).
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -275,6 +277,32 @@ hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s) {
   const size_t n = bytes / 4;
   const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
   MOE_LAUNCH(k_fill_zero, dim3(blocks), dim3(256), 0, s, (uint32_t*)ws, n);
+  return hipGetLastError();
+}
+
+// out[i] += y[i] for i < n (the tiered layer adds the host-computed miss sum to the
+// GPU's hits + shared output).  float4 for the bulk, scalars for a tail.
+__global__ __launch_bounds__(256) void k_add_f32(float* __restrict__ out, const float* __restrict__ y, size_t n) {
+  const size_t n4 = n / 4;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    float4 a = reinterpret_cast<float4*>(out)[i];
+    const float4 b = reinterpret_cast<const float4*>(y)[i];
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+    reinterpret_cast<float4*>(out)[i] = a;
+  }
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) out[i] += y[i];
+}
+
+hipError_t launch_add_f32(float* out, const float* y, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (((uintptr_t)out | (uintptr_t)y) & 15) return hipErrorInvalidValue;
+  const size_t want = (n / 4 + 255) / 256;
+  const unsigned blocks = (unsigned)std::min<size_t>(std::max<size_t>(want, 1), 2048);
+  MOE_LAUNCH(k_add_f32, dim3(blocks), dim3(256), 0, s, out, y, n);
   return hipGetLastError();
 }
 

@@ -246,6 +246,9 @@ bool gemm_shape_ok(int H, int I);
 hipError_t launch_miss_list(const int32_t* ids, int Tk, const int32_t* slot_map, int32_t* miss_rows, int32_t* n_miss,
                             hipStream_t s);
 
+// out[i] += y[i], i < n (both 16-byte aligned)
+hipError_t launch_add_f32(float* out, const float* y, size_t n, hipStream_t s);
+
 hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint16_t* out, hipStream_t s);
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,

@@ -74,3 +74,60 @@ def test_cached_layer(pool, layer):
     hits = T * k - nm
     print(f"cache layer {layer}: hits {hits}/{T * k}, max|err|/rms = {err:.3e}")
     assert err <= OUT_TOL
+
+
+def _tiered(pool, layer, T, slot_of):
+    """Tiered layer through the C ABI with the full host bank of the layer, and the oracle's full layer."""
+    _, hpool, dpool = pool
+    w = synth.CONFIGS["cache"]
+    s = w.shape
+    k, E, H, I = s.top_k, s.n_experts, s.hidden, s.inter
+    hl = W.cache_layer("cache", layer, hpool)
+    x, _ = W.activations_with_margin(hl, T)
+    full = synth.bank(w.seed, layer, s.fmt, range(E), H, I)     # every routed expert of the layer, host memory
+    hbank = B.make_host_bank(s.fmt, E, H, I, full)
+    sb = DeviceBank(s.fmt, 1, H, I, hl.shared)
+    dl = DeviceLayer(H, E, k, I, hl.wr, hl.bias, dpool, sb)
+    ws = dl.workspace(T)
+    host_ws = torch.empty(B.tiered_host_bytes(dl.struct, T), dtype=torch.uint8, pin_memory=True)
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    n_miss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    print(f"tiered layer {layer} T={T}", flush=True)
+    B.layer_forward_tiered(dl.struct, layer, w.layers, to_device(slot_of), dpool.struct, hbank, to_device(x), T, out,
+                           ids, gates, miss, n_miss, ws, host_ws)
+    torch.cuda.synchronize()
+    smat = OF.expert_matrices(s.fmt, hl.shared, H, I)
+    ref, ids_r, gates_r, _ = OL.layer_forward(x, hl.wr, k, OL.bank_expert_fn(s.fmt, full, H, I), lambda: smat,
+                                              bias=hl.bias)
+    assert_route_matches(host(ids), host(gates), hl.logits(x), k, f"tiered layer {layer}")
+    nm = int(host(n_miss)[0])
+    want = np.flatnonzero(slot_of[layer][ids_r.reshape(-1)] < 0).astype(np.int32)
+    assert nm == len(want)
+    np.testing.assert_array_equal(host(miss)[:nm], want)
+    err = OL.rel_max_err(host(out), ref)
+    print(f"tiered layer {layer} T={T}: misses {nm}/{T * k} on the host, max|err|/rms = {err:.3e}")
+    assert err <= OUT_TOL
+    return nm
+
+
+@pytest.mark.parametrize("layer,T", [(0, 64), (17, 4), (47, 1)])
+def test_tiered_layer(pool, layer, T):
+    # hits on the GPU + misses on the host CPU = the oracle's full layer
+    _tiered(pool, layer, T, pool[0])
+
+
+def test_tiered_layer_mostly_misses(pool):
+    # only the 8 most popular experts of the layer keep their slots: most entries go to the host
+    slot_of = pool[0].copy()
+    layer = 5
+    row = slot_of[layer]
+    cached = np.flatnonzero(row >= 0)
+    keep = cached[np.argsort(row[cached])[:8]]                # slots are given in order of popularity
+    cut = np.full_like(row, -1)
+    cut[keep] = row[keep]
+    slot_of[layer] = cut
+    nm = _tiered(pool, layer, 8, slot_of)
+    assert nm >= 8 * 10 // 4                                  # Zipf routing: the top 8 still take over half

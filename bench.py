@@ -322,11 +322,12 @@ def bench_tiered(layers, pool, d_slot, xs, ws, wl, rounds=25, tier_layers=(0, 12
     from quantized_expert_ffn_02_amd import binding as B
     s = wl.shape
     H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    threads = max(1, min(16, os.cpu_count() or 1) * 3 // 4)   # the library's default
     banks = {l: synth.bank(wl.seed, l, s.fmt, range(E), H, I) for l in tier_layers}
     hb = {l: B.make_host_bank(s.fmt, E, H, I, banks[l]) for l in tier_layers}
     out = torch.empty((wl.tokens[0], H), dtype=torch.float32, device="cuda")
     res = {"host_layers": list(tier_layers), "host_bank_GB_per_layer": sum(v.nbytes for v in banks[0].values()) / 1e9,
-           "isa": {2: "avx512", 1: "avx2"}.get(B.cpu_isa(), "none"), "threads": min(16, os.cpu_count() or 1),
+           "isa": {2: "avx512", 1: "avx2"}.get(B.cpu_isa(), "none"), "threads": threads,
            "cpu": _cpu_model()}
     for T in (wl.tokens[0], 4):
         xt = [x[:T].contiguous() for x in xs]
@@ -338,7 +339,7 @@ def bench_tiered(layers, pool, d_slot, xs, ws, wl, rounds=25, tier_layers=(0, 12
 
         def tiered(l, j):
             B.layer_forward_tiered(layers[l].struct, l, wl.layers, d_slot, pool.struct, hb[l], xt[j % len(xt)], T,
-                                   out, ids, gates, miss, nmiss, ws, host_ws)
+                                   out, ids, gates, miss, nmiss, ws, host_ws, threads)
 
         def cached(l, j):
             B.layer_forward_cached(layers[l].struct, l, wl.layers, d_slot, pool.struct, xt[j % len(xt)], T, out,
@@ -369,7 +370,7 @@ def bench_tiered(layers, pool, d_slot, xs, ws, wl, rounds=25, tier_layers=(0, 12
         t0 = time.perf_counter()
         for _ in range(rounds):
             for (l, x, i_, g_, rows) in lists:
-                B.cpu_expert_ffn(hb[l], x, T, k, i_, g_, rows, len(rows), y)
+                B.cpu_expert_ffn(hb[l], x, T, k, i_, g_, rows, len(rows), y, threads)
         cpu_s = (time.perf_counter() - t0) / (rounds * len(lists))
         misses = float(np.mean([len(t[4]) for t in lists]))
         res[f"T{T}"] = {"tiered_us": timings["tiered"] * 1e6, "cached_gpu_us": timings["cached"] * 1e6,

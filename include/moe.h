@@ -24,8 +24,11 @@
  *
  * Conventions for every call
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors)
- *     owned by the caller; structs (moe_layer_t, moe_bank_t) live in host memory
- *     and are read during the call only.  bf16 / fp16 values travel as uint16_t
+ *     owned by the caller, except in the host miss tier (moe_cpu_expert_ffn and
+ *     moe_layer_forward_tiered), which says which of its arguments live in host
+ *     memory and is the one part that blocks and is not capturable; structs
+ *     (moe_layer_t, moe_bank_t) live in host memory and are read during the call
+ *     only.  bf16 / fp16 values travel as uint16_t
  *     bit patterns.  Row-major unless stated.
  *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue kernels and
  *     return without synchronising; they allocate nothing and call no memset, so
@@ -203,7 +206,7 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
  * r = t*k + i, strictly ascending, each below T*k (a miss list).  y fp32 [T x H] is
  * overwritten: y[t] = sum over the listed entries r of token t, in ascending r, of
  * gates[r] * FFN_{ids[r]}(x[t]); tokens with no listed entry get zero rows.
- * n_threads: worker threads (0: the smaller of 16 and the host's hardware threads).
+ * n_threads: worker threads (0: three quarters of min(16, the host's hardware threads)).
  * Arithmetic: fp32 on AVX-512 where the CPU has AVX-512F/BW/VL/DQ, else AVX2 + FMA.
  * The result does not depend on n_threads.  Blocks until done; concurrent calls
  * are serialised.  MOE_EINVAL for bad arguments (unsorted rows, an id outside the

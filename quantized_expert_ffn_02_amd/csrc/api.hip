@@ -785,28 +785,23 @@ int moe_layer_forward_cached(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                       ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 
-// Host staging of the tiered layer: x, ids, gates, miss rows and count copied from
-// the device, then the miss sum computed on the host.
+// Host staging of the tiered layer: x, ids, gates, miss rows and their count back
+// to back (4-byte aligned; one copy from the device), then the miss sum.
 struct HostStage {
-  size_t x, ids, gates, rows, n_rows, y, total;
+  size_t x, ids, gates, rows, n_rows, packed, y, total;
 };
 
 static HostStage host_stage(const moe_layer_t* L, int64_t T) {
   const int64_t k = L->top_k, H = L->hidden;
   HostStage h;
-  size_t p = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = p;
-    p = align_up(p + bytes);
-    return at;
-  };
-  h.x = take(T * H * 2);
-  h.ids = take(T * k * 4);
-  h.gates = take(T * k * 4);
-  h.rows = take(T * k * 4);
-  h.n_rows = take(4);
-  h.y = take(T * H * 4);
-  h.total = p;
+  h.x = 0;
+  h.ids = h.x + T * H * 2;
+  h.gates = h.ids + T * k * 4;
+  h.rows = h.gates + T * k * 4;
+  h.n_rows = h.rows + T * k * 4;
+  h.packed = h.n_rows + 4;
+  h.y = align_up(h.packed);
+  h.total = h.y + T * H * 4;
   return h;
 }
 
@@ -823,6 +818,7 @@ int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   int rc = check_shape(L);
   if (rc) return rc;
   if (!host_bank || !host_ws || T <= 0 || n_threads < 0) return MOE_EINVAL;
+  if ((uintptr_t)x & 3) return MOE_EINVAL;   // copied to the host as 4-byte words
   if (!slot_pool) return MOE_EINVAL;
   if ((rc = check_bank(*host_bank, L->n_experts, L->hidden, L->inter))) return rc;
   if (host_bank->fmt != slot_pool->fmt) return MOE_EUNSUPPORTED;
@@ -836,13 +832,27 @@ int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   hipEvent_t routed_ev = nullptr;
   const int32_t* ids = nullptr;
   const float* gates = nullptr;
-  // after the routing and the miss list: their copy to the host, then an event the host waits on
+  // The workspace's expert-output area stages the packed routing (before the cached
+  // experts write it) and later the miss sum (after the combine has read it); the
+  // stream orders both.  It holds T(k+1)H floats, more than the packed bytes.
+  moe_layer_t Lc = *L;
+  Lc.routed = *slot_pool;
+  Lc.routed.n_experts = L->n_experts;
+  float* dy = at<float>(ws, make_layout(&Lc, T).y);
+  // after the routing and the miss list: one copy of them (and x) to the host, then an
+  // event the host waits on
   const std::function<int()> to_host = [&]() -> int {
-    MOE_TRY(hipMemcpyAsync(hb + hs.x, x, (size_t)T * H * 2, hipMemcpyDeviceToHost, s));
-    MOE_TRY(hipMemcpyAsync(hb + hs.ids, ids, (size_t)T * k * 4, hipMemcpyDeviceToHost, s));
-    MOE_TRY(hipMemcpyAsync(hb + hs.gates, gates, (size_t)T * k * 4, hipMemcpyDeviceToHost, s));
-    MOE_TRY(hipMemcpyAsync(hb + hs.rows, miss_rows, (size_t)T * k * 4, hipMemcpyDeviceToHost, s));
-    MOE_TRY(hipMemcpyAsync(hb + hs.n_rows, n_miss, 4, hipMemcpyDeviceToHost, s));
+    PackWords pw;
+    pw.src[0] = (const uint32_t*)x;
+    pw.words[0] = (uint32_t)((size_t)T * H / 2);
+    pw.src[1] = (const uint32_t*)ids;
+    pw.src[2] = (const uint32_t*)gates;
+    pw.src[3] = (const uint32_t*)miss_rows;
+    pw.words[1] = pw.words[2] = pw.words[3] = (uint32_t)(T * k);
+    pw.src[4] = (const uint32_t*)n_miss;
+    pw.words[4] = 1;
+    MOE_TRY(launch_pack_words(pw, (uint32_t*)dy, s));
+    MOE_TRY(hipMemcpyAsync(hb, dy, hs.packed, hipMemcpyDeviceToHost, s));
     MOE_TRY(hipEventCreateWithFlags(&routed_ev, hipEventDisableTiming));
     MOE_TRY(hipEventRecord(routed_ev, s));
     return MOE_OK;
@@ -863,11 +873,6 @@ int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_
   rc = moe_cpu_expert_ffn(host_bank, (const uint16_t*)(hb + hs.x), T, k, (const int32_t*)(hb + hs.ids),
                           (const float*)(hb + hs.gates), (const int32_t*)(hb + hs.rows), nm, hy, n_threads);
   if (rc) return rc;
-  // stage the miss sum in the workspace's expert-output area (free once the combine has run)
-  moe_layer_t Lc = *L;
-  Lc.routed = *slot_pool;
-  Lc.routed.n_experts = L->n_experts;
-  float* dy = at<float>(ws, make_layout(&Lc, T).y);
   MOE_TRY(hipMemcpyAsync(dy, hy, (size_t)T * H * 4, hipMemcpyHostToDevice, s));
   MOE_TRY(launch_add_f32(out, dy, (size_t)T * H, s));
   return MOE_OK;

@@ -306,4 +306,27 @@ hipError_t launch_add_f32(float* out, const float* y, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Word ranges gathered back to back into dst (the tiered layer copies its routing
+// and x to the host in one transfer).
+__global__ __launch_bounds__(256) void k_pack_words(PackWords p, uint32_t* __restrict__ dst) {
+  uint32_t total = 0;
+  for (int s = 0; s < PackWords::kMax; ++s) total += p.words[s];
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    uint32_t off = i;
+    int s = 0;
+    while (s < PackWords::kMax - 1 && off >= p.words[s]) off -= p.words[s++];
+    dst[i] = p.src[s][off];
+  }
+}
+
+hipError_t launch_pack_words(const PackWords& p, uint32_t* dst, hipStream_t s) {
+  size_t total = 0;
+  for (int i = 0; i < PackWords::kMax; ++i) total += p.words[i];
+  if (total == 0) return hipSuccess;
+  if (total > 0xFFFFFFFFu) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 1024);
+  MOE_LAUNCH(k_pack_words, dim3(blocks), dim3(256), 0, s, p, dst);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -6,17 +6,20 @@
 // Work of one call, entries r = t*k + i of the miss list:
 //   1. group the entries by expert (ascending expert id, entries ascending within);
 //   2. reorder each token's activations for the row dot (act_pos order);
-//   3. gate/up: per (expert, 16 rows of I), a = Wg x and b = Wu x for every token of
+//   3. gate/up: per (expert, 8 rows of I), a = Wg x and b = Wu x for every token of
 //      the group, h = SiLU(a) * b;
-//   4. down: per (expert, 64 rows of H), z_r = Wd h_r for every entry of the group;
+//   4. down: per (expert, 32 rows of H), z_r = Wd h_r for every entry of the group;
 //   5. y[t] = sum over t's entries in ascending r of gate[r] * z_r (zero if none).
 // Each output is computed by one thread in a fixed order, so the result does not
 // depend on the thread count.
 #include <stdint.h>
 #include <string.h>
 
+#include <immintrin.h>
+
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <functional>
@@ -58,15 +61,19 @@ Kernels kernels() {
 
 // Persistent workers; run(units, fn) calls fn(u) for every u < units across the
 // workers and the calling thread (dynamic assignment) and returns when all are done.
+// Idle workers poll for new work for up to kSpinMicros before they sleep, so the
+// barriers between the phases of a call, and calls that follow each other closely
+// (one per layer), do not pay a sleeping thread's wake-up.
 class Pool {
  public:
+  static constexpr int kSpinMicros = 50;
   explicit Pool(int n) : n_(n) {
     for (int i = 1; i < n; ++i) th_.emplace_back([this] { worker(); });
   }
   ~Pool() {
     {
       std::lock_guard<std::mutex> g(mu_);
-      stop_ = true;
+      stop_.store(true);
     }
     cv_.notify_all();
     for (auto& t : th_) t.join();
@@ -78,52 +85,60 @@ class Pool {
       for (int u = 0; u < units; ++u) fn(u);
       return;
     }
+    fn_ = &fn;
+    units_ = units;
+    next_.store(0, std::memory_order_relaxed);
+    busy_.store((int)th_.size(), std::memory_order_relaxed);
     {
-      std::lock_guard<std::mutex> g(mu_);
-      fn_ = &fn;
-      units_ = units;
-      next_.store(0);
-      busy_ = (int)th_.size();
-      ++gen_;
+      std::lock_guard<std::mutex> g(mu_);   // a worker checks gen_ under the lock before it sleeps
+      gen_.fetch_add(1, std::memory_order_release);
     }
     cv_.notify_all();
     drain();
-    std::unique_lock<std::mutex> lk(mu_);
-    done_.wait(lk, [&] { return busy_ == 0; });
+    while (busy_.load(std::memory_order_acquire) != 0) _mm_pause();
     fn_ = nullptr;
   }
 
  private:
   void drain() {
     for (;;) {
-      const int u = next_.fetch_add(1);
+      const int u = next_.fetch_add(1, std::memory_order_relaxed);
       if (u >= units_) return;
       (*fn_)(u);
     }
   }
+  // Returns false when the pool is being destroyed.
+  bool wait_for_work(uint64_t seen) {
+    const auto until = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinMicros);
+    for (int i = 0;; ++i) {
+      if (gen_.load(std::memory_order_acquire) != seen) return true;
+      if (stop_.load(std::memory_order_relaxed)) return false;
+      _mm_pause();
+      if ((i & 63) == 63 && std::chrono::steady_clock::now() > until) break;
+    }
+    std::unique_lock<std::mutex> lk(mu_);
+    cv_.wait(lk, [&] { return stop_.load() || gen_.load(std::memory_order_acquire) != seen; });
+    return !stop_.load();
+  }
   void worker() {
     uint64_t seen = 0;
     for (;;) {
-      {
-        std::unique_lock<std::mutex> lk(mu_);
-        cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
-        if (stop_) return;
-        seen = gen_;
-      }
+      if (!wait_for_work(seen)) return;
+      seen = gen_.load(std::memory_order_acquire);
       drain();
-      std::lock_guard<std::mutex> g(mu_);
-      if (--busy_ == 0) done_.notify_one();
+      busy_.fetch_sub(1, std::memory_order_release);
     }
   }
   const int n_;
   std::vector<std::thread> th_;
   std::mutex mu_;
-  std::condition_variable cv_, done_;
+  std::condition_variable cv_;
   const std::function<void(int)>* fn_ = nullptr;
-  int units_ = 0, busy_ = 0;
-  uint64_t gen_ = 0;
-  bool stop_ = false;
+  int units_ = 0;
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<int> busy_{0};
   std::atomic<int> next_{0};
+  std::atomic<bool> stop_{false};
 };
 
 // One call at a time: the pool and the scratch buffers are shared.
@@ -131,9 +146,12 @@ std::mutex g_call;
 std::unique_ptr<Pool> g_pool;
 std::vector<float> g_xp, g_hp, g_z;
 
+// Three quarters of the hardware threads, at most 12: the HIP runtime's own threads
+// and the caller's GPU work need cores too (with 16 threads on a 16-thread share the
+// tiered layer ran no faster than with 12).
 int default_threads() {
   const unsigned hw = std::thread::hardware_concurrency();
-  return (int)std::max(1u, std::min(16u, hw ? hw : 1u));
+  return (int)std::max(1u, std::min(16u, hw ? hw : 1u) * 3 / 4);
 }
 
 HostMat expert_mat(const moe_bank_t& b, bool w13, int e) {
@@ -150,8 +168,8 @@ HostMat expert_mat(const moe_bank_t& b, bool w13, int e) {
 
 float silu(float a) { return a / (1.0f + std::exp(-a)); }
 
-constexpr int kGateRows = 16;   // rows of I per gate/up unit
-constexpr int kDownRows = 64;   // rows of H per down unit
+constexpr int kGateRows = 8;    // rows of I per gate/up unit
+constexpr int kDownRows = 32;   // rows of H per down unit
 constexpr int kSumCols = 256;   // columns of H per final-sum unit
 
 }  // namespace

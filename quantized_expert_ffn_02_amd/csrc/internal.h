@@ -246,6 +246,15 @@ bool gemm_shape_ok(int H, int I);
 hipError_t launch_miss_list(const int32_t* ids, int Tk, const int32_t* slot_map, int32_t* miss_rows, int32_t* n_miss,
                             hipStream_t s);
 
+// Up to kMax word ranges (src[i], words[i]; unused ranges have 0 words) copied back
+// to back into dst.
+struct PackWords {
+  static constexpr int kMax = 5;
+  const uint32_t* src[kMax] = {};
+  uint32_t words[kMax] = {};
+};
+hipError_t launch_pack_words(const PackWords& p, uint32_t* dst, hipStream_t s);
+
 // out[i] += y[i], i < n (both 16-byte aligned)
 hipError_t launch_add_f32(float* out, const float* y, size_t n, hipStream_t s);
 

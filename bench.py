@@ -256,12 +256,17 @@ def bench_cache(steps):
     s = wl.shape
     H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
     T = wl.tokens[0]
-    slot_of = synth.hot_slot_table(wl.seed, wl.layers, E, wl.slots_per_layer)
+    # One pool serves every slot budget: each layer's `stride` most popular experts, layer-major; a budget's
+    # slot table maps a prefix of each layer's run (the pages' 1,589 and 3,872, and this workload's 3,072).
+    budgets = {n: synth.budget_per_layer(wl.layers, n) for n in synth.CACHE_SLOT_BUDGETS}
+    stride = int(max(int(p.max()) for p in budgets.values()))
+    tables = {n: synth.budget_slot_table(wl.seed, wl.layers, E, p, stride=stride) for n, p in budgets.items()}
+    slot_of = tables[wl.slots]
     parts = []
     for l in range(wl.layers):
-        order = np.argsort(synth.zipf_ranks(wl.seed, l, E))[:wl.slots_per_layer]
-        parts.append(synth.bank(wl.seed, l, s.fmt, order, H, I))
-    pool = DeviceBank(s.fmt, wl.slots, H, I, {n: np.concatenate([p[n] for p in parts]) for n in parts[0]})
+        order = np.argsort(synth.zipf_ranks(wl.seed, l, E))[:stride]
+        parts.append(synth.bank(wl.seed, l, s.fmt, order, H, I, workers=16))
+    pool = DeviceBank(s.fmt, wl.layers * stride, H, I, {n: np.concatenate([p[n] for p in parts]) for n in parts[0]})
     del parts
     layers = []
     for l in range(wl.layers):
@@ -303,6 +308,29 @@ def bench_cache(steps):
            "layer_us": ms * 1e3, "tokens_per_s": T / (ms * 1e-3), "hit_rate": 1 - float(nm.mean()) / (T * k),
            "algorithmic_MB_per_call": gb / 1e6, "GBps": gb / (ms * 1e-3) / 1e9,
            "hbm_frac": gb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    res["slot_budgets"] = {}
+    for nb, table in tables.items():
+        dt = to_device(table)
+        for l in range(wl.layers):
+            B.layer_forward_cached(layers[l].struct, l, wl.layers, dt, pool.struct, xs[l % 8], T, out, ids[l], None,
+                                   miss, nmiss[l:l + 1], ws)
+        torch.cuda.synchronize()
+        ids_b, nm_b = ids.cpu().numpy(), nmiss.cpu().numpy()
+        mb = float(np.mean([E * H * 2 + E * 4 + (int((table[l][np.unique(ids_b[l])] >= 0).sum()) + 1) *
+                            q3_expert_bytes(H, I) for l in range(wl.layers)]))
+        t0.record()
+        n = 0
+        for _ in range(steps):
+            for l in range(wl.layers):
+                B.layer_forward_cached(layers[l].struct, l, wl.layers, dt, pool.struct, xs[l % 8], T, out, None,
+                                       None, miss, nmiss[l:l + 1], ws)
+                n += 1
+        t1.record()
+        torch.cuda.synchronize()
+        msb = t0.elapsed_time(t1) / n
+        res["slot_budgets"][str(nb)] = {
+            "slots": nb, "cache_GB": nb * q3_expert_bytes(H, I) / 1e9, "hit_rate": 1 - float(nm_b.mean()) / (T * k),
+            "layer_us": msb * 1e3, "algorithmic_MB_per_call": mb / 1e6, "GBps": mb / (msb * 1e-3) / 1e9}
     res["tiered"] = bench_tiered(layers, pool, d_slot, xs, ws, wl)
     del layers, pool
     torch.cuda.empty_cache()
@@ -379,6 +407,53 @@ def bench_tiered(layers, pool, d_slot, xs, ws, wl, rounds=25, tier_layers=(0, 12
     return res
 
 
+def bench_coder(steps, rotate=16):
+    """The pruned "Coder" layer shape: 256 experts, top-10 + shared, 2-bit, same kernels; T = 1, 4 (decode)
+    and 64 (the 32-row GEMM path), 16 distinct layers rotated."""
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+    wl = synth.CONFIGS["coder"]
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    layers = []
+    for l in range(rotate):
+        wr = synth.router_weight(wl.seed, l, E, H)
+        rb = DeviceBank(s.fmt, E, H, I, synth.bank(wl.seed, l, s.fmt, range(E), H, I, workers=16))
+        sb = DeviceBank(s.fmt, 1, H, I, synth.bank(wl.seed, l, s.fmt, [E], H, I))
+        layers.append(DeviceLayer(H, E, k, I, wr, None, rb, sb))
+    res = {"workload": "coder: real-shape 2-bit layer with 256 experts (the pruned build), top-10 + shared, "
+                       f"{rotate} distinct layers rotated"}
+    for T in wl.tokens:
+        xs = [to_device(synth.activations(wl.seed + 7000, j, T, H)) for j in range(16)]
+        ws = layers[0].workspace(T)
+        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        n_steps = steps if T <= 16 else max(steps // 10, 1)
+        ids = torch.empty((n_steps, T, k), dtype=torch.int32, device="cuda")
+        for i in range(50):
+            B.layer_forward(layers[i % rotate].struct, xs[i % 16], T, out, ws)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(n_steps):
+            B.layer_forward(layers[i % rotate].struct, xs[i % 16], T, out, ws, topk_ids=ids[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / n_steps
+        ids_h = ids.cpu().numpy()
+        d = float(np.mean([len(np.unique(ids_h[i])) for i in range(n_steps)]))
+        step_bytes = E * H * 2 + (d + 1) * q2_expert_bytes(H, I) + T * H * 2 + T * H * 4
+        res[f"T{T}"] = {"layer_us": ms * 1e3, "tokens_per_s": T / (ms * 1e-3), "unique_experts_per_step": d,
+                        "layer_GBps": step_bytes / (ms * 1e-3) / 1e9,
+                        "layer_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -406,6 +481,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--cache-steps", type=int, default=5)
     ap.add_argument("--no-cache", action="store_true")
+    ap.add_argument("--coder-steps", type=int, default=2000)
+    ap.add_argument("--no-coder", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run 10 plain device copies of BYTES bytes (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -555,6 +632,8 @@ def main():
         result["stack"] = bench_stack(args.stack_steps)
     if not args.no_cache:
         result["cache"] = bench_cache(args.cache_steps)
+    if not args.no_coder:
+        result["coder"] = bench_coder(args.coder_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host0, T, args.cpu_seconds)
         result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]

@@ -5,4 +5,4 @@ layer's arithmetic (no routing, no dequantisation, no bit layout).  Both sides
 receive the same byte buffers from it and interpret them on their own.
 """
 from .inputs import *  # noqa: F401,F403
-from .configs import CONFIGS, LayerShape  # noqa: F401
+from .configs import CACHE_SLOT_BUDGETS, CONFIGS, LayerShape  # noqa: F401

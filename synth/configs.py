@@ -49,4 +49,12 @@ CONFIGS = {
     # 3-bit layer with a 3,072-slot expert cache (top 64 experts of each of 48 layers), 64 tokens.
     "cache": Workload("cache", 5, LayerShape(2560, 512, 10, 640, True, "q3", 1.1), (64,), layers=48,
                       slots=3072, slots_per_layer=64),
+    # The pruned "Coder" build: 256 of 512 experts kept per layer, still top-10 + shared (page "Strata Runs 125B
+    # Qwen3.8-Flash-Next on a 12GB Gaming GPU", section "The Coder build: half the experts, most of the skill").
+    "coder": Workload("coder", 6, LayerShape(2560, 256, 10, 640, True, "q2", None), (1, 4, 64)),
 }
+
+# Expert-cache sizes the pages report: 1,589 cached experts at 262K context with the KV cache on the GPU, 3,872
+# once most of it moves to RAM (page "Strata Runs 125B Qwen3.8-Flash-Next on a 12GB Gaming GPU", section "How a
+# 125B model fits in 12 GB"); 3,072 is the cache workload's own size.
+CACHE_SLOT_BUDGETS = (1589, 3072, 3872)

@@ -24,7 +24,8 @@ import numpy as np
 
 __all__ = [
     "stream", "f32_to_bf16_bits", "activation_row", "activations", "router_weight", "zipf_ranks",
-    "zipf_bias", "expert_tensors", "bank", "hot_slot_table", "expert_nbytes",
+    "zipf_bias", "expert_tensors", "bank", "hot_slot_table", "expert_nbytes", "budget_per_layer",
+    "budget_slot_table",
 ]
 
 _KIND = {
@@ -145,4 +146,26 @@ def hot_slot_table(seed, n_layers, E, per_layer):
         r = zipf_ranks(seed, l, E)
         hot = r < per_layer
         slot_of[l, hot] = l * per_layer + r[hot]
+    return slot_of
+
+
+def budget_per_layer(n_layers, slots):
+    """Slots of each layer when a budget of ``slots`` is shared out evenly: slots // n_layers each, one more
+    for the first slots % n_layers layers."""
+    q, r = divmod(int(slots), int(n_layers))
+    return np.array([q + (1 if l < r else 0) for l in range(n_layers)], dtype=np.int64)
+
+
+def budget_slot_table(seed, n_layers, E, per_layer, stride=None):
+    """slot_of [n_layers, E] int32 for per-layer slot counts: the per_layer[l] most popular experts of layer l
+    get slots base[l] + rank.  base[l] = l * stride (a pool laid out for ``stride`` slots a layer) or, if stride
+    is None, the running sum of per_layer (a packed pool)."""
+    per_layer = np.asarray(per_layer, dtype=np.int64)
+    base = np.arange(n_layers, dtype=np.int64) * stride if stride is not None else \
+        np.concatenate([[0], np.cumsum(per_layer)[:-1]])
+    slot_of = np.full((n_layers, E), -1, dtype=np.int32)
+    for l in range(n_layers):
+        r = zipf_ranks(seed, l, E)
+        hot = r < per_layer[l]
+        slot_of[l, hot] = base[l] + r[hot]
     return slot_of

@@ -131,3 +131,48 @@ def test_tiered_layer_mostly_misses(pool):
     slot_of[layer] = cut
     nm = _tiered(pool, layer, 8, slot_of)
     assert nm >= 8 * 10 // 4                                  # Zipf routing: the top 8 still take over half
+
+
+@pytest.mark.parametrize("budget", [1589, 3872])
+def test_slot_budget(budget):
+    # The pages' other cache sizes, shared out over 48 layers (1,589: 34 or 33 slots
+    # a layer; 3,872: 81 or 80).  One layer's pool is built from the budget's table;
+    # hits, misses and the output must match the oracle as at 3,072 slots.
+    w = synth.CONFIGS["cache"]
+    s = w.shape
+    k, E, H, I = s.top_k, s.n_experts, s.hidden, s.inter
+    layer = 40
+    per = synth.budget_per_layer(w.layers, budget)
+    table = synth.budget_slot_table(w.seed, w.layers, E, per)
+    row = table[layer]
+    order = np.argsort(synth.zipf_ranks(w.seed, layer, E))[:per[layer]]
+    lpool = synth.bank(w.seed, layer, s.fmt, order, H, I)          # this layer's slots, in slot order
+    local = np.where(row >= 0, row - row[row >= 0].min(), -1).astype(np.int32)
+    slot_of = np.full_like(table, -1)
+    slot_of[layer] = local
+    dpool = DeviceBank(s.fmt, int(per[layer]), H, I, lpool)
+    hl = W.cache_layer("cache", layer, lpool)
+    T = w.tokens[0]
+    x, _ = W.activations_with_margin(hl, T)
+    dl = DeviceLayer(H, E, k, I, hl.wr, hl.bias, dpool, DeviceBank(s.fmt, 1, H, I, hl.shared))
+    ws = dl.workspace(T)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    n_miss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.layer_forward_cached(dl.struct, layer, w.layers, to_device(slot_of), dpool.struct, to_device(x), T, out, ids,
+                           gates, miss, n_miss, ws)
+    torch.cuda.synchronize()
+    smat = OF.expert_matrices(s.fmt, hl.shared, H, I)
+    slot_fn = lambda sl: OF.expert_matrices(s.fmt, lpool, H, I, sl)
+    ref, ids_r, gates_r, misses_r, _ = OL.cached_layer_forward(x, hl.wr, k, local, slot_fn, lambda: smat,
+                                                                bias=hl.bias)
+    assert_route_matches(host(ids), host(gates), hl.logits(x), k, f"budget {budget}")
+    nm = int(host(n_miss)[0])
+    assert nm == len(misses_r)
+    np.testing.assert_array_equal(host(miss)[:nm], misses_r)
+    err = OL.rel_max_err(host(out), ref)
+    print(f"slot budget {budget} (layer {layer}: {per[layer]} slots): hits {T * k - nm}/{T * k}, "
+          f"max|err|/rms = {err:.3e}")
+    assert err <= OUT_TOL

@@ -186,6 +186,24 @@ def test_decode_small_q2_shape(T):
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
 
 
+@pytest.mark.parametrize("T", [1, 4, 64])
+def test_coder_shape(T):
+    # The pruned "Coder" layer: 256 experts instead of 512, top-10 + shared, same
+    # kernels (decode on the matrix cores at T = 1, 4; the 32-row grouped GEMM at
+    # T = 64, whose fp16 h bounds it at the layer's 1e-2).
+    hl = W.host_layer("coder")
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+    assert hl.shape.n_experts == 256
+    assert_route_matches(ids, gates, hl.logits(x), hl.shape.top_k, f"coder T={T}")
+    err = OL.rel_max_err(out, ref)
+    print(f"coder T={T}: max|err|/rms = {err:.3e}")
+    assert err <= (1e-4 if T <= 16 else 1e-2)
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
 def test_decode_extreme_activation_blocks():
     # The 2-bit decode path carries each 32-column block of x (and of h) as
     # fixed-point e4m3 pieces against the block's largest magnitude.  Blocks

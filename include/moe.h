@@ -244,6 +244,54 @@ int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                              void* ws, size_t ws_bytes, void* host_ws, size_t host_ws_bytes,
                              int32_t n_threads, void* stream);
 
+/* Adaptive expert cache (first page, section "How a 125B model fits in 12 GB": the
+ * cache of hot experts adapts to the conversation; the aireport.net page: the few
+ * thousand most used experts, learned while chatting; every expert stays in pinned
+ * system RAM).  The pages give no policy; the library's reading: decayed usage
+ * counts per (layer, expert), each layer's cache periodically re-selected as its
+ * most used experts, and slots refilled from host memory in the background.
+ *
+ * moe_expert_usage: counts uint32 [E] (device) = (counts >> decay_shift) + the number
+ * of entries of topk_ids int32 [n_ids] (device) equal to e; ids outside [0, E) are
+ * ignored.  E <= 1024, 0 <= decay_shift <= 31.  Exact (integer); one launch. */
+int moe_expert_usage(const int32_t* topk_ids, int32_t n_ids, int32_t E, uint32_t* counts,
+                     int32_t decay_shift, void* stream);
+
+/* moe_cache_plan (HOST pointers, no HIP call): the moves that make one layer's cache
+ * its n_slots most used experts.  counts uint32 [E]; slot_row int32 [E]: the layer's
+ * current slot of each expert or -1; layer_slots int32 [n_slots]: the pool slots the
+ * layer owns (distinct; every slot in slot_row must be one of them, one expert each).
+ * Wanted = the n_slots largest counts (ties: lower id).  Incoming = wanted experts
+ * without a slot, by count descending (ties: lower id); targets = the layer's free
+ * slots ascending, then the slots of resident unwanted experts by count ascending
+ * (ties: lower id).  Move i puts incoming[i] into targets[i], for
+ * i < min(|incoming|, |targets|, max_moves): move_experts / move_slots int32
+ * [max_moves], *n_moves the count.  MOE_EINVAL for an inconsistent slot_row. */
+int moe_cache_plan(const uint32_t* counts, const int32_t* slot_row, int32_t E,
+                   const int32_t* layer_slots, int32_t n_slots, int32_t max_moves,
+                   int32_t* move_experts, int32_t* move_slots, int32_t* n_moves);
+
+/* moe_cache_refill: starts the moves (at most 64; move lists in HOST memory) of layer
+ * layer_idx.  host_bank: the layer's E routed experts in host memory (allocate it
+ * pinned, e.g. hipHostMalloc, or the copies are not asynchronous); slot_pool: the
+ * device pool (same format, Q2 or Q3); slot_of int32 [n_layers x E] (device).
+ * On ``stream``: unmaps every expert that sits in a target slot and every incoming
+ * expert (their entries become misses).  On ``copy_stream`` (NULL: ``stream``), after
+ * that: copies each incoming expert's tensors into its slot, then records
+ * done_event (a caller-created hipEvent_t).  Returns without waiting. */
+int moe_cache_refill(const moe_bank_t* host_bank, const moe_bank_t* slot_pool, int32_t* slot_of,
+                     int32_t layer_idx, int32_t n_layers, int32_t E,
+                     const int32_t* move_experts, const int32_t* move_slots, int32_t n_moves,
+                     void* done_event, void* stream, void* copy_stream);
+
+/* moe_cache_commit: on ``stream``, waits for done_event (if not NULL) and maps each
+ * incoming expert to its slot (the same move lists, n_slots = the pool's slot
+ * count).  Calls on ``stream`` between refill and commit see the moved experts as
+ * misses; calls after the commit see them as hits. */
+int moe_cache_commit(int32_t* slot_of, int32_t layer_idx, int32_t n_layers, int32_t E, int32_t n_slots,
+                     const int32_t* move_experts, const int32_t* move_slots, int32_t n_moves,
+                     void* done_event, void* stream);
+
 /* Measurement support.  Arms start_event / stop_event (hipEvent_t, created by
  * the caller) for the NEXT launch of the named kernel by any call above, then
  * forgets them (one-shot).  The events are attached to that kernel's dispatch

@@ -236,6 +236,41 @@ def cached_layer_forward(x_bits, wr_bits, k, slot_row, slot_fn, shared_fn=None, 
     return out, ids, gates, misses, margin
 
 
+# ---------------------------------------------------------------- adaptive cache [A "How a 125B model fits", C]
+# The pages say the cache of hot experts adapts to the conversation; they give no
+# policy.  Reading: decayed integer usage counts, each layer's cache re-selected as
+# its most used experts.
+
+def usage_update(counts, ids, E, shift):
+    """counts[e] // 2**shift + (number of ids equal to e), in uint32; ids outside [0, E) ignored."""
+    out = [int(c) >> shift for c in counts]
+    for e in np.asarray(ids).reshape(-1).tolist():
+        if 0 <= e < E:
+            out[e] += 1
+    return np.array(out, dtype=np.uint64).astype(np.uint32)
+
+
+def cache_plan(counts, slot_row, layer_slots, max_moves):
+    """Moves (expert, slot) that turn a layer's cache into its len(layer_slots) most used experts.
+
+    wanted: the most used experts (ties to the lower id); incoming: wanted ones
+    without a slot, most used first; targets: free slots in ascending order, then
+    the slots of unwanted residents, least used first (ties to the lower id).
+    Returns lists (experts, slots) of length min(len(incoming), len(targets), max_moves)."""
+    E = len(counts)
+    n_slots = len(layer_slots)
+    ranked = sorted(range(E), key=lambda e: (-int(counts[e]), e))
+    wanted = set(ranked[:n_slots])
+    incoming = [e for e in ranked[:n_slots] if slot_row[e] < 0]
+    used = {int(slot_row[e]) for e in range(E) if slot_row[e] >= 0}
+    free = sorted(int(s) for s in layer_slots if int(s) not in used)
+    unwanted = sorted((e for e in range(E) if slot_row[e] >= 0 and e not in wanted),
+                      key=lambda e: (int(counts[e]), e))
+    targets = free + [int(slot_row[e]) for e in unwanted]
+    n = min(len(incoming), len(targets), max_moves)
+    return incoming[:n], targets[:n]
+
+
 # ---------------------------------------------------------------- parity metric
 
 def rel_max_err(got, ref):

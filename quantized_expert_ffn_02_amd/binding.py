@@ -56,6 +56,11 @@ _SIGS = {
     "moe_layer_forward_tiered": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank),
                                                 ctypes.POINTER(Bank), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                                 _vp, _sz, _i32, _vp]),
+    "moe_expert_usage": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp]),
+    "moe_cache_plan": (ctypes.c_int, [_vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "moe_cache_refill": (ctypes.c_int, [ctypes.POINTER(Bank), ctypes.POINTER(Bank), _vp, _i32, _i32, _i32, _vp, _vp,
+                                        _i32, _vp, _vp, _vp]),
+    "moe_cache_commit": (ctypes.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]),
     "moe_time_next_launch": (ctypes.c_int, [_i32, _vp, _vp]),
     "moe_rmsnorm_bf16": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -224,6 +229,40 @@ def layer_forward_tiered(layer, layer_idx, n_layers, slot_of, slot_pool, host_ba
         ctypes.byref(host_bank), ptr(x), int(T), ptr(out), ptr(topk_ids), ptr(topk_gates), ptr(miss_rows),
         ptr(n_miss), ptr(ws), ws.numel() * ws.element_size(), hptr(host_ws),
         host_ws.numel() * host_ws.element_size(), int(n_threads), _stream(stream)))
+
+
+def expert_usage(topk_ids, n_ids, E, counts, decay_shift=0, stream=None):
+    """counts (device uint32/int32 [E]) = (counts >> decay_shift) + selections of each expert in topk_ids."""
+    _check("moe_expert_usage", lib().moe_expert_usage(ptr(topk_ids), int(n_ids), int(E), ptr(counts),
+                                                      int(decay_shift), _stream(stream)))
+
+
+def cache_plan(counts, slot_row, layer_slots, max_moves):
+    """Host call on numpy arrays: returns (move_experts, move_slots) int32 arrays."""
+    import numpy as np
+    counts = np.ascontiguousarray(counts, dtype=np.uint32)
+    slot_row = np.ascontiguousarray(slot_row, dtype=np.int32)
+    layer_slots = np.ascontiguousarray(layer_slots, dtype=np.int32)
+    me = np.zeros(max(int(max_moves), 1), dtype=np.int32)
+    ms = np.zeros_like(me)
+    n = np.zeros(1, dtype=np.int32)
+    _check("moe_cache_plan", lib().moe_cache_plan(hptr(counts), hptr(slot_row), len(slot_row), hptr(layer_slots),
+                                                  len(layer_slots), int(max_moves), hptr(me), hptr(ms), hptr(n)))
+    return me[:n[0]].copy(), ms[:n[0]].copy()
+
+
+def cache_refill(host_bank, slot_pool, slot_of, layer_idx, n_layers, E, move_experts, move_slots, done_event,
+                 stream=None, copy_stream=None):
+    """move lists: host int32 numpy arrays; done_event: a hipEvent_t handle (int)."""
+    _check("moe_cache_refill", lib().moe_cache_refill(
+        ctypes.byref(host_bank), ctypes.byref(slot_pool), ptr(slot_of), int(layer_idx), int(n_layers), int(E),
+        hptr(move_experts), hptr(move_slots), len(move_experts), done_event, _stream(stream), copy_stream))
+
+
+def cache_commit(slot_of, layer_idx, n_layers, E, n_slots, move_experts, move_slots, done_event, stream=None):
+    _check("moe_cache_commit", lib().moe_cache_commit(
+        ptr(slot_of), int(layer_idx), int(n_layers), int(E), int(n_slots), hptr(move_experts), hptr(move_slots),
+        len(move_experts), done_event, _stream(stream)))
 
 
 def time_next_launch(kernel, start_event, stop_event):

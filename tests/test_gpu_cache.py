@@ -176,3 +176,91 @@ def test_slot_budget(budget):
     print(f"slot budget {budget} (layer {layer}: {per[layer]} slots): hits {T * k - nm}/{T * k}, "
           f"max|err|/rms = {err:.3e}")
     assert err <= OUT_TOL
+
+
+# ------------------------------------------------------------------ adaptive cache
+
+@pytest.mark.parametrize("n_ids,E,shift", [(40, 512, 1), (81920, 512, 2), (7, 1024, 0), (0, 16, 31), (640, 256, 5)])
+def test_expert_usage_counts(n_ids, E, shift):
+    # decayed usage counts: bit-exact against the oracle's integer definition
+    rng = np.random.default_rng(n_ids + E)
+    ids = rng.integers(-2, E + 2, size=n_ids).astype(np.int32)       # a few ids outside [0, E)
+    counts0 = rng.integers(0, 2 ** 32, size=E, dtype=np.uint64).astype(np.uint32)
+    d_counts = to_device(counts0)
+    B.expert_usage(to_device(ids) if n_ids else None, n_ids, E, d_counts, shift)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(d_counts).view(np.uint32), OL.usage_update(counts0, ids, E, shift))
+
+
+def _pinned(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).pin_memory()
+
+
+@pytest.mark.parametrize("fmt", ["q2", "q3"])
+def test_cache_adapts(fmt):
+    # A small layer (H = 512, I = 256, 32 experts, top-4 + shared, Zipf routing) with an
+    # 8-slot pool that starts empty.  Each round: a cached call, usage counts from its
+    # ids, a plan, refill on a second stream, commit.  After every round the pool
+    # holds each mapped expert's exact bytes, the slot table is the oracle's plan
+    # applied, and the next cached call matches the oracle with that table.
+    H, I, E, k, n_slots, T = 512, 256, 32, 4, 8, 16
+    shape = synth.LayerShape(H, E, k, I, True, fmt, 1.1)
+    hl = W.host_layer("cache", shape=shape)
+    host_t = {n: _pinned(v) for n, v in hl.routed.items()}
+    g = host_t.get
+    hbank = B.make_bank(fmt, E, H, I, g("w13"), g("w13_hi"), g("w13_scale"), g("w2"), g("w2_hi"), g("w2_scale"))
+    per_expert = {n: len(v) // E for n, v in hl.routed.items()}
+    dpool = DeviceBank(fmt, n_slots, H, I, {n: np.zeros(per_expert[n] * n_slots, dtype=v.dtype)
+                                            for n, v in hl.routed.items()})
+    dl = DeviceLayer(H, E, k, I, hl.wr, hl.bias, dpool, DeviceBank(fmt, 1, H, I, hl.shared))
+    ws = dl.workspace(T)
+    slot_of = torch.full((1, E), -1, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    layer_slots = np.arange(n_slots, dtype=np.int32)
+    copy_stream = torch.cuda.Stream()
+    smat = OF.expert_matrices(fmt, hl.shared, H, I)
+    row_ref = np.full(E, -1, dtype=np.int32)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    n_miss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hits = []
+    for rnd in range(3):
+        x, _ = W.activations_with_margin(hl, T, x_seed=100 + rnd)
+        B.layer_forward_cached(dl.struct, 0, 1, slot_of, dpool.struct, to_device(x), T, out, ids, gates, miss,
+                               n_miss, ws)
+        B.expert_usage(ids, T * k, E, counts, 1)
+        torch.cuda.synchronize()
+        # the cached call against the oracle with the table it saw (slot -> expert from the reference
+        # table; weights from the host bank, never from the device pool)
+        expert_of = {int(sl): int(e) for e, sl in enumerate(row_ref) if sl >= 0}
+        slot_fn = lambda sl: OF.expert_matrices(fmt, hl.routed, H, I, expert_of[sl])
+        ref, _, _, misses_r, _ = OL.cached_layer_forward(x, hl.wr, k, row_ref, slot_fn, lambda: smat, bias=hl.bias)
+        nm = int(host(n_miss)[0])
+        np.testing.assert_array_equal(host(miss)[:nm], misses_r)
+        assert OL.rel_max_err(host(out), ref) <= OUT_TOL
+        hits.append(T * k - nm)
+        # plan, refill, commit
+        c_h = host(counts).view(np.uint32)
+        me, ms = B.cache_plan(c_h, row_ref, layer_slots, 64)
+        want = OL.cache_plan(c_h, row_ref, layer_slots, 64)
+        assert me.tolist() == want[0] and ms.tolist() == want[1]
+        ev = torch.cuda.Event()
+        ev.record()                                   # creates the underlying hipEvent
+        B.cache_refill(hbank, dpool.struct, slot_of, 0, 1, E, me, ms, ev.cuda_event,
+                       copy_stream=copy_stream.cuda_stream)
+        B.cache_commit(slot_of, 0, 1, E, n_slots, me, ms, ev.cuda_event)
+        torch.cuda.synchronize()
+        for e, s in zip(me.tolist(), ms.tolist()):
+            row_ref[row_ref == s] = -1
+            row_ref[e] = s
+        np.testing.assert_array_equal(host(slot_of)[0], row_ref)
+        for e in np.flatnonzero(row_ref >= 0):
+            s = int(row_ref[e])
+            for n, t in dpool.tensors.items():
+                b = per_expert[n] * hl.routed[n].itemsize
+                got = t.view(torch.uint8)[s * b:(s + 1) * b].cpu().numpy()
+                np.testing.assert_array_equal(got, hl.routed[n].view(np.uint8)[e * b:(e + 1) * b])
+    print(f"{fmt}: hits per round {hits} of {T * k}")
+    assert hits[0] == 0 and hits[-1] > hits[0]

@@ -407,6 +407,124 @@ def bench_tiered(layers, pool, d_slot, xs, ws, wl, rounds=25, tier_layers=(0, 12
     return res
 
 
+def bench_adaptive(steps=320, period=8, shift_at=120, max_moves=16, slots=64, T=64):
+    """Adaptive expert cache on one real-shape 3-bit layer (512 experts, 64 slots, 64-token batches, Zipf(1.1)
+    routing): the cache starts as the first popularity order's top 64; at step ``shift_at`` the router's bias
+    switches to another popularity order (a change of topic).  Every step adds its selections to decayed usage
+    counts; every ``period`` steps the previous refill is committed and a new plan of at most ``max_moves`` moves
+    is started on a copy stream from pinned host memory."""
+    import time
+
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_expert_ffn_02_amd import binding as B
+    from quantized_expert_ffn_02_amd.device_layer import DeviceBank, DeviceLayer, to_device
+    wl = synth.CONFIGS["cache"]
+    s = wl.shape
+    H, I, E, k = s.hidden, s.inter, s.n_experts, s.top_k
+    layer = 0
+    full = synth.bank(wl.seed, layer, s.fmt, range(E), H, I, workers=16)
+    host_t = {n: torch.from_numpy(v.view(np.uint8)).pin_memory() for n, v in full.items()}
+    g = host_t.get
+    hbank = B.make_bank(s.fmt, E, H, I, g("w13"), g("w13_hi"), g("w13_scale"), g("w2"), g("w2_hi"), g("w2_scale"))
+    order = np.argsort(synth.zipf_ranks(wl.seed, layer, E))[:slots]
+    pool = DeviceBank(s.fmt, slots, H, I, synth.bank(wl.seed, layer, s.fmt, order, H, I))
+    table0 = np.full((1, E), -1, dtype=np.int32)
+    table0[0, order] = np.arange(slots, dtype=np.int32)
+    wr = synth.router_weight(wl.seed, layer, E, H)
+    sb = DeviceBank(s.fmt, 1, H, I, synth.bank(wl.seed, layer, s.fmt, [E], H, I))
+    topics = [DeviceLayer(H, E, k, I, wr, synth.zipf_bias(wl.seed, lb, E, s.zipf), pool, sb) for lb in (layer, 100)]
+    xs = [to_device(synth.activations(wl.seed + 13000, j, T, H)) for j in range(16)]
+    ws = topics[0].workspace(T)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    nmiss = torch.zeros(steps, dtype=torch.int32, device="cuda")
+    layer_slots = np.arange(slots, dtype=np.int32)
+    copy_stream = torch.cuda.Stream()
+
+    def run(adapt):
+        slot_of = to_device(table0)
+        counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+        pending, moved = None, 0
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record()
+        for step in range(steps):
+            L = topics[0 if step < shift_at else 1]
+            B.layer_forward_cached(L.struct, 0, 1, slot_of, pool.struct, xs[step % 16], T, out, ids, gates, miss,
+                                   nmiss[step:step + 1], ws)
+            evs[step + 1].record()
+            if adapt:
+                B.expert_usage(ids, T * k, E, counts, 1 if step % period == 0 else 0)
+            torch.cuda.current_stream().synchronize()        # a decode loop waits for each step's output
+            if not adapt or step % period != period - 1:
+                continue
+            # one refill in flight, committed once its copies are done (the compute stream never waits
+            # for them); the next plan is made after the commit
+            if pending is not None:
+                if not pending[2].query():
+                    continue
+                B.cache_commit(slot_of, 0, 1, E, slots, pending[0], pending[1], pending[2].cuda_event)
+                pending = None
+            me, ms = B.cache_plan(counts.cpu().numpy().view(np.uint32), slot_of.cpu().numpy()[0], layer_slots,
+                                  max_moves)
+            if len(me):
+                ev = torch.cuda.Event()
+                ev.record()
+                B.cache_refill(hbank, pool.struct, slot_of, 0, 1, E, me, ms, ev.cuda_event,
+                               copy_stream=copy_stream.cuda_stream)
+                pending = (me, ms, ev)
+                moved += len(me)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        hit = 1.0 - nmiss.cpu().numpy().astype(np.float64) / (T * k)
+        # stream time per step (event to event) over the 40 steps before the shift and the last 40
+        win = {"before_shift": evs[shift_at - 40].elapsed_time(evs[shift_at]) / 40 * 1e3,
+               "last_40": evs[steps - 40].elapsed_time(evs[steps]) / 40 * 1e3}
+        return dt, hit, moved, win
+
+    run(False)                                            # warm-up
+    static_s, static_hit, _, static_win = run(False)
+    adapt_s, hit, moved, adapt_win = run(True)
+    before = float(hit[shift_at - 40:shift_at].mean())
+    target = 0.95 * before
+    after = hit[shift_at:]
+    rec = next((i for i in range(len(after) - 7) if after[i:i + 8].mean() >= target), None)
+    # refill bandwidth on an idle GPU: 16 experts from pinned memory into their slots (the second of two
+    # refills of the same experts: the first DMA from a pinned page costs extra)
+    me = np.arange(16, dtype=np.int32) + 200
+    ms = np.arange(16, dtype=np.int32)
+    slot_of = to_device(table0)
+    e0, done = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done.record(copy_stream)                              # creates the underlying hipEvent
+    B.cache_refill(hbank, pool.struct, slot_of, 0, 1, E, me, ms, done.cuda_event, copy_stream=copy_stream.cuda_stream)
+    torch.cuda.synchronize()
+    e0.record(copy_stream)
+    B.cache_refill(hbank, pool.struct, slot_of, 0, 1, E, me, ms, done.cuda_event, copy_stream=copy_stream.cuda_stream)
+    torch.cuda.synchronize()
+    refill_ms = e0.elapsed_time(done)
+    refill_bytes = 16 * q3_expert_bytes(H, I)
+    return {"workload": "adaptive cache: one real-shape 3-bit layer, 64 slots of 512 experts, 64-token batches, "
+                        f"Zipf(1.1) routing whose popularity order changes at step {shift_at} of {steps}; each step waits for "
+                        f"its output (as a decode loop does); re-plan every {period} steps (at most {max_moves} moves, "
+                        "one refill in flight, committed once its copies are done), "
+                        "refills from pinned host memory",
+            "hit_rate_before_shift": before, "hit_rate_first_period_after": float(after[:period].mean()),
+            "hit_rate_last_40_steps": float(hit[-40:].mean()),
+            "hit_rate_last_40_steps_static": float(static_hit[-40:].mean()),
+            "steps_to_recover_95pct": rec, "experts_moved": moved,
+            "step_us_adaptive": adapt_s * 1e6, "step_us_static": static_s * 1e6,
+            "stream_us_per_step_before_shift": {"adaptive": adapt_win["before_shift"],
+                                                "static": static_win["before_shift"]},
+            "stream_us_per_step_last_40": {"adaptive": adapt_win["last_40"], "static": static_win["last_40"]},
+            "refill_16_experts_ms": refill_ms, "refill_GBps": refill_bytes / (refill_ms * 1e-3) / 1e9}
+
+
 def bench_coder(steps, rotate=16):
     """The pruned "Coder" layer shape: 256 experts, top-10 + shared, 2-bit, same kernels; T = 1, 4 (decode)
     and 64 (the 32-row GEMM path), 16 distinct layers rotated."""
@@ -483,6 +601,7 @@ def main():
     ap.add_argument("--no-cache", action="store_true")
     ap.add_argument("--coder-steps", type=int, default=2000)
     ap.add_argument("--no-coder", action="store_true")
+    ap.add_argument("--no-adaptive", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run 10 plain device copies of BYTES bytes (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -634,6 +753,8 @@ def main():
         result["cache"] = bench_cache(args.cache_steps)
     if not args.no_coder:
         result["coder"] = bench_coder(args.coder_steps)
+    if not args.no_adaptive:
+        result["adaptive"] = bench_adaptive()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host0, T, args.cpu_seconds)
         result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]

@@ -132,3 +132,52 @@ def test_other_entry_points_validate(lib):
     assert lib.moe_time_next_launch(99, None, None) == B.MOE_EINVAL
     assert lib.moe_time_next_launch(1, FAKE, None) == B.MOE_EINVAL
     assert lib.moe_workspace_clear(None, 0, None) == B.MOE_EWORKSPACE
+
+
+def test_host_tier_and_cache_entry_points_validate(lib):
+    # every case returns before any HIP call
+    L = q2_layer(fmt="q3")
+    pool = q2_layer(fmt="q3").routed
+    hb = q2_layer(fmt="q3").routed
+    i32 = ctypes.c_int32
+
+    def tiered(host_bank=ctypes.byref(hb), x=FAKE, host_ws=FAKE * 64, host_ws_bytes=1 << 40, pool_=pool, T=64):
+        return lib.moe_layer_forward_tiered(ctypes.byref(L), 0, 48, FAKE, ctypes.byref(pool_), host_bank, x, T, FAKE,
+                                            None, None, FAKE, FAKE, FAKE * 64, 1 << 40, host_ws, host_ws_bytes, 0,
+                                            None)
+
+    assert lib.moe_tiered_host_bytes(ctypes.byref(L), 0) == 0
+    need = lib.moe_tiered_host_bytes(ctypes.byref(L), 64)
+    assert need >= 64 * 2560 * 2 + 3 * 64 * 10 * 4 + 4 + 64 * 2560 * 4
+    assert tiered(host_bank=None) == B.MOE_EINVAL
+    assert tiered(x=FAKE + 2) == B.MOE_EINVAL                      # x copied as 4-byte words
+    assert tiered(host_ws_bytes=need - 1) == B.MOE_EWORKSPACE
+    assert tiered(host_ws=FAKE + 8) == B.MOE_EWORKSPACE             # not 256-byte aligned
+    assert tiered(pool_=q2_layer(fmt="q2").routed) == B.MOE_EUNSUPPORTED   # host bank and pool formats differ
+
+    ids = (i32 * 3)(1, 2, 3)
+    slots = (i32 * 3)(0, 1, 2)
+    dup = (i32 * 3)(0, 1, 1)
+    far = (i32 * 3)(1, 2, 512)
+
+    def refill(experts=ids, slots_=slots, n=3, done=FAKE, layer=0, host_bank=hb, pool_=pool):
+        return lib.moe_cache_refill(ctypes.byref(host_bank), ctypes.byref(pool_), FAKE, layer, 48, 512, experts,
+                                    slots_, n, done, None, None)
+
+    pool.n_experts = 64
+    assert refill(done=None) == B.MOE_EINVAL
+    assert refill(n=65) == B.MOE_EINVAL
+    assert refill(slots_=dup) == B.MOE_EINVAL
+    assert refill(experts=far) == B.MOE_EINVAL                      # expert id outside the bank
+    assert refill(slots_=(i32 * 3)(0, 1, 64)) == B.MOE_EINVAL       # slot outside the pool
+    assert refill(layer=48) == B.MOE_EINVAL
+    assert refill(host_bank=q2_layer(fmt="bf16").routed, pool_=q2_layer(fmt="bf16").routed) == B.MOE_EUNSUPPORTED
+    assert lib.moe_cache_commit(FAKE, 0, 48, 512, 0, ids, slots, 3, None, None) == B.MOE_EINVAL     # no slots
+    assert lib.moe_cache_commit(FAKE, 0, 48, 512, 64, dup, slots, 3, None, None) == B.MOE_EINVAL   # repeated expert
+    assert lib.moe_cache_commit(FAKE, -1, 48, 512, 64, ids, slots, 3, None, None) == B.MOE_EINVAL
+
+    assert lib.moe_expert_usage(FAKE, 10, 0, FAKE, 0, None) == B.MOE_EINVAL
+    assert lib.moe_expert_usage(FAKE, 10, 1025, FAKE, 0, None) == B.MOE_EINVAL
+    assert lib.moe_expert_usage(FAKE, 10, 512, FAKE, 32, None) == B.MOE_EINVAL
+    assert lib.moe_expert_usage(None, 10, 512, FAKE, 0, None) == B.MOE_EINVAL
+    assert lib.moe_expert_usage(FAKE, 10, 512, None, 0, None) == B.MOE_EINVAL

@@ -296,19 +296,26 @@ __global__ __launch_bounds__((NS + TAIL) * 64) void k_decode_down_mx(MxFfnArgs a
   }
 }
 
-// Down projection and combine of token t and 64 output rows: wave i < k takes
-// routed entry t k + i, wave k the shared expert, each over all K = I columns
-// (256-column chunks, then the 128-column tail, in order); waves past the
-// token's entries only join the barrier.  The block then adds the entries'
-// gate-scaled rows in rank order, the shared expert's row and the residual.
-template <int W, int NS, int TAIL>
+// Down projection and combine of token t and RB (64 or 32) output rows: wave
+// i < k takes routed entry t k + i, wave k the shared expert, each over all
+// K = I columns (256-column chunks, then the 128-column tail, in order); waves
+// past the token's entries only join the barrier.  The block then adds the
+// entries' gate-scaled rows in rank order, the shared expert's row and the
+// residual.  32-row blocks double the blocks of a small batch; the sums of
+// squares for the next layer's norm come in 64-row groups, so only 64-row
+// blocks write them.
+template <int W, int NS, int TAIL, int RB>
 __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, const uint16_t* __restrict__ residual,
                                                                   float* __restrict__ out,
                                                                   uint16_t* __restrict__ out_bf16,
                                                                   float* __restrict__ sq_out) {
   constexpr int NV = 2 * NS + TAIL;   // activation chunks of K
-  __shared__ __attribute__((aligned(16))) float red[W][4][64];
+  constexpr int S = RB / 16;          // 16-row MFMA groups of the block
+  static_assert(RB == 64 || RB == 32, "64- or 32-row blocks");
+  __shared__ __attribute__((aligned(16))) float red[W][S][64];
   const int tok = blockIdx.x, rg = blockIdx.y;
+  // 64-row weight tile of the block, and the block's first row inside it
+  const int tile = RB == 64 ? rg : rg >> 1, r0 = RB == 64 ? 0 : (rg & 1) * 32;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int K = a.I;
@@ -332,52 +339,54 @@ __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, 
     const int n = lane & 15, q = lane >> 4;
     const int nch64 = K / 64, n128 = K / 128;
 
-    u32x4 cw[NS + TAIL][4];
-    uint32_t sc[NS + TAIL][4];
+    u32x4 cw[NS + TAIL][S];
+    uint32_t sc[NS + TAIL][S];
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
-      const uint32_t cso = (uint32_t)(((size_t)rg * nch64 + 4 * c) * 1024);
-      const uint32_t sso = (uint32_t)(((size_t)rg * n128 + 2 * c) * 512);
+      const uint32_t cso = (uint32_t)(((size_t)tile * nch64 + 4 * c) * 1024);
+      const uint32_t sso = (uint32_t)(((size_t)tile * n128 + 2 * c) * 512);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        cw[c][s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(q * 1024 + (16 * s + n) * 16), cso, 0);
+      for (int s = 0; s < S; ++s) {
+        cw[c][s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(q * 1024 + (r0 + 16 * s + n) * 16), cso, 0);
         sc[c][s] = __builtin_amdgcn_raw_buffer_load_b32(
-            rs, (uint32_t)(((q >> 1) * 64 + 16 * s + n) * 8 + (q & 1) * 4), sso, 0);
+            rs, (uint32_t)(((q >> 1) * 64 + r0 + 16 * s + n) * 8 + (q & 1) * 4), sso, 0);
       }
     }
     if (TAIL) {
       const int c = 2 * NS;
-      const uint32_t cso = (uint32_t)(((size_t)rg * nch64 + 2 * c) * 1024);
-      const uint32_t sso = (uint32_t)(((size_t)rg * n128 + c) * 512);
+      const uint32_t cso = (uint32_t)(((size_t)tile * nch64 + 2 * c) * 1024);
+      const uint32_t sso = (uint32_t)(((size_t)tile * n128 + c) * 512);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < S; ++s) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b64(
-            rc, (uint32_t)((((q >> 1) * 64 + 16 * s + n) * 16) + 8 * (q & 1)), cso, 0);
+            rc, (uint32_t)((((q >> 1) * 64 + r0 + 16 * s + n) * 16) + 8 * (q & 1)), cso, 0);
         cw[NS][s] = u32x4{v[0], v[1], 0u, 0u};
-        sc[NS][s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(((16 * s + n) * 4 + q) * 2), sso, 0);
+        sc[NS][s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(((r0 + 16 * s + n) * 4 + q) * 2), sso, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first product
     const mx_v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float y[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) y[s] = 0.0f;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int c = v >> 1, pi = v & 1;   // the tail chunk (v = 2 NS) reads words 0, 1 of its own loads
       const mx_v8i A = mx_act_operand(X[v]);
       const mx_v4f off = mx_mfma(A, mx_minus_one(), (int)X[v].sa, zero);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < S; ++s) {
         const u32x4& w = cw[c][s];
         const mx_v4f o = mx_mfma(A, pi ? mx_weights(w.z, w.w) : mx_weights(w.x, w.y), (int)X[v].sa, off);
         y[s] = mx_accumulate(o, pi ? sc[c][s] >> 16 : sc[c][s] & 0xFFFFu, y[s]);
       }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) red[wv][s][(lane & 15) * 4 + (lane >> 4)] = y[s];
+    for (int s = 0; s < S; ++s) red[wv][s][(lane & 15) * 4 + (lane >> 4)] = y[s];
   }
   __syncthreads();
   const int t = threadIdx.x;
-  if (t < 64) {
+  if (t < RB) {
     // row t: subgroup s = t / 16, row n = t % 16 of it; entries in rank order,
     // then the shared expert, then the residual
     const int s = t >> 4, nn = t & 15;
@@ -387,12 +396,12 @@ __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, 
       const float e = ((v.x + v.y) + v.z) + v.w;
       acc += (w < a.k ? a.gates[(size_t)tok * a.k + w] : 1.0f) * e;
     }
-    const size_t o = (size_t)tok * a.H + (size_t)rg * 64 + t;
+    const size_t o = (size_t)tok * a.H + (size_t)rg * RB + t;
     if (residual) acc += bf16_to_f32(residual[o]);
     out[o] = acc;
     const uint32_t ob = f32_to_bf16_rne(acc);
     if (out_bf16) out_bf16[o] = (uint16_t)ob;
-    if (sq_out) {
+    if (RB == 64 && sq_out) {
       // wave 0 holds the block's 64 rows: the sum of squares of their bf16 values
       const float sq = rms_group_sum(bf16_to_f32(ob));
       if (t == 0) sq_out[(size_t)tok * (a.H / 64) + rg] = sq;
@@ -433,10 +442,22 @@ hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
 hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
                                          float* sq_out, hipStream_t s) {
   const int n_ent = a.k + (a.with_shared ? 1 : 0);
-  dim3 grid(a.T, a.H / 64);
+  // 32-row blocks when 64-row ones would be very few (one token: 40 blocks at
+  // H = 2560; measured 18.1 against 19.5 us a layer, while at four tokens 320
+  // 32-row blocks were slower than 160 64-row ones) and no sums of squares are
+  // asked for (they come in 64-row groups)
+  const bool rows32 = !sq_out && a.T * (a.H / 64) <= 64;
+  dim3 grid(a.T, a.H / (rows32 ? 32 : 64));
   if (!decode_down_combine_mx_ok(a.I, a.k, a.with_shared)) return hipErrorInvalidValue;
-#define MOE_DC_MX(W, NS, TL) \
-  MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16, sq_out)
+#define MOE_DC_MX(W, NS, TL)                                                                                  \
+  do {                                                                                                        \
+    if (rows32)                                                                                               \
+      MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL, 32>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16, \
+                 sq_out);                                                                                     \
+    else                                                                                                      \
+      MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL, 64>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16, \
+                 sq_out);                                                                                     \
+  } while (0)
   const bool small = n_ent <= 11;
   switch (a.I) {
     case 512: if (small) MOE_DC_MX(11, 2, 0); else MOE_DC_MX(16, 2, 0); break;

@@ -31,13 +31,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM traffic of the decode gate/up kernel (T = 4, 44 x 10 blocks) from two
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; command and figures in the
 # profiles/ counter summary), each scaled by what the counter reads for a plain
-# 256 MiB device copy: FETCH_SIZE reads 131,084.5 KiB for 262,144 KiB read
+# 256 MiB device copy: FETCH_SIZE reads 131,084.3 KiB for 262,144 KiB read
 # (factor 2.0), WRITE_SIZE 262,144 KiB for 262,144 KiB written (factor 1.0).
 # Reported only while the kernel's sources are the ones that were counted.
 GATEUP_TRAFFIC = {
     "sources": ["decode_mx.hip", "mx.h", "mfma.h", "device.h", "topk.h"],
-    "sha256": "c37a46a89085abcf11afa72a4cc77787d45a6567abda0e9c8c052ac509f3dbd4",
-    "fetch_kib": 22239.4, "fetch_scale": 262144.0 / 131084.5,
+    "sha256": "00f3790f89d24454c30911e4847f1190a8069a63f88cd36210e32208942314a6",
+    "fetch_kib": 22239.9, "fetch_scale": 262144.0 / 131084.3,
     "write_kib": 118.8, "write_scale": 1.0,
     "tokens": 4,
 }

@@ -116,7 +116,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xmx_exps = take(Tm * mx_exps_bytes((int)H));
   o.hmx_data = take(nm * mx_data_bytes((int)I));
   o.hmx_exps = take(nm * mx_exps_bytes((int)I));
-  o.norm_sq = take(Tm * (H / 64) * 4);
+  o.norm_sq = take(Tm * (H / 16) * 4);   // squares' sums per 16 output columns
   o.out_f32 = take(T * H * 4);
   o.xa = take(T * H * 2);
   o.xb = take(T * H * 2);
@@ -447,8 +447,8 @@ static bool fused_norm_path(const moe_layer_t* L, int T) {
 }
 
 // norm_sq_in: x is the layer input before its RMSNorm, with its partial sums of
-// squares ([T][H / 64]); norm_sq_out: write those of out_bf16.  Both only on
-// the fused-norm decode path (fused_norm_path).
+// squares ([T][H / 16], per 16 columns); norm_sq_out: write those of out_bf16.
+// Both only on the fused-norm decode path (fused_norm_path).
 static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
                               float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
                               void* ws, const Layout& lay, hipStream_t s, const float* norm_sq_in = nullptr,

@@ -301,9 +301,9 @@ __global__ __launch_bounds__((NS + TAIL) * 64) void k_decode_down_mx(MxFfnArgs a
 // K = I columns (256-column chunks, then the 128-column tail, in order); waves
 // past the token's entries only join the barrier.  The block then adds the
 // entries' gate-scaled rows in rank order, the shared expert's row and the
-// residual.  32-row blocks double the blocks of a small batch; the sums of
-// squares for the next layer's norm come in 64-row groups, so only 64-row
-// blocks write them.
+// residual.  32-row blocks double the blocks of a small batch.  sq_out (the
+// next layer's norm): the squares' sums of the bf16 outputs per 16 rows,
+// [token][H / 16].
 template <int W, int NS, int TAIL, int RB>
 __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, const uint16_t* __restrict__ residual,
                                                                   float* __restrict__ out,
@@ -401,10 +401,11 @@ __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, 
     out[o] = acc;
     const uint32_t ob = f32_to_bf16_rne(acc);
     if (out_bf16) out_bf16[o] = (uint16_t)ob;
-    if (RB == 64 && sq_out) {
-      // wave 0 holds the block's 64 rows: the sum of squares of their bf16 values
-      const float sq = rms_group_sum(bf16_to_f32(ob));
-      if (t == 0) sq_out[(size_t)tok * (a.H / 64) + rg] = sq;
+    if (sq_out) {
+      // the block's rows are lanes 0 .. RB - 1 of wave 0; lane 16 j holds the
+      // squares' sum of rows 16 j .. 16 j + 15
+      const float sq = rms_row16_sums(bf16_to_f32(ob));
+      if ((t & 15) == 0) sq_out[(size_t)tok * (a.H / 16) + rg * (RB / 16) + (t >> 4)] = sq;
     }
   }
 }
@@ -444,9 +445,8 @@ hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* res
   const int n_ent = a.k + (a.with_shared ? 1 : 0);
   // 32-row blocks when 64-row ones would be very few (one token: 40 blocks at
   // H = 2560; measured 18.1 against 19.5 us a layer, while at four tokens 320
-  // 32-row blocks were slower than 160 64-row ones) and no sums of squares are
-  // asked for (they come in 64-row groups)
-  const bool rows32 = !sq_out && a.T * (a.H / 64) <= 64;
+  // 32-row blocks were slower than 160 64-row ones)
+  const bool rows32 = a.T * (a.H / 64) <= 64;
   dim3 grid(a.T, a.H / (rows32 ? 32 : 64));
   if (!decode_down_combine_mx_ok(a.I, a.k, a.with_shared)) return hipErrorInvalidValue;
 #define MOE_DC_MX(W, NS, TL)                                                                                  \

@@ -83,11 +83,31 @@ __device__ __forceinline__ float rms_inv_from_groups(float group_sum_or_zero, in
   return 1.0f / sqrtf(wave_sum_rows(group_sum_or_zero) / (float)H + eps);
 }
 
-// RMSNorm scale of row t from its group sums sq[t * G + g]; wave-uniform, every
-// lane must call.
+// The squares' sums of the 16-column rows of a 64-column group, as
+// rms_group_sum forms them (each at lane 16 j of the 16-lane row j; a kernel with
+// 32 columns in lanes 0..31 gets rows 0 and 1 with the same bits).
+__device__ __forceinline__ float rms_row16_sums(float v) {
+#pragma clang fp contract(off)
+  float q = v * v;
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0xB1, 0xF, 0xF, true));
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x4E, 0xF, 0xF, true));
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x124, 0xF, 0xF, true));
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x128, 0xF, 0xF, true));
+  return q;
+}
+
+// RMSNorm scale of row t from its 16-column sums sq[t * (H / 16) + j]: group g
+// adds its four in the order rms_group_sum does, then the groups as
+// rms_inv_from_groups does.  Wave-uniform, every lane must call.
 __device__ __forceinline__ float row_inv_rms(const float* __restrict__ sq, int t, int H, float eps) {
+#pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, G = H / 64;
-  return rms_inv_from_groups(lane < G ? sq[(size_t)t * G + lane] : 0.0f, H, eps);
+  float g = 0.0f;
+  if (lane < G) {
+    const float4 r = *reinterpret_cast<const float4*>(sq + (size_t)t * (H / 16) + 4 * lane);
+    g = ((r.x + r.y) + r.z) + r.w;
+  }
+  return rms_inv_from_groups(g, H, eps);
 }
 
 typedef __bf16 moe_bf16x2_t __attribute__((ext_vector_type(2)));

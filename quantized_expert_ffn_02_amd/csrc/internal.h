@@ -97,8 +97,8 @@ struct SmallRouteArgs {
   float* xinit;
   uint8_t* xmx_data = nullptr;   // fp8-piece activation table (mx.h; NULL: not built)
   uint8_t* xmx_exps = nullptr;
-  // x before its RMSNorm: per-row partial sums of squares over 64-column groups
-  // ([T][H / 64]) and eps; every use of x applies the norm (NULL: x is used as is)
+  // x before its RMSNorm: per-row partial sums of squares over 16-column runs
+  // ([T][H / 16]) and eps; every use of x applies the norm (NULL: x is used as is)
   const float* norm_sq = nullptr;
   float norm_eps = 0.0f;
   int32_t* ids;

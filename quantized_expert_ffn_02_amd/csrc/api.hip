@@ -389,12 +389,21 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
 // tile plan, x -> fp16 pair order, gate/up, down, combine.  In expert-cache
 // mode ``routed`` is the slot pool and ``slot_map`` maps routed groups to pool
 // slots (-1: a miss, whose rows contribute zero).
+// The next stack layer's normalised input, written by this layer's combine.
+struct NormNext {
+  uint16_t* xn;     // bf16 RMSNorm of out_bf16
+  uint16_t* f16p;   // its fp16 pair-order copy (the next GEMM's input)
+  float eps;
+};
+
 // x_f16_ready: the workspace's fp16 pair-order copy of x is already written.
 // after_route (optional) enqueues work that needs only the routing (ids, gates).
+// norm_next (optional): the combine also writes the next layer's norm.
 static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int32_t* slot_map, const uint16_t* x,
                        int32_t T, const uint16_t* residual, float* out, uint16_t* out_bf16, int32_t* ids,
                        float* gates, float* margin, void* ws, const Layout& lay, hipStream_t s,
-                       bool x_f16_ready = false, const std::function<int()>* after_route = nullptr) {
+                       bool x_f16_ready = false, const std::function<int()>* after_route = nullptr,
+                       const NormNext* norm_next = nullptr) {
   const int k = L->top_k, E = L->n_experts, H = L->hidden, I = L->inter;
   const int with_shared = has_shared(L) ? 1 : 0;
   const int n = T * k + (with_shared ? T : 0);
@@ -425,7 +434,11 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
     return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
                           nullptr, nullptr, kSmallTileRows, q3, slot_map);
   }));
-  MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
+  if (norm_next)
+    MOE_TRY(launch_combine_norm(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, norm_next->eps,
+                                norm_next->xn, norm_next->f16p, s));
+  else
+    MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
   return MOE_OK;
 }
 
@@ -452,7 +465,9 @@ static bool fused_norm_path(const moe_layer_t* L, int T) {
 static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
                               float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
                               void* ws, const Layout& lay, hipStream_t s, const float* norm_sq_in = nullptr,
-                              float* norm_sq_out = nullptr, bool x_f16_ready = false) {
+                              float* norm_sq_out = nullptr, bool x_f16_ready = false,
+                              const NormNext* norm_next = nullptr) {
+  if (norm_next && !medium_path_taken(L, T)) return MOE_EINVAL;   // only the 32-row GEMM path's combine writes it
   const int k = L->top_k, E = L->n_experts;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
   float* gates = topk_gates ? topk_gates : at<float>(ws, lay.gates);
@@ -566,7 +581,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   }
   if (medium_path_taken(L, T))
     return medium_path(L, L->routed, nullptr, x, T, residual, out, out_bf16, ids, gates, margin, ws, lay, s,
-                       x_f16_ready);
+                       x_f16_ready, nullptr, norm_next);
   if (n <= kSmallRouteMaxEntries) {
     // decode / MTP-verify batch: router, activation table, top-k and permutation in one launch
     SmallRouteArgs a;
@@ -653,6 +668,14 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
   // x (no separate norm launch); otherwise the norm runs on its own.
   bool have_sq = false;
   size_t sq_off = 0;
+  // Between two layers of one shape on the 32-row GEMM path, the first one's
+  // combine writes the second one's normalised input and its fp16 copy (same
+  // workspace layout, so those regions are free by then); no norm launch.
+  bool norm_done = false;
+  auto same_shape = [](const moe_layer_t& a, const moe_layer_t& b) {
+    return a.hidden == b.hidden && a.n_experts == b.n_experts && a.top_k == b.top_k && a.inter == b.inter &&
+           a.routed.fmt == b.routed.fmt && a.shared.fmt == b.shared.fmt;
+  };
   for (int l = 0; l < n_layers; ++l) {
     const Layout lay = make_layout(&layers[l], T);
     uint16_t* nxt = (l == n_layers - 1) ? x_out : at<uint16_t>(ws, (l % 2) ? lay.xb : lay.xa);
@@ -665,7 +688,9 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
     // on the 32-row GEMM path the norm also writes the GEMM's fp16 copy of its output
     const bool f16 = !norm_in && medium_path_taken(&layers[l], T) && layers[l].routed.fmt != MOE_FMT_BF16 &&
                      rmsnorm_f16_pairs_ok(layers[l].hidden);
-    if (!norm_in) {
+    if (norm_done) {
+      lin = at<uint16_t>(ws, lay.xn);
+    } else if (!norm_in) {
       uint16_t* xn = at<uint16_t>(ws, lay.xn);
       if (f16)
         MOE_TRY(launch_rmsnorm_bf16_f16pairs(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, at<uint16_t>(ws, lay.xf16), s));
@@ -673,9 +698,18 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
         MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
       lin = xn;
     }
+    NormNext nn;
+    const NormNext* next = nullptr;
+    if (f16 && l + 1 < n_layers && same_shape(layers[l], layers[l + 1]) && combine_norm_ok(layers[l].hidden)) {
+      nn.xn = at<uint16_t>(ws, lay.xn);
+      nn.f16p = at<uint16_t>(ws, lay.xf16);
+      nn.eps = MOE_RMS_EPS;
+      next = &nn;
+    }
     rc = layer_forward_impl(&layers[l], lin, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s,
-                            norm_in ? sq : nullptr, norm_out ? sq : nullptr, f16);
+                            norm_in ? sq : nullptr, norm_out ? sq : nullptr, f16, next);
     if (rc) return rc;
+    norm_done = next != nullptr;
     have_sq = norm_out;
     sq_off = lay.norm_sq;
     cur = nxt;

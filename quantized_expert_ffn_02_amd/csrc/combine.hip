@@ -18,14 +18,11 @@ namespace moe {
 // thread waits for one memory round trip per batch instead of one per entry.
 static constexpr int kCombineBatch = 12;
 
-__global__ __launch_bounds__(1024) void k_combine(const float* __restrict__ y_sorted,
-                                                 const int32_t* __restrict__ row_to_sorted,
-                                                 const float* __restrict__ gates, int T, int k, int H,
-                                                 int with_shared, const uint16_t* __restrict__ residual,
-                                                 float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
-  const int t = blockIdx.y;
-  const int q = blockIdx.x * blockDim.x + threadIdx.x;   // index of 4 consecutive outputs
-  if (q * 4 >= H) return;
+// Outputs 4q .. 4q + 3 of token row t: sum_i g_i y_i in rank order, the shared
+// expert's row, then the residual (bf16), in fp32.
+__device__ __forceinline__ float4 combine4(const float* __restrict__ y_sorted, const int32_t* __restrict__ row_to_sorted,
+                                           const float* __restrict__ gates, int T, int k, int H, int with_shared,
+                                           const uint16_t* __restrict__ residual, int t, int q) {
   const size_t H4 = H / 4;
   uint2 rb = make_uint2(0u, 0u);
   if (residual) rb = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[q];
@@ -62,7 +59,19 @@ __global__ __launch_bounds__(1024) void k_combine(const float* __restrict__ y_so
     acc.z += bf16_to_f32(rb.y & 0xFFFFu);
     acc.w += bf16_to_f32(rb.y >> 16);
   }
-  reinterpret_cast<float4*>(out)[(size_t)t * H4 + q] = acc;
+  return acc;
+}
+
+__global__ __launch_bounds__(1024) void k_combine(const float* __restrict__ y_sorted,
+                                                 const int32_t* __restrict__ row_to_sorted,
+                                                 const float* __restrict__ gates, int T, int k, int H,
+                                                 int with_shared, const uint16_t* __restrict__ residual,
+                                                 float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+  const int t = blockIdx.y;
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;   // index of 4 consecutive outputs
+  if (q * 4 >= H) return;
+  const float4 acc = combine4(y_sorted, row_to_sorted, gates, T, k, H, with_shared, residual, t, q);
+  reinterpret_cast<float4*>(out)[(size_t)t * (H / 4) + q] = acc;
   if (out_bf16) {
     uint2 o;
     o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
@@ -176,29 +185,65 @@ __device__ __forceinline__ float block_sum_fixed(float v, float* part, int nw) {
 // stack path uses; output rounded to bf16 (nearest even).
 // f16p (may be NULL): also the fp16 copy of the output in pair order (u32 j of
 // each 16-column group = columns j and j + 8, the grouped GEMM's A layout).
-__global__ __launch_bounds__(1024) void k_rmsnorm_bf16_g64(const uint16_t* __restrict__ x, int H, float eps,
-                                                           uint16_t* __restrict__ out, uint32_t* __restrict__ f16p) {
-  __shared__ float part[64];
-  const int row = blockIdx.x, lane = threadIdx.x & 63;
+// RMSNorm of one bf16 row (value of column c: get(c)) with the 64-column group
+// sums (rms_group_sum, lane = column, one wave per group) and their total
+// (rms_inv_from_groups, lane = group): out_row = bf16(x * inv); with f16p, also
+// the fp16 pair-order copy (columns c, c + 8 of each 16-column group in one word)
+// of row `row`.  Every thread of the block calls it; part holds G <= 64 floats.
+template <class Get>
+__device__ __forceinline__ void rms_norm_row_g64(Get get, int H, float eps, float* part, uint16_t* __restrict__ out_row,
+                                                 uint32_t* __restrict__ f16p, size_t row) {
+  const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int G = H / 64;
-  const uint16_t* __restrict__ xr = x + (size_t)row * H;
   for (int g = w; g < G; g += nw) {
-    const float s = rms_group_sum(bf16_to_f32(xr[64 * g + lane]));
+    const float s = rms_group_sum(get(64 * g + lane));
     if (lane == 0) part[g] = s;
   }
   __syncthreads();
   const float inv = rms_inv_from_groups(lane < G ? part[lane] : 0.0f, H, eps);
   for (int g = w; g < G; g += nw) {
-    const __bf16 o = (__bf16)(bf16_to_f32(xr[64 * g + lane]) * inv);
-    out[(size_t)row * H + 64 * g + lane] = __builtin_bit_cast(uint16_t, o);
+    const __bf16 o = (__bf16)(get(64 * g + lane) * inv);
+    out_row[64 * g + lane] = __builtin_bit_cast(uint16_t, o);
     if (f16p) {
       // column + 8 of the same 16-column group: rotate the 16-lane row by 8
       const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(float)o);
       const uint32_t h8 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x128, 0xF, 0xF, true);
-      if ((lane & 15) < 8) f16p[((size_t)row * H + 64 * g + lane) / 16 * 8 + (lane & 7)] = h | (h8 << 16);
+      if ((lane & 15) < 8) f16p[(row * H + 64 * g + lane) / 16 * 8 + (lane & 7)] = h | (h8 << 16);
     }
   }
+}
+
+__global__ __launch_bounds__(1024) void k_rmsnorm_bf16_g64(const uint16_t* __restrict__ x, int H, float eps,
+                                                           uint16_t* __restrict__ out, uint32_t* __restrict__ f16p) {
+  __shared__ float part[64];
+  const int row = blockIdx.x;
+  const uint16_t* __restrict__ xr = x + (size_t)row * H;
+  rms_norm_row_g64([&](int c) { return bf16_to_f32(xr[c]); }, H, eps, part, out + (size_t)row * H, f16p,
+                   (size_t)row);
+}
+
+// The combine of a stack layer followed by the next layer's RMSNorm of its bf16
+// result, one block of H / 4 threads per token row (H % 256 == 0, H <= 4096): the
+// row goes through LDS to the norm, which runs exactly as k_rmsnorm_bf16_g64.
+__global__ __launch_bounds__(1024) void k_combine_norm(const float* __restrict__ y_sorted,
+                                                      const int32_t* __restrict__ row_to_sorted,
+                                                      const float* __restrict__ gates, int T, int k, int H,
+                                                      int with_shared, const uint16_t* __restrict__ residual,
+                                                      float* __restrict__ out, uint16_t* __restrict__ out_bf16,
+                                                      float eps, uint16_t* __restrict__ xn, uint32_t* __restrict__ f16p) {
+  __shared__ float xs[4096];
+  __shared__ float part[64];
+  const int t = blockIdx.x, q = threadIdx.x;
+  const float4 acc = combine4(y_sorted, row_to_sorted, gates, T, k, H, with_shared, residual, t, q);
+  if (out) reinterpret_cast<float4*>(out)[(size_t)t * (H / 4) + q] = acc;
+  const uint32_t b0 = f32_to_bf16_rne(acc.x), b1 = f32_to_bf16_rne(acc.y);
+  const uint32_t b2 = f32_to_bf16_rne(acc.z), b3 = f32_to_bf16_rne(acc.w);
+  reinterpret_cast<uint2*>(out_bf16 + (size_t)t * H)[q] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+  *reinterpret_cast<float4*>(xs + 4 * q) = make_float4(bf16_to_f32(b0), bf16_to_f32(b1), bf16_to_f32(b2),
+                                                       bf16_to_f32(b3));
+  __syncthreads();
+  rms_norm_row_g64([&](int c) { return xs[c]; }, H, eps, part, xn + (size_t)t * H, f16p, (size_t)t);
 }
 
 __global__ __launch_bounds__(1024) void k_rmsnorm_bf16_v8(const uint16_t* __restrict__ x, int H, float eps,
@@ -258,6 +303,18 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint1
 }
 
 bool rmsnorm_f16_pairs_ok(int H) { return H % 64 == 0 && H / 64 <= 64; }
+
+bool combine_norm_ok(int H) { return H % 256 == 0 && H <= 4096; }
+
+hipError_t launch_combine_norm(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
+                               int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                               float eps, uint16_t* xn, uint16_t* f16p, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (!combine_norm_ok(H) || !out_bf16 || !xn) return hipErrorInvalidValue;
+  MOE_LAUNCH(k_combine_norm, dim3(T), dim3(H / 4), 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared,
+             residual, out, out_bf16, eps, xn, reinterpret_cast<uint32_t*>(f16p));
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm_bf16_f16pairs(const uint16_t* x, int T, int H, float eps, uint16_t* out, uint16_t* f16p,
                                         hipStream_t s) {

@@ -255,6 +255,14 @@ struct PackWords {
 };
 hipError_t launch_pack_words(const PackWords& p, uint32_t* dst, hipStream_t s);
 
+// The combine (as launch_combine, out may be NULL, out_bf16 required) followed by
+// the RMSNorm of its bf16 result into xn (and, if f16p, the fp16 pair-order copy),
+// bit for bit as launch_rmsnorm_bf16_f16pairs on out_bf16.  combine_norm_ok(H).
+bool combine_norm_ok(int H);
+hipError_t launch_combine_norm(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
+                               int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
+                               float eps, uint16_t* xn, uint16_t* f16p, hipStream_t s);
+
 // out[i] += y[i], i < n (both 16-byte aligned)
 hipError_t launch_add_f32(float* out, const float* y, size_t n, hipStream_t s);
 

@@ -264,3 +264,43 @@ def test_cache_adapts(fmt):
                 np.testing.assert_array_equal(got, hl.routed[n].view(np.uint8)[e * b:(e + 1) * b])
     print(f"{fmt}: hits per round {hits} of {T * k}")
     assert hits[0] == 0 and hits[-1] > hits[0]
+
+
+@pytest.mark.parametrize("T", [8, 32])
+def test_tiered_layer_q2_small(T):
+    # 2-bit weights end to end through the tiered layer: a small layer (H = 512, I = 256,
+    # 32 experts, top-4 + shared, Zipf routing) whose experts of popularity rank 2..9 are
+    # cached on the GPU; the host computes the rest, the two most popular among them (so
+    # every batch has misses).  T = 8 routes as a decode batch, T = 32 takes the 32-row
+    # GEMM path.
+    shape = synth.LayerShape(512, 32, 4, 256, True, "q2", 1.1)
+    H, I, E, k = shape.hidden, shape.inter, shape.n_experts, shape.top_k
+    hl = W.host_layer("cache", shape=shape)
+    w = synth.CONFIGS["cache"]
+    order = np.argsort(synth.zipf_ranks(w.seed, 0, E))[2:10]
+    pool = synth.bank(w.seed, 0, "q2", order, H, I)
+    slot_of = np.full((1, E), -1, dtype=np.int32)
+    slot_of[0, order] = np.arange(8, dtype=np.int32)
+    dpool = DeviceBank("q2", 8, H, I, pool)
+    hbank = B.make_host_bank("q2", E, H, I, hl.routed)
+    dl = DeviceLayer(H, E, k, I, hl.wr, hl.bias, dpool, DeviceBank("q2", 1, H, I, hl.shared))
+    x, _ = W.activations_with_margin(hl, T)
+    ws = dl.workspace(T)
+    host_ws = torch.empty(B.tiered_host_bytes(dl.struct, T), dtype=torch.uint8, pin_memory=True)
+    out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    n_miss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    print(f"tiered q2 T={T}", flush=True)
+    B.layer_forward_tiered(dl.struct, 0, 1, to_device(slot_of), dpool.struct, hbank, to_device(x), T, out, ids, gates,
+                           miss, n_miss, ws, host_ws)
+    torch.cuda.synchronize()
+    ref, ids_r, _, _ = hl.oracle_forward(x)
+    assert_route_matches(host(ids), host(gates), hl.logits(x), k, f"tiered q2 T={T}")
+    nm = int(host(n_miss)[0])
+    want = np.flatnonzero(slot_of[0][ids_r.reshape(-1)] < 0).astype(np.int32)
+    np.testing.assert_array_equal(host(miss)[:nm], want)
+    err = OL.rel_max_err(host(out), ref)
+    print(f"tiered q2 T={T}: misses {nm}/{T * k} on the host, max|err|/rms = {err:.3e}")
+    assert nm > 0 and err <= OUT_TOL

@@ -304,3 +304,35 @@ def test_tiered_layer_q2_small(T):
     err = OL.rel_max_err(host(out), ref)
     print(f"tiered q2 T={T}: misses {nm}/{T * k} on the host, max|err|/rms = {err:.3e}")
     assert nm > 0 and err <= OUT_TOL
+
+
+def test_cache_refill_moves_a_resident_expert():
+    # Moving an expert that already has a slot to another slot unmaps its old one (an
+    # expert never maps to two slots); experts not named keep their slots; the new slot
+    # holds the expert's exact bytes.
+    H, I, E, n_slots = 512, 256, 16, 4
+    fmt = "q2"
+    routed = synth.bank(9, 0, fmt, range(E), H, I)
+    host_t = {n: _pinned(v) for n, v in routed.items()}
+    g = host_t.get
+    hbank = B.make_bank(fmt, E, H, I, g("w13"), g("w13_hi"), g("w13_scale"), g("w2"), g("w2_hi"), g("w2_scale"))
+    per_expert = {n: len(v) // E for n, v in routed.items()}
+    dpool = DeviceBank(fmt, n_slots, H, I, {n: np.zeros(per_expert[n] * n_slots, dtype=v.dtype)
+                                            for n, v in routed.items()})
+    row = np.full(E, -1, dtype=np.int32)
+    row[3], row[5] = 0, 1
+    slot_of = to_device(row.reshape(1, E))
+    me, ms = np.array([3, 7], dtype=np.int32), np.array([2, 0], dtype=np.int32)   # 3: slot 0 -> 2; 7 into slot 0
+    ev = torch.cuda.Event()
+    ev.record()
+    B.cache_refill(hbank, dpool.struct, slot_of, 0, 1, E, me, ms, ev.cuda_event)
+    B.cache_commit(slot_of, 0, 1, E, n_slots, me, ms, ev.cuda_event)
+    torch.cuda.synchronize()
+    want = np.full(E, -1, dtype=np.int32)
+    want[3], want[5], want[7] = 2, 1, 0
+    np.testing.assert_array_equal(host(slot_of)[0], want)
+    for e, s in ((3, 2), (7, 0)):
+        for n, t in dpool.tensors.items():
+            b = per_expert[n] * routed[n].itemsize
+            np.testing.assert_array_equal(t.view(torch.uint8)[s * b:(s + 1) * b].cpu().numpy(),
+                                          routed[n].view(np.uint8)[e * b:(e + 1) * b])

@@ -153,6 +153,92 @@ def test_bf16_tiled_layout_hand_derived():
     np.testing.assert_array_equal(W, expect)
 
 
+# Expert slicing of a bank.  Three experts at H = 128, I = 128: per expert W13 is [2I, H] = [256, 128]
+# (gate rows 0..127, then up rows 128..255) and W2 is [H, I] = [128, 128].  Per expert that is, in the
+# 2-bit code plane, 256*128/4 = 8,192 bytes of W13 and 128*128/4 = 4,096 of W2; in fp16 scales 1,024 and
+# 512; in the 3-bit high plane 4,096 and 2,048 bytes; in bf16 32,768 and 16,384 elements.  Expert j starts
+# at j times those counts.  Every weight of the bank is 0 except five markers at positions worked out by
+# hand from the layout definitions (tile t = (n // 64) * (K // 64) + k // 64 with K = 128, so two tiles per
+# 64-row band):
+#
+#   marker                          W13/W2 (n, k)   tile   code byte in the matrix              bits
+#   A  expert 1, gate[5, 7]   = +1  W13 (5, 7)       0     0*1024 +  5*16 +  7//4 =   81        6-7
+#   B  expert 1, up[3, 70]    = -1  W13 (131, 70)    5     5*1024 +  3*16 +  6//4 = 5169        4-5
+#   C  expert 2, down[100, 33]= +2  W2  (100, 33)    2     2*1024 + 36*16 + 33//4 = 2632        2-3
+#   D  expert 2, gate[127,127]= -1  W13 (127, 127)   3     3*1024 + 63*16 + 63//4 = 4095        6-7
+#   E  expert 2, up[0, 0]     = +1  W13 (128, 0)     4     4*1024 +  0    +  0    = 4096        0-1
+#
+# Scales are 1.0 except B's block, 0.5: scale index ((131//64)*(128//128) + (70//32)//4)*256 + 3*4 + 2 = 526,
+# and C's block, 2.0: ((100//64)*1 + (33//32)//4)*256 + 36*4 + 1 = 401.
+# Q3 high bits (8 bytes per (tile, row); k % 64 = 16w + j -> bit 32(w//2) + 8(w%2) + j%8 + 16(j//8)):
+#   B  (131, 70): k%64 = 6 = 16*0 + 6 -> bit 6 of the word at 5*512 + 3*8 = 2584 -> byte 2584, bit 6
+#   D  (127, 127): k%64 = 63 = 16*3 + 15 -> bit 32 + 8 + 7 + 16 = 63 of the word at 3*512 + 63*8 = 2040
+#                  -> byte 2047, bit 7
+# bf16 elements ((n//64)*(K//8) + k//8)*512 + (n%64)*8 + k%8 with K//8 = 16:
+#   A (5, 7): 0*512 + 40 + 7 = 47          B (131, 70): (2*16 + 8)*512 + 24 + 6 = 20510
+#   C (100, 33): (16 + 4)*512 + 288 + 1 = 10529 (in W2)
+#   D (127, 127): (16 + 15)*512 + 504 + 7 = 16383      E (128, 0): (2*16)*512 = 16384
+
+_XM_H, _XM_I = 128, 128
+_XM_EXPECT = {   # (expert, matrix, row, col) -> value
+    (1, "gate", 5, 7): 1.0, (1, "up", 3, 70): -1.0, (2, "down", 100, 33): 2.0,
+    (2, "gate", 127, 127): -1.0, (2, "up", 0, 0): 1.0,
+}
+
+
+def _xm_bank(fmt):
+    n13_codes, n2_codes, n13_sc, n2_sc, n13_hi, n2_hi = 8192, 4096, 1024, 512, 4096, 2048
+    if fmt == "bf16":
+        w13 = np.zeros(3 * 32768, dtype=np.uint16)
+        w2 = np.zeros(3 * 16384, dtype=np.uint16)
+        w13[1 * 32768 + 47] = 0x3F80             # A +1
+        w13[1 * 32768 + 20510] = 0xBF80          # B -1
+        w2[2 * 16384 + 10529] = 0x4000           # C +2
+        w13[2 * 32768 + 16383] = 0xBF80          # D -1
+        w13[2 * 32768 + 16384] = 0x3F80          # E +1
+        return {"w13": w13, "w2": w2}
+    s13 = np.full(3 * n13_sc, 0x3C00, dtype=np.uint16)
+    s2 = np.full(3 * n2_sc, 0x3C00, dtype=np.uint16)
+    s13[1 * n13_sc + 526] = 0x3800               # B's block: 0.5
+    s2[2 * n2_sc + 401] = 0x4000                 # C's block: 2.0
+    if fmt == "q2":                               # code 2 everywhere (weight 0)
+        c13 = np.full(3 * n13_codes, 0xAA, dtype=np.uint8)
+        c2 = np.full(3 * n2_codes, 0xAA, dtype=np.uint8)
+        c13[1 * n13_codes + 81] = 0xEA           # A: bits 6-7 = 3 -> +1
+        c13[1 * n13_codes + 5169] = 0x8A         # B: bits 4-5 = 0 -> -2 * 0.5
+        c2[2 * n2_codes + 2632] = 0xAE           # C: bits 2-3 = 3 -> +1 * 2.0
+        c13[2 * n13_codes + 4095] = 0x6A         # D: bits 6-7 = 1 -> -1
+        c13[2 * n13_codes + 4096] = 0xAB         # E: bits 0-1 = 3 -> +1
+        return {"w13": c13, "w13_scale": s13, "w2": c2, "w2_scale": s2}
+    # q3: lo 0 and hi 1 everywhere (c = 4, weight 0)
+    c13 = np.zeros(3 * n13_codes, dtype=np.uint8)
+    c2 = np.zeros(3 * n2_codes, dtype=np.uint8)
+    h13 = np.full(3 * n13_hi, 0xFF, dtype=np.uint8)
+    h2 = np.full(3 * n2_hi, 0xFF, dtype=np.uint8)
+    c13[1 * n13_codes + 81] = 0x40               # A: lo 1, hi 1 -> c 5 -> +1
+    c13[1 * n13_codes + 5169] = 0x20             # B: lo 2 ...
+    h13[1 * n13_hi + 2584] = 0xBF                # ... hi 0 -> c 2 -> -2 * 0.5
+    c2[2 * n2_codes + 2632] = 0x04               # C: lo 1, hi 1 -> +1 * 2.0
+    c13[2 * n13_codes + 4095] = 0xC0             # D: lo 3 ...
+    h13[2 * n13_hi + 2047] = 0x7F                # ... hi 0 -> c 3 -> -1
+    c13[2 * n13_codes + 4096] = 0x01             # E: lo 1, hi 1 -> +1
+    return {"w13": c13, "w13_hi": h13, "w13_scale": s13, "w2": c2, "w2_hi": h2, "w2_scale": s2}
+
+
+@pytest.mark.parametrize("fmt", ["q2", "q3", "bf16"])
+def test_expert_matrices_slices_the_right_expert_and_projection(fmt):
+    bank = _xm_bank(fmt)
+    for j in range(3):
+        wg, wu, wd = F.expert_matrices(fmt, bank, _XM_H, _XM_I, j)
+        assert wg.shape == (_XM_I, _XM_H) and wu.shape == (_XM_I, _XM_H) and wd.shape == (_XM_H, _XM_I)
+        for name, m in (("gate", wg), ("up", wu), ("down", wd)):
+            expect = np.zeros(m.shape)
+            for (e, mat, r, c), v in _XM_EXPECT.items():
+                if e == j and mat == name:
+                    expect[r, c] = v
+            np.testing.assert_array_equal(m, expect, err_msg=f"{fmt} expert {j} {name}")
+
+
 def test_dequant_exact_for_every_fp16_scale_and_code():
     # 63,488 finite fp16 patterns = the blocks of a 64 x 31,744 matrix; each block's
     # 32 weights cycle through the four codes.  Expected values in exact rationals.
@@ -544,6 +630,25 @@ def _mutations():
     def ffn_dropped_up(x, wg, wu, wd):
         return Lm.silu(x @ wg.T) @ wd.T
 
+    orig_matrices = Fm.expert_matrices
+
+    def matrices_gate_up_swapped(fmt, tensors, H, I, j=0):
+        wg, wu, wd = orig_matrices(fmt, tensors, H, I, j)
+        return wu, wg, wd
+
+    def matrices_always_expert_0(fmt, tensors, H, I, j=0):
+        return orig_matrices(fmt, tensors, H, I, 0)
+
+    def matrices_scale_stride_off(fmt, tensors, H, I, j=0):
+        # expert j's fp16 scales read from the previous expert's block (a per-expert offset slip)
+        if fmt == "bf16" or j == 0:
+            return orig_matrices(fmt, tensors, H, I, j)
+        t = dict(tensors)
+        n13, n2 = 2 * I * H // 32, H * I // 32
+        t["w13_scale"] = np.concatenate([tensors["w13_scale"][n13:], tensors["w13_scale"][:n13]])
+        t["w2_scale"] = np.concatenate([tensors["w2_scale"][n2:], tensors["w2_scale"][:n2]])
+        return orig_matrices(fmt, t, H, I, j)
+
     return [
         (Fm, "q2_codes", codes_msb_first, [test_q2_layout_hand_derived, test_q2_layout_writer_reader_agree]),
         (Lm, "select_topk", topk_high_index, [test_topk_forced_tie_goes_to_lower_index]),
@@ -552,10 +657,18 @@ def _mutations():
         (Lm, "silu", silu_sign_slip, [test_silu_closed_forms, test_expert_ffn_closed_form]),
         (Lm, "expert_ffn", _swap_gate_up(orig_ffn), [test_expert_ffn_closed_form]),
         (Lm, "expert_ffn", ffn_dropped_up, [test_single_expert_layer_equals_dense_swiglu]),
+        (Fm, "expert_matrices", matrices_gate_up_swapped, [_xm_pin_all_formats]),
+        (Fm, "expert_matrices", matrices_always_expert_0, [_xm_pin_all_formats]),
+        (Fm, "expert_matrices", matrices_scale_stride_off, [_xm_pin_all_formats]),
     ]
 
 
-@pytest.mark.parametrize("case", range(7))
+def _xm_pin_all_formats():
+    for fmt in ("q2", "q3", "bf16"):
+        test_expert_matrices_slices_the_right_expert_and_projection(fmt)
+
+
+@pytest.mark.parametrize("case", range(10))
 def test_planted_mistakes_are_caught(case, monkeypatch):
     mod, name, bad, pins = _mutations()[case]
     monkeypatch.setattr(mod, name, bad)

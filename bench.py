@@ -68,31 +68,42 @@ def gateup_bytes_per_expert(H, I):
 
 
 def cpu_baseline(hl_args, T, seconds):
-    """The fp64 oracle (tests' reference implementation, untuned) on a bounded sample."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+    """The fp64 oracle (tests' reference implementation, untuned) on a bounded sample, single-threaded:
+    BLAS limited to one thread and the process pinned to one core for the duration (restored after)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import synth
     from oracle import formats as OF
     from oracle import layer as OL
     seed, shape, wr, routed, shared = hl_args
     H, I, k = shape.hidden, shape.inter, shape.top_k
-    smat = OF.expert_matrices(shape.fmt, shared, H, I)
-    t0 = time.perf_counter()
-    tokens, batches = 0, 0
-    while True:
-        x = synth.activations(seed + 7000, batches, T, H)
-        fn = OL.bank_expert_fn(shape.fmt, routed, H, I)      # fresh: every used expert is dequantised again
-        OL.layer_forward(x, wr, k, fn, lambda: smat)
-        tokens += T
-        batches += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    return {"value": tokens / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{batches} decode batches of T={T} tokens on layer 0 (fp64 numpy, experts dequantised on "
-                      f"demand), {el:.1f} s"}
+    n_cpus = os.cpu_count() or 1
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    os.sched_setaffinity(0, {core})
+    try:
+        with threadpool_limits(limits=1):
+            smat = OF.expert_matrices(shape.fmt, shared, H, I)
+            threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+            t0 = time.perf_counter()
+            tokens, batches = 0, 0
+            while True:
+                x = synth.activations(seed + 7000, batches, T, H)
+                fn = OL.bank_expert_fn(shape.fmt, routed, H, I)   # fresh: every used expert is dequantised again
+                OL.layer_forward(x, wr, k, fn, lambda: smat)
+                tokens += T
+                batches += 1
+                el = time.perf_counter() - t0
+                if el >= seconds:
+                    break
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cores_note": f"1 core of {n_cpus} (process pinned to core {core}, {len(allowed)} allowed; "
+                          f"BLAS threads during the run: {threads})",
+            "cpu_model": _cpu_model(),
+            "sample": f"{batches} decode batches of T={T} tokens on layer 0 of the decode workload (fp64 numpy, "
+                      f"experts dequantised on demand), {el:.1f} s"}
 
 
 def bench_prefill(steps):
@@ -716,7 +727,10 @@ def main():
                         f"{R} distinct layers rotated",
             "hidden": H, "experts": E, "top_k": k, "shared_experts": 1, "inter": I,
             "weights": "2-bit codes, 32-weight blocks, fp16 scales (1,536,000 B per expert)",
-            "arithmetic": "bf16 activations x exact 2-bit codes, fp32 accumulation, fp32 output",
+            "arithmetic": "2-bit codes enter the fp8 x fp4 block-scaled matrix cores exactly (fp4 c/2); bf16 x "
+                          "and fp32 h enter as four fixed-point e4m3 pieces per 32-column block (within 2^-19 of "
+                          "the block's largest magnitude); fp16 block scales applied in fp32; fp32 accumulation "
+                          "and output",
             "tokens": T, "layers_rotated": R,
         },
         "decode": {

@@ -62,7 +62,7 @@ bool has_shared(const moe_layer_t* L) { return L->shared.fmt != MOE_FMT_NONE; }
 struct Layout {
   size_t logits, rparts, ids, gates, margin;
   size_t counts, base, offsets, sorted_rows, row_to_sorted, items, n_items;
-  size_t xtab_pairs, xtab_init, xf32, xf16, hf16, tiles, n_tiles;
+  size_t xtab_pairs, xtab_init, xf32, xf16, xexp, hf16, tiles, n_tiles;
   size_t h, htab_pairs, htab_init, y;
   size_t xmx_data, xmx_exps, hmx_data, hmx_exps;   // fp8-piece tables (mx.h)
   size_t norm_sq;                                   // partial sums of squares of a stack layer's output
@@ -101,6 +101,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xtab_init = take(dense ? 0 : T * (H / 32) * 4);
   o.xf32 = take(dense ? T * H * 4 : 0);
   o.xf16 = take(dense ? 0 : T * H * 2);
+  o.xexp = take(dense ? 0 : T * 4);   // row exponents of the fp16 copy
   o.hf16 = take(dense ? 0 : n * I * 2);
   o.tiles = take((n / kSmallTileRows + E + 2) * 3 * 4);   // GEMM tiles (128 or 32 rows)
   o.n_tiles = take(4);
@@ -243,12 +244,14 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
   const bool gemm = gemm_tiles && !q3;
   const int max_tiles = gemm ? n_entries / gemm_tile_rows() + E + 2 : 0;
   uint16_t* hf = at<uint16_t>(ws, lay.hf16);
+  int32_t* xexp = at<int32_t>(ws, lay.xexp);
   if (gemm) {
     uint16_t* xf = at<uint16_t>(ws, lay.xf16);
-    MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
+    MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
     MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
       return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles,
-                            perm.sorted_rows, T, perm.k, xf, hf, s);
+                            perm.sorted_rows, T, perm.k, xf, hf, s, nullptr, nullptr, gemm_tile_rows(), false,
+                            nullptr, xexp);
     }));
   }
   if (!y16) {
@@ -260,7 +263,8 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
   if (gemm) {
     MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
       return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles,
-                            perm.sorted_rows, T, perm.k, hf, y_sorted, s, gates, y16);
+                            perm.sorted_rows, T, perm.k, hf, y_sorted, s, gates, y16, gemm_tile_rows(), false,
+                            nullptr, xexp);
     }));
   }
   if (y16) return MOE_OK;
@@ -425,14 +429,16 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   uint16_t* xf = at<uint16_t>(ws, lay.xf16);
   uint16_t* hf = at<uint16_t>(ws, lay.hf16);
   float* y = at<float>(ws, lay.y);
-  if (!x_f16_ready) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, s));
+  // the stack's normalised input comes with its fp16 copy unscaled (a = 0: rows of unit rms)
+  int32_t* xexp = x_f16_ready ? nullptr : at<int32_t>(ws, lay.xexp);
+  if (!x_f16_ready) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
-                          nullptr, nullptr, kSmallTileRows, q3, slot_map);
+                          nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp);
   }));
   MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
-                          nullptr, nullptr, kSmallTileRows, q3, slot_map);
+                          nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp);
   }));
   if (norm_next)
     MOE_TRY(launch_combine_norm(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, norm_next->eps,
@@ -632,7 +638,8 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
                          gemm ? at<int32_t>(ws, lay.n_tiles) : nullptr, nullptr, gates, y16);
   if (rc) return rc;
   if (y16)
-    MOE_TRY(launch_combine16(y16, inv, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
+    MOE_TRY(launch_combine16(y16, inv, T, k, L->hidden, with_shared, residual, out, out_bf16,
+                             at<int32_t>(ws, lay.xexp), s));
   else
     MOE_TRY(launch_combine(y, inv, gates, T, k, L->hidden, with_shared, residual, out, out_bf16, s));
   return MOE_OK;

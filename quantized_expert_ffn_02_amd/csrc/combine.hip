@@ -94,16 +94,19 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* row_to_sorted, c
 }
 
 // The same combine over fp16 rows that already carry their gate (the prompt
-// path's down GEMM writes them): out[t] = sum_i y16[row_to_sorted[t k + i]]
-// (i = 0..k-1) + y16[row_to_sorted[T k + t]] (+ residual), summed in fp32 in
-// that order.  Eight consecutive outputs per thread.
+// path's down GEMM writes them in the scale of their token's row, y 4^a):
+// out[t] = 4^-a (sum_i y16[row_to_sorted[t k + i]] (i = 0..k-1) +
+// y16[row_to_sorted[T k + t]]) (+ residual), summed in fp32 in that order.
+// Eight consecutive outputs per thread.
 __global__ __launch_bounds__(1024) void k_combine16(const uint16_t* __restrict__ y16,
                                                    const int32_t* __restrict__ row_to_sorted, int T, int k, int H,
                                                    int with_shared, const uint16_t* __restrict__ residual,
-                                                   float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+                                                   float* __restrict__ out, uint16_t* __restrict__ out_bf16,
+                                                   const int32_t* __restrict__ xexp) {
   const int t = blockIdx.y;
   const int q = blockIdx.x * blockDim.x + threadIdx.x;   // index of 8 consecutive outputs
   if (q * 8 >= H) return;
+  const int ue = xexp ? -2 * xexp[t] : 0;
   const size_t H8 = H / 8;
   float acc[8];
 #pragma unroll
@@ -131,6 +134,9 @@ __global__ __launch_bounds__(1024) void k_combine16(const uint16_t* __restrict__
       }
     }
   }
+  // the rows were computed for x 2^a: the sum is y 4^a
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = ldexpf(acc[j], ue);
   if (residual) {
     const uint32_t w[4] = {rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
@@ -153,13 +159,15 @@ __global__ __launch_bounds__(1024) void k_combine16(const uint16_t* __restrict__
 }
 
 hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,
-                            const uint16_t* residual, float* out, uint16_t* out_bf16, hipStream_t s) {
+                            const uint16_t* residual, float* out, uint16_t* out_bf16, const int32_t* xexp,
+                            hipStream_t s) {
   if (T <= 0) return hipSuccess;
   // one block per token row when it fits (no partly idle second block)
   const int threads = ((H / 8 + 63) / 64) * 64;
   const dim3 block(threads <= 1024 ? threads : 256);
   dim3 grid((H / 8 + block.x - 1) / block.x, T);
-  MOE_LAUNCH(k_combine16, grid, block, 0, s, y16, row_to_sorted, T, k, H, with_shared, residual, out, out_bf16);
+  MOE_LAUNCH(k_combine16, grid, block, 0, s, y16, row_to_sorted, T, k, H, with_shared, residual, out, out_bf16,
+             xexp);
   return hipGetLastError();
 }
 

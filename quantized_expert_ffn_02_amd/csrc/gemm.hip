@@ -10,11 +10,14 @@
 //
 // Precision: the weights are dequantised EXACTLY into fp16 (mfma.h: s (c - 2)
 // with an fp16 scale and c - 2 in {-2, -1, 0, 1} is an fp16 value; 3-bit
-// weights as two exact fragments), activations enter as fp16 (bf16 -> fp16 is
-// exact for normal values below 65504), products are exact and accumulate in
-// fp32 (v_mfma_f32_32x32x16_f16); h = SiLU(gate) * up is carried in fp16
-// between the two GEMMs.  The down projection writes fp32 rows, or, for a
-// prompt chunk, fp16 rows already multiplied by their gate.
+// weights as two exact fragments), activations enter as fp16 after a per-row
+// power-of-two scale (k_x_to_f16_rows: every bf16 value of at least 2^-17 of
+// its row's largest magnitude converts exactly, whatever that magnitude),
+// products are exact and accumulate in fp32 (v_mfma_f32_32x32x16_f16); h =
+// SiLU(gate) * up is carried in fp16 between the two GEMMs, in the row's
+// scale (h 4^a).  The down projection writes fp32 rows with the scale undone,
+// or, for a prompt chunk, fp16 rows in the row's scale already multiplied by
+// their gate (the combine undoes the scale).
 //
 // Operand order: the 2-bit unpacking yields weights in "pair order" -- inside
 // each aligned group of 16 columns the order is (0, 8, 1, 9, ..., 7, 15).  The
@@ -35,34 +38,66 @@ static constexpr int BM = 128, BN = 128, BK = 64;
 static constexpr int LDS_STRIDE = BK + 8;   // halves per LDS row (padding against bank conflicts)
 
 // ---------------------------------------------------------------------------
-// x (bf16) -> fp16 in pair order
+// x (bf16) -> fp16 in pair order, each row scaled by a power of two.
+//
+// fp16 holds a bf16 value exactly only between about 2^-17 and 65,504, so a
+// row is first scaled by 2^a, a = -floor(log2 max|x_row|): its largest
+// magnitude lands in [1, 2) and every element of at least 2^-17 of it converts
+// exactly (the rest are below the fp16 grid's 2^-25 rounding, far under the
+// products that matter).  The GEMMs work on x' = x 2^a and undo the scale in
+// fp32 (exact: a power of two): gate/up writes h' = g' u' sigma(g' 2^-a) =
+// h 4^a, the down projection y 4^-a.  Zero, inf or NaN maxima give a = 0.
+// One block of 256 threads per row: the row's largest magnitude from its bit
+// patterns (|x| orders as the low 15 bits of a finite bf16), then the scaled
+// conversion (the second read hits the cache).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_x_to_f16_pairs(const uint16_t* __restrict__ x, size_t n16,
-                                                        uint16_t* __restrict__ out) {
-  // one thread per 16-group
-  for (size_t g = (size_t)blockIdx.x * 256 + threadIdx.x; g < n16; g += (size_t)gridDim.x * 256) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + g * 16);
-    const uint4 a = src[0], b = src[1];
+__device__ __forceinline__ int bf16_row_exponent(uint32_t maxbits15) {
+  if (maxbits15 == 0u || maxbits15 >= 0x7F80u) return 0;      // zero row, or inf / NaN
+  const int be = (int)(maxbits15 >> 7);
+  const int e2 = be ? be - 127 : (31 - __builtin_clz(maxbits15 & 0x7Fu)) - 133;   // floor(log2 max)
+  return -e2;
+}
+
+__global__ __launch_bounds__(256) void k_x_to_f16_rows(const uint16_t* __restrict__ x, int H,
+                                                       uint16_t* __restrict__ out, int32_t* __restrict__ xexp) {
+  __shared__ uint32_t wmax[4];
+  const int row = blockIdx.x, n16 = H / 16;
+  const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)row * H);
+  uint32_t m = 0;
+  for (int g = threadIdx.x; g < n16; g += 256) {
+    const uint4 a = src[2 * g], b = src[2 * g + 1];
     const uint32_t in[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, max(in[j] & 0x7FFFu, (in[j] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const int a = bf16_row_exponent(m);
+  if (threadIdx.x == 0) xexp[row] = a;
+  uint4* dst = reinterpret_cast<uint4*>(out + (size_t)row * H);
+  for (int g = threadIdx.x; g < n16; g += 256) {
+    const uint4 va = src[2 * g], vb = src[2 * g + 1];
+    const uint32_t in[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
     uint32_t o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // column j (low half of in[j/2] if j even) and column j + 8
       const uint32_t v0 = (j & 1) ? (in[j >> 1] >> 16) : (in[j >> 1] & 0xFFFFu);
       const uint32_t v1 = (j & 1) ? (in[4 + (j >> 1)] >> 16) : (in[4 + (j >> 1)] & 0xFFFFu);
-      const _Float16 f0 = (_Float16)bf16_to_f32(v0), f1 = (_Float16)bf16_to_f32(v1);
+      const _Float16 f0 = (_Float16)ldexpf(bf16_to_f32(v0), a), f1 = (_Float16)ldexpf(bf16_to_f32(v1), a);
       o[j] = (uint32_t)__builtin_bit_cast(uint16_t, f0) | ((uint32_t)__builtin_bit_cast(uint16_t, f1) << 16);
     }
-    uint4* dst = reinterpret_cast<uint4*>(out + g * 16);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    dst[2 * g] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[2 * g + 1] = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
-hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s) {
-  const size_t n16 = (size_t)T * H / 16;
-  const int blocks = (int)((n16 + 255) / 256 < 2048 ? (n16 + 255) / 256 : 2048);
-  MOE_LAUNCH(k_x_to_f16_pairs, dim3(blocks), dim3(256), 0, s, x, n16, out);
+hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, int32_t* xexp, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  MOE_LAUNCH(k_x_to_f16_rows, dim3(T), dim3(256), 0, s, x, H, out, xexp);
   return hipGetLastError();
 }
 
@@ -93,6 +128,13 @@ static constexpr int GCOLS = 256;            // weight rows per block (4 waves x
 // row 32 mi + l % 32 and, in registers 4 q .. 4 q + 3, four consecutive output
 // columns 8 q + 4 (l / 32) + (0..3) -- the epilogue stores rows in 8- and
 // 16-byte pieces instead of 2-byte scatters.
+// h' = h 4^a from the accumulators g' = g 2^a, u' = u 2^a of a row scaled by 2^a:
+// SiLU(g) u 4^a = g' u' sigma(g), with g = g' 2^-a formed only inside sigma
+// (which saturates), so h' stays finite whatever the scale of x.
+__device__ __forceinline__ float swiglu_scaled(float gv, float uv, int a) {
+  return gv * uv / (1.0f + expf(-ldexpf(gv, -a)));
+}
+
 template <bool TR>
 __device__ __forceinline__ f16x_t mfma_op(h8_t a, h8_t b, f16x_t c) {
   return TR ? __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0)
@@ -221,6 +263,7 @@ struct GemmArgs {
   float* y_out;           // down, fp32 rows (NULL when y16 is used)
   uint16_t* y16;          // down, fp16 rows already multiplied by their entry's gate
   const float* row_gate;  // LDS: gate of each of the tile's rows (y16 only)
+  const int32_t* row_exp; // LDS: row exponent a of each of the tile's rows (x' = x 2^a; NULL: 0)
   uint32_t a_bytes;       // bytes of a_src, code and scale bytes of this expert
   uint32_t code_bytes, scale_bytes;
 };
@@ -428,14 +471,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
         const int row = mi * 32 + l32;
         if (row < t.rows) {
           uint16_t* dst = g.h_out + (size_t)(t.m0 + row) * g.I + hb;
+          const int ae = g.row_exp ? g.row_exp[row] : 0;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float hv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float gv = acc[mi][0][4 * q + j], uv = acc[mi][1][4 * q + j];
-              hv[j] = gv / (1.0f + expf(-gv)) * uv;
-            }
+            for (int j = 0; j < 4; ++j) hv[j] = swiglu_scaled(acc[mi][0][4 * q + j], acc[mi][1][4 * q + j], ae);
             *reinterpret_cast<u2v*>(dst + 8 * q) = u2v{pack2(hv[0], hv[1]), pack2(hv[2], hv[3])};
           }
         }
@@ -484,12 +525,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
         const int row = mi * 32 + l32;
         if (row < t.rows) {
           float* dst = g.y_out + (size_t)(t.m0 + row) * g.H + cb;
+          const int ue = g.row_exp ? -2 * g.row_exp[row] : 0;   // y = y' 4^-a
 #pragma unroll
           for (int f = 0; f < 2; ++f)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               *reinterpret_cast<f4v*>(dst + 32 * f + 8 * q) =
-                  f4v{acc[mi][f][4 * q], acc[mi][f][4 * q + 1], acc[mi][f][4 * q + 2], acc[mi][f][4 * q + 3]};
+                  f4v{ldexpf(acc[mi][f][4 * q], ue), ldexpf(acc[mi][f][4 * q + 1], ue),
+                      ldexpf(acc[mi][f][4 * q + 2], ue), ldexpf(acc[mi][f][4 * q + 3], ue)};
         }
       }
     }
@@ -505,8 +548,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
       for (int r = 0; r < 16; ++r) {
         const int row = mi * 32 + acc_row(r, lane);
         if (row < t.rows) {
-          const float gv = acc[mi][0][r], uv = acc[mi][1][r];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          const float hv = swiglu_scaled(acc[mi][0][r], acc[mi][1][r], g.row_exp ? g.row_exp[row] : 0);
           g.h_out[(size_t)(t.m0 + row) * g.I + pcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
         }
       }
@@ -530,7 +572,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = mi * 32 + acc_row(r, lane);
-          if (row < t.rows) g.y_out[(size_t)(t.m0 + row) * g.H + (f ? n1 : n0)] = acc[mi][f][r];
+          if (row < t.rows)
+            g.y_out[(size_t)(t.m0 + row) * g.H + (f ? n1 : n0)] =
+                ldexpf(acc[mi][f][r], g.row_exp ? -2 * g.row_exp[row] : 0);
         }
   }
 }
@@ -547,6 +591,7 @@ struct GemmKArgs {
   const float* gates;
   uint16_t* y16;
   const int32_t* slot_map;   // expert-cache mode: pool slot of routed group g, or -1 (a miss)
+  const int32_t* xexp;       // row exponent of each token (x' = x 2^a), or NULL (a = 0)
 };
 
 // One kernel per projection, tile height and format: MAXNMI = 4 (128-row
@@ -558,6 +603,7 @@ template <bool GATEUP, int MAXNMI, bool Q3>
 __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(GemmKArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[3 * 32 * MAXNMI * A_STRIDE];
   __shared__ float row_gate[32 * MAXNMI];
+  __shared__ int32_t row_exp[32 * MAXNMI];
   GemmTile t;
   if (!load_tile(a.tiles, a.n_tiles, t)) return;
   const bool sh = t.g == a.E;
@@ -580,6 +626,13 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(Ge
       row_gate[i] = r < a.T * a.k ? a.gates[r] : 1.0f;
     }
   }
+  if (a.xexp) {
+    // exponent of every row's token, read in the epilogue after the K loop's barriers
+    for (int i = threadIdx.x; i < t.rows; i += blockDim.x) {
+      const int r = a.sorted_rows[t.m0 + i];
+      row_exp[i] = a.xexp[r < a.T * a.k ? r / a.k : r - a.T * a.k];
+    }
+  }
   const MatRef& M = sh ? a.shared : a.routed;
   const size_t eidx = sh ? 0 : (size_t)slot;
   GemmArgs g;
@@ -596,6 +649,7 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(Ge
   g.y_out = a.y_out;
   g.y16 = a.y16;
   g.row_gate = row_gate;
+  g.row_exp = a.xexp ? row_exp : nullptr;
   // byte sizes of the buffer resources (the host checks that they fit 31 bits)
   g.a_bytes = GATEUP ? (uint32_t)a.T * (uint32_t)a.H * 2u : (uint32_t)(a.T * a.k + a.T) * (uint32_t)a.I * 2u;
   g.code_bytes = (uint32_t)M.code_stride;
@@ -631,7 +685,7 @@ static hipError_t launch_gemm_q2_t(GemvKind kind, GemmKArgs a, int max_tiles, vo
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
-                          uint16_t* y16, int tile_rows, bool q3, const int32_t* slot_map) {
+                          uint16_t* y16, int tile_rows, bool q3, const int32_t* slot_map, const int32_t* xexp) {
   if (max_tiles <= 0) return hipSuccess;
   // the kernels address activations and one expert's weights with 32-bit
   // buffer offsets
@@ -653,6 +707,7 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
   a.gates = gates;
   a.y16 = y16;
   a.slot_map = slot_map;
+  a.xexp = xexp;
   if (q3) {
     // 3-bit weights run on 32-row tiles only (the 128-row kernel's registers
     // have no room for the high-bit planes); y16 is not used with them

@@ -218,12 +218,13 @@ hipError_t launch_gemv_dense(GemvKind kind, const MatRef& routed, const MatRef& 
                              hipStream_t s);
 
 // MFMA path (gemm.hip)
-hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, hipStream_t s);
+// x' = x 2^a per row (a = -floor(log2 max|x_row|), written to xexp[T]) as fp16 in pair order
+hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, int32_t* xexp, hipStream_t s);
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates = nullptr,
                           uint16_t* y16 = nullptr, int tile_rows = 128, bool q3 = false,
-                          const int32_t* slot_map = nullptr);
+                          const int32_t* slot_map = nullptr, const int32_t* xexp = nullptr);
 // rows per tile of the grouped GEMM for batches beyond a decode step and below a prompt chunk
 static constexpr int kSmallTileRows = 32;
 // router of such batches (router_split.hip): 32 tokens x 64 experts per unit, K split over
@@ -232,10 +233,12 @@ static constexpr int kSmallTileRows = 32;
 int router_parts(int T, int E, int H);
 hipError_t launch_router_split(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                                float* out, int parts, hipStream_t s);
-// out[t] = sum over the token's entries of the gate-scaled fp16 rows y16 (rank
-// order, then the shared expert) (+ residual), fp32, optional bf16 copy
+// out[t] = 4^-a_t (sum over the token's entries of the gate-scaled fp16 rows y16,
+// rank order, then the shared expert) (+ residual), fp32, optional bf16 copy;
+// a_t = xexp[t] is the row exponent the rows were computed in (xexp NULL: 0)
 hipError_t launch_combine16(const uint16_t* y16, const int32_t* row_to_sorted, int T, int k, int H, int with_shared,
-                            const uint16_t* residual, float* out, uint16_t* out_bf16, hipStream_t s);
+                            const uint16_t* residual, float* out, uint16_t* out_bf16, const int32_t* xexp,
+                            hipStream_t s);
 hipError_t launch_plan(const int32_t* offsets, int E, int min_rows, int items_per, int32_t* tiles,
                        int32_t* n_tiles, int32_t* items, int32_t* n_items, hipStream_t s, int tile_rows = 0);
 int gemm_tile_rows();

@@ -41,6 +41,30 @@ def test_q3_layer_forward(T):
     assert err <= OUT_TOL
 
 
+def test_q3_gemm_extreme_activations():
+    # 3-bit weights on the 32-row grouped GEMM (T = 64) with rows rescaled over bf16's
+    # range (x1e5, x1e12, x2^-20, x2^-40, tiny blocks, one large value among tiny ones):
+    # each row enters the fp16 products scaled by a power of two, undone in fp32.
+    from tests.test_gpu_parity import _extreme_rows
+    hl = W.host_layer("cache")
+    T = 64
+    x0, _ = W.activations_with_margin(hl, T)
+    rows = list(range(3, 10))
+    x = x0.copy()
+    x[rows] = _extreme_rows(x0[rows], rows=range(7), H=hl.H)
+    assert (OL.topk_margin(hl.logits(x), hl.shape.top_k) >= 1e-4).all()
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    assert np.isfinite(out).all()
+    assert_route_matches(ids, gates, hl.logits(x), hl.shape.top_k, "q3 extreme")
+    ref, *_ = hl.oracle_forward(x)
+    for t in range(T):
+        err = OL.rel_max_err(out[t], ref[t])
+        if t in rows:
+            print(f"q3 extreme row {t}: max|err|/rms = {err:.3e}")
+        assert err <= OUT_TOL, f"row {t}"
+
+
 @pytest.mark.parametrize("layer", [0, 17, 47])
 def test_cached_layer(pool, layer):
     slot_of, hpool, dpool = pool

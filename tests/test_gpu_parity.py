@@ -27,6 +27,30 @@ def setup_module(module):
     B.lib()
 
 
+# Host layers shared by the tests of this module: the oracle dequantises each used
+# expert once per layer object and keeps it, so the prompt-sized compares reuse it.
+_LAYERS = {}
+
+
+def shared_host_layer(name):
+    if name not in _LAYERS:
+        _LAYERS[name] = W.host_layer(name)
+    return _LAYERS[name]
+
+
+_PROMPT = {}
+
+
+def prompt_case(T):
+    """The prefill layer, T margin-checked tokens and the oracle's output for them (computed once)."""
+    if T not in _PROMPT:
+        hl = shared_host_layer("prefill")
+        x, _ = W.activations_with_margin(hl, T)
+        ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+        _PROMPT[T] = (hl, x, ref, ids_r, gates_r)
+    return _PROMPT[T]
+
+
 def host(t):
     a = t.detach().cpu().numpy()
     return a.view(np.uint16) if a.dtype == np.int16 else a
@@ -252,11 +276,26 @@ def test_layer_forward_residual_and_determinism(workload, T):
     assert OL.rel_max_err(out1, ref) <= OUT_TOL
 
 
-def test_steps_match_fused_layer():
-    # route -> permute -> expert FFN -> combine through the separate entry points
-    hl = W.host_layer("decode")
-    T = 4
-    x, _ = W.activations_with_margin(hl, T)
+def oracle_rows_by_group(hl, x, ids, off, srt):
+    """The oracle's FFN output of every entry, in sorted order (one product per group of the permutation)."""
+    from oracle import formats as OF
+    T, k = ids.shape
+    E, H = hl.shape.n_experts, hl.H
+    x64 = OF.bf16_to_f64(x)
+    fn, sfn = hl.expert_fn(), hl.shared_fn()
+    y = np.empty((len(srt), H))
+    for g in range(E + 1):
+        a, b = int(off[g]), int(off[g + 1])
+        if a == b:
+            continue
+        r = srt[a:b].astype(np.int64)
+        tok = np.where(r < T * k, r // k, r - T * k)
+        y[a:b] = OL.expert_ffn(x64[tok], *(fn(g) if g < E else sfn()))
+    return y
+
+
+def run_steps(hl, x, T):
+    """route -> permute -> expert FFN -> combine through the four step entry points."""
     d = W.upload(hl)
     k, E, H = hl.shape.top_k, hl.shape.n_experts, hl.H
     ws = d.workspace(T)
@@ -268,36 +307,59 @@ def test_steps_match_fused_layer():
     off = torch.empty(E + 2, dtype=torch.int32, device="cuda")
     srt = torch.empty(n, dtype=torch.int32, device="cuda")
     inv = torch.empty(n, dtype=torch.int32, device="cuda")
-    ws2 = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    ws2 = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     B.permute(ids, T, k, E, True, off, srt, inv, ws2)
     y = torch.empty((n, H), dtype=torch.float32, device="cuda")
     B.expert_ffn_q2(d.struct, xd, T, off, srt, y, ws)
     out = torch.empty((T, H), dtype=torch.float32, device="cuda")
     B.combine(y, inv, gates, T, k, H, True, None, out)
     torch.cuda.synchronize()
-    # every expert row against the oracle FFN of that (token, expert)
-    ids_h, srt_h, y_h = host(ids), host(srt), host(y)
-    x64 = __import__("oracle").formats.bf16_to_f64(x)
-    fn, sfn = hl.expert_fn(), hl.shared_fn()
-    for p, r in enumerate(srt_h):
-        if r < T * k:
-            t, e = divmod(int(r), k)[0], int(ids_h.reshape(-1)[r])
-            ref = OL.expert_ffn(x64[t:t + 1], *fn(e))[0]
-        else:
-            t = int(r) - T * k
-            ref = OL.expert_ffn(x64[t:t + 1], *sfn())[0]
-        assert OL.rel_max_err(y_h[p], ref) <= OUT_TOL, f"row {p}"
-    ref_out, *_ = hl.oracle_forward(x)
-    assert OL.rel_max_err(host(out), ref_out) <= OUT_TOL
-    # The fused layer addresses a decode batch's entries directly (top-k inside
-    # the gate/up launch) and runs its 2-bit products on the fp8 x fp4 matrix
-    # cores: x and h enter as four fixed-point e4m3 pieces per 32-column block,
-    # exact to 2^-19 of the block's largest magnitude.  For h (largest / rms of
-    # a block about 4) that is about 2^-19 * 4 / sqrt(3) ~ 4e-6 relative per
-    # element; over 2,560 output rows the largest deviation is a few times
-    # that, so the two paths agree to well under 4e-5 (max |diff| / rms).
-    out_f, *_ = run_layer(d, x, T)
-    assert OL.rel_max_err(host(out), out_f.astype(np.float64)) <= 4e-5
+    return d, host(ids), host(gates), host(off), host(srt), host(inv), host(y), host(out)
+
+
+@pytest.mark.parametrize("workload,T", [("decode", 4), ("prefill", 300), ("prefill", 8192)])
+def test_steps_match_oracle(workload, T):
+    # The four step calls at a decode batch (GEMV work items), a verify-sized batch of
+    # Zipf-routed tokens (3,600 entries: groups of 32 or more on the 128-row grouped GEMM,
+    # the rest on the GEMV) and a prompt chunk (90,112 entries, every group on the
+    # GEMM).  Every y_sorted row is compared with the oracle's FFN of its (token,
+    # expert); the combine output with the oracle's combine of those rows.
+    if workload == "prefill":
+        hl, x, _, _, _ = prompt_case(T)
+    else:
+        hl = shared_host_layer(workload)
+        x, _ = W.activations_with_margin(hl, T)
+    k, E = hl.shape.top_k, hl.shape.n_experts
+    d, ids, gates, off, srt, inv, y, out = run_steps(hl, x, T)
+    logits = hl.logits(x)
+    assert_route_matches(ids, gates, logits, k, f"steps T={T}")
+    o_r, s_r, i_r = OL.permute(ids, E, True)
+    np.testing.assert_array_equal(off, o_r)
+    np.testing.assert_array_equal(srt, s_r)
+    np.testing.assert_array_equal(inv, i_r)
+    y_ref = oracle_rows_by_group(hl, x, ids, off, srt)
+    err_y = OL.rel_max_err(y, y_ref)
+    ids_r = OL.select_topk(logits, k)
+    ref_out = OL.combine(y_ref, i_r, OL.renormalised_gates(logits, ids), True)
+    err_o = OL.rel_max_err(out, ref_out)
+    counts = np.diff(off)
+    print(f"steps {workload} T={T}: y_sorted max|err|/rms = {err_y:.3e} over {len(srt)} rows, "
+          f"combine {err_o:.3e}; groups of >= 32 rows: {(counts[:E] >= 32).sum()}")
+    assert err_y <= OUT_TOL
+    assert err_o <= OUT_TOL
+    if T <= 16:
+        # The fused layer addresses a decode batch's entries directly and runs its
+        # 2-bit products on the fp8 x fp4 matrix cores: x and h enter as four
+        # fixed-point e4m3 pieces per 32-column block, within 2^-19 of the block's
+        # largest magnitude (the step path here computes on exact bf16 pairs).  For
+        # h, whose block maximum is about 4 rms, that is at most 2^-19 * 4 ~ 7.6e-6
+        # of an element's rms, and a rounding error spread uniformly has an rms of
+        # 1/sqrt(3) of its bound; each output sums 640 such terms with random signs,
+        # so its deviation has an rms of about 4.4e-6 of the output's rms, and the
+        # largest over the 10,240 outputs lies near 4 of those, 1.8e-5 (the x pieces
+        # add a term of the same form, an order smaller: x blocks have max/rms ~ 2).
+        out_f, *_ = run_layer(d, x, T)
+        assert OL.rel_max_err(out, out_f.astype(np.float64)) <= 2e-5
 
 
 # ------------------------------------------------------------------ prefill (MFMA grouped GEMM)
@@ -319,30 +381,111 @@ def test_gemm_path_medium_full_compare():
     assert err <= OUT_TOL
 
 
-def test_prefill_8192_sampled():
-    # the full prefill chunk; top-k checked for every token, outputs on a sample
-    # of tokens recomputed one by one by the oracle
-    hl = W.host_layer("prefill")
-    T = 8192
-    x, _ = W.activations_with_margin(hl, T)
+@pytest.mark.parametrize("T", [1024, 3000, 8192])
+def test_prompt_chunk_full_compare(T):
+    # Prompt-sized chunks (T >= 1,024: every group on the 128-row grouped GEMM, the
+    # gate-scaled fp16 rows and their combine), Zipf-routed, compared with the oracle
+    # over the whole [T, H] output.  T = 3,000 and 8,192 leave ragged tail tiles in hot
+    # groups; 8,192 is the pages' largest chunk.
+    hl, x, ref, ids_r, gates_r = prompt_case(T)
     d = W.upload(hl)
     out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
-    logits = hl.logits(x)
-    assert_route_matches(ids, gates, logits, hl.shape.top_k, "prefill T=8192")
+    assert_route_matches(ids, gates, hl.logits(x), hl.shape.top_k, f"prompt T={T}")
     counts = np.bincount(ids.reshape(-1), minlength=hl.shape.n_experts)
-    hot = np.argsort(-counts)[:3]
-    cold = np.flatnonzero((counts > 0) & (counts < 32))
-    rng = np.random.default_rng(5)
-    pick = set(rng.choice(T, 24, replace=False).tolist())
-    for e in list(hot) + list(cold[:8]):                 # tokens of hot (MFMA) and cold (GEMV) experts
-        pick.update(np.flatnonzero((ids == e).any(axis=1))[:3].tolist())
-    pick = np.array(sorted(pick))
-    ref, ids_r, _, _ = hl.oracle_forward(x[pick])
-    np.testing.assert_array_equal(np.sort(ids[pick], axis=1), np.sort(ids_r, axis=1))
-    err = OL.rel_max_err(out[pick], ref)
-    print(f"prefill T=8192: {len(pick)} sampled tokens, max|err|/rms = {err:.3e}; "
-          f"experts >= 32 rows: {(counts >= 32).sum()}, empty: {(counts == 0).sum()}")
+    full = counts[counts > 0]
+    assert (full % 128 != 0).sum() >= 3 and (full > 128).sum() >= 3      # ragged tails of multi-tile groups
+    err = OL.rel_max_err(out, ref)
+    print(f"prompt T={T}: max|err|/rms = {err:.3e} over the whole [T, H] output; "
+          f"non-empty groups {len(full)}, largest {counts.max()}, empty {(counts == 0).sum()}")
     assert err <= OUT_TOL
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
+def _extreme_rows(x, rows, H):
+    """x with rows rescaled over bf16's range: whole rows x1e5, x1e12, x2^-20, x2^-40; blocks of
+    2^-24 inside a normal row; one value of 100 among values of 2^-30; alternating 1e4 and 1e-4."""
+    from oracle import formats
+    xf = formats.bf16_to_f64(x).astype(np.float32)
+    r = list(rows)
+    xf[r[0]] *= 1e5
+    xf[r[1]] *= 1e12
+    xf[r[2]] *= 2.0 ** -20
+    xf[r[3]] *= 2.0 ** -40
+    for b in range(0, H // 32, 3):
+        xf[r[4], 32 * b:32 * b + 32] *= 2.0 ** -24
+    xf[r[5]] = np.float32(2.0 ** -30) * np.sign(xf[r[5]])
+    xf[r[5], 7] = 100.0
+    xf[r[6]] = np.where(np.arange(H) % 2 == 0, 1e4, 1e-4).astype(np.float32) * np.sign(xf[r[6]])
+    return synth.f32_to_bf16_bits(xf)
+
+
+@pytest.mark.parametrize("T", [64, 8192])
+def test_gemm_paths_extreme_activations(T):
+    # The grouped-GEMM paths (32-row tiles at T = 64, the prompt chunk at 8,192) take
+    # any bf16 activation: each row enters the fp16 products scaled by a power of two
+    # that puts its largest magnitude in [1, 2), and the scale is undone in fp32.
+    # Rows scaled by 1e5 and 1e12 (whose h would overflow fp16 unscaled) and by 2^-20,
+    # 2^-40 (whose elements would fall under fp16's range) are compared one by one.
+    if T == 8192:
+        hl, x0, ref0, _, _ = prompt_case(T)
+    else:
+        hl = shared_host_layer("prefill")
+        x0, _ = W.activations_with_margin(hl, T)
+        ref0 = None
+    rows = list(range(3, 3 + 7))
+    x = x0.copy()
+    x[rows] = _extreme_rows(x0[rows], rows=range(7), H=hl.H)
+    logits = hl.logits(x)
+    m = OL.topk_margin(logits, hl.shape.top_k)
+    assert (m >= 1e-4).all(), f"router margin of the rescaled rows: {m[rows]}"
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    assert np.isfinite(out).all()
+    assert_route_matches(ids, gates, logits, hl.shape.top_k, f"extreme T={T}")
+    ref_rows, *_ = hl.oracle_forward(x[rows])
+    for j, t in enumerate(rows):
+        err = OL.rel_max_err(out[t], ref_rows[j])
+        print(f"extreme T={T} row {t}: max|err|/rms = {err:.3e} (rms {np.sqrt(np.mean(ref_rows[j] ** 2)):.3e})")
+        assert err <= OUT_TOL
+    others = np.setdiff1d(np.arange(T), rows)
+    if ref0 is None:
+        ref0, *_ = hl.oracle_forward(x0)
+    err = OL.rel_max_err(out[others], ref0[others])
+    print(f"extreme T={T}: the other rows max|err|/rms = {err:.3e}")
+    assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("T", [1, 4, 64, 8192])
+def test_layer_forced_tie(T):
+    # Three identical router rows (17, 300, 301) with the largest bias give exactly
+    # equal logits for every token: the fused layer must select them in index order
+    # with equal gates at every batch size (the top-k inside the decode gate/up
+    # launch at T = 1, 4; split-K router planes + bias at 64; the MFMA router at 8,192).
+    # The bias lead of 20 is 14 standard deviations of the router's x . Wr noise
+    # difference (about 1.43 here), so no other expert overtakes the trio even
+    # over 8,192 tokens.
+    hl = shared_host_layer("prefill")
+    wr = hl.wr.copy()
+    wr[300] = wr[17]
+    wr[301] = wr[17]
+    bias = hl.bias.copy()
+    bias[300] = bias[17] = bias[301] = bias.max() + 20.0
+    hl2 = W.HostLayer(hl.seed, 0, hl.shape, wr, bias, hl.routed, hl.shared)
+    x = synth.activations(99, 0, T, hl.H)
+    d = W.upload(hl2)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    assert (ids[:, 0] == 17).all() and (ids[:, 1] == 300).all() and (ids[:, 2] == 301).all()
+    assert (gates[:, 0] == gates[:, 1]).all() and (gates[:, 1] == gates[:, 2]).all()
+    # the rest of each token's selection matches the oracle's (ties to the lower index)
+    logits = OL.router_logits(x, wr, bias)
+    ids_r = OL.select_topk(logits, hl.shape.top_k)
+    np.testing.assert_array_equal(ids_r[:, :3], np.tile([17, 300, 301], (T, 1)))
+    m = OL.topk_margin(logits, hl.shape.top_k)
+    ok = m >= 1e-4
+    for t in np.flatnonzero(ok):
+        assert set(ids[t].tolist()) == set(ids_r[t].tolist()), f"token {t}"
+    g_r = OL.renormalised_gates(logits, ids_r)
+    np.testing.assert_allclose(gates[:, :3], g_r[:, :3], rtol=0, atol=GATE_TOL)
 
 
 def test_graph_replay_matches_eager():

@@ -77,7 +77,8 @@ enum {
   MOE_EINVAL = -1,        /* null pointer, non-positive size, k > E, bad shape */
   MOE_EUNSUPPORTED = -2,  /* format or shape this build has no kernel for */
   MOE_EWORKSPACE = -3,    /* workspace missing, misaligned or too small */
-  MOE_EHIP = -4           /* a HIP launch reported an error */
+  MOE_EHIP = -4,          /* a HIP launch reported an error */
+  MOE_ESCRATCH = -5       /* the batch needs more than the built-in scratch (moe_layer_forward_noalloc) */
 };
 
 enum { MOE_FMT_NONE = -1, MOE_FMT_BF16 = 0, MOE_FMT_Q2 = 1, MOE_FMT_Q3 = 2 };
@@ -163,6 +164,25 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
 int moe_layer_forward(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
                       float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates,
                       float* margin, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, kernels and results as moe_layer_forward; the
+ * workspace is a built-in device array of MOE_NOALLOC_SCRATCH_BYTES, one per GPU,
+ * held from the library's first call of this function on that GPU until the process
+ * ends.  It covers every batch whose moe_workspace_bytes() fits (at H = 2,560,
+ * I = 640, 512 experts, top-10 + shared: up to T = 128 tokens in the 2-bit and the
+ * 3-bit format); larger batches return MOE_ESCRATCH before anything is enqueued.
+ * The scratch of the CURRENT device is used, so ``stream`` must belong to it.  The
+ * call allocates nothing (no hipMalloc, no library allocation); the scratch's address
+ * is looked up once per device, on the first call made with that device current.
+ * Every call on one GPU shares that GPU's scratch and leaves its last contents there
+ * (no part of it has to start at zero): calls that overlap on one GPU race, so
+ * serialise them (one stream, or events). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+int moe_layer_forward_noalloc(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
+                              float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates,
+                              float* margin, void* stream);
 
 /* Parameter-free RMSNorm of each bf16 row: out = bf16(x / sqrt(mean(x^2) + eps)),
  * rounded to nearest even, fp32 arithmetic; x, out bf16 [T x H] (may not overlap). */

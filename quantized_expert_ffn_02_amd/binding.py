@@ -10,7 +10,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 40 << 20
 FMT_NONE, FMT_BF16, FMT_Q2, FMT_Q3 = -1, 0, 1, 2
 FMT_BY_NAME = {"bf16": FMT_BF16, "q2": FMT_Q2, "q3": FMT_Q3}
 WS_CONTROL_BYTES = 65536
@@ -47,6 +48,8 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _sz, _vp]),
+    "moe_layer_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Layer), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp]),
     "moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_forward_cached": (ctypes.c_int, [ctypes.POINTER(Layer), _i32, _i32, _vp, ctypes.POINTER(Bank), _vp,
                                                 _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -174,6 +177,13 @@ def layer_forward(layer, x, T, out, ws, residual=None, out_bf16=None, topk_ids=N
     _check("moe_layer_forward", lib().moe_layer_forward(
         ctypes.byref(layer), ptr(x), int(T), ptr(residual), ptr(out), ptr(out_bf16), ptr(topk_ids),
         ptr(topk_gates), ptr(margin), ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer_forward_noalloc(layer, x, T, out, residual=None, out_bf16=None, topk_ids=None, topk_gates=None,
+                          margin=None, stream=None):
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        ctypes.byref(layer), ptr(x), int(T), ptr(residual), ptr(out), ptr(out_bf16), ptr(topk_ids),
+        ptr(topk_gates), ptr(margin), _stream(stream)))
 
 
 def stack_forward(layers, x0, T, x_out, ws, out_last=None, stream=None):

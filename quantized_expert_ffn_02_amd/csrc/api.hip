@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <functional>
+#include <mutex>
 
 #include "internal.h"
 #include "mx.h"
@@ -310,6 +311,7 @@ const char* moe_strerror(int code) {
     case MOE_EUNSUPPORTED: return "unsupported format or shape";
     case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_EHIP: return "HIP launch error";
+    case MOE_ESCRATCH: return "batch needs more than the built-in scratch of moe_layer_forward_noalloc";
     default: return "unknown status";
   }
 }
@@ -653,6 +655,51 @@ int moe_layer_forward(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
   if (!x || !out || T <= 0) return MOE_EINVAL;
   const Layout lay = make_layout(L, T);
   if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
+  return layer_forward_impl(L, x, T, residual, out, out_bf16, topk_ids, topk_gates, margin, ws, lay,
+                            (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// Workspace of moe_layer_forward_noalloc: one array per GPU in the library's code
+// object, so using it needs no allocation.  Host code never passes the array's name
+// to a kernel (in host code it is a stand-in, not a device address): it looks up
+// each device's own address once with hipGetSymbolAddress and uses that.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch of the current device (looked up on the first call with it current).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward_noalloc(const moe_layer_t* L, const uint16_t* x, int32_t T, const uint16_t* residual,
+                              float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
+                              void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!x || !out || T <= 0) return MOE_EINVAL;
+  const Layout lay = make_layout(L, T);
+  if (lay.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ESCRATCH;
+  void* ws = nullptr;
+  if ((rc = current_scratch(&ws))) return rc;
   return layer_forward_impl(L, x, T, residual, out, out_bf16, topk_ids, topk_gates, margin, ws, lay,
                             (hipStream_t)stream);
 }

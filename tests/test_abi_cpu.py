@@ -181,3 +181,20 @@ def test_host_tier_and_cache_entry_points_validate(lib):
     assert lib.moe_expert_usage(FAKE, 10, 512, FAKE, 32, None) == B.MOE_EINVAL
     assert lib.moe_expert_usage(None, 10, 512, FAKE, 0, None) == B.MOE_EINVAL
     assert lib.moe_expert_usage(FAKE, 10, 512, None, 0, None) == B.MOE_EINVAL
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    # Checked on the host before the scratch is looked up: invalid arguments, and a
+    # batch whose workspace exceeds the built-in scratch (a real-shape 2-bit layer
+    # fits up to T = 128 tokens, not T = 256).
+    L = q2_layer()
+    def call(T=1, x=FAKE, out=FAKE):
+        return lib.moe_layer_forward_noalloc(ctypes.byref(L), x, T, None, out, None, None, None, None, None)
+    assert call(T=0) == B.MOE_EINVAL
+    assert call(x=None) == B.MOE_EINVAL
+    assert call(out=None) == B.MOE_EINVAL
+    assert B.workspace_bytes(L, 128) <= B.NOALLOC_SCRATCH_BYTES < B.workspace_bytes(L, 256)
+    assert B.workspace_bytes(q2_layer(fmt="q3"), 128) <= B.NOALLOC_SCRATCH_BYTES
+    assert call(T=256) == B.MOE_ESCRATCH
+    assert call(T=8192) == B.MOE_ESCRATCH
+    assert "scratch" in B.strerror(B.MOE_ESCRATCH)

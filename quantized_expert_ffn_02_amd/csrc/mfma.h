@@ -12,7 +12,11 @@
 // codes sit at bits 2q and 16 + 2q of the code word shifted right by 8h.  OR-ing
 // a code under the exponent of 1024 gives the fp16 value 1024 + c 4^q; one
 // v_pk_fma_f16 turns it into c - 2 and one v_pk_mul_f16 applies the block scale,
-// both exact (c - 2 in {-2, -1, 0, 1} times an fp16 scale is an fp16 value).
+// both exact: c - 2 in {-2, -1, 0, 1} times an fp16 scale s is an fp16 value
+// as long as |s| <= 32,752 (beyond that, -2 s overflows to infinity; the
+// decode kernels, which apply the scale in fp32, have no such limit).  3-bit
+// weights enter as two fragments, s (lo - 2) and s (4 hi - 2) = +-2 s, with the
+// same limit.
 #pragma once
 
 #include <math.h>

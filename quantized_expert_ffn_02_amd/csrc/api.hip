@@ -398,7 +398,8 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
 // The next stack layer's normalised input, written by this layer's combine.
 struct NormNext {
   uint16_t* xn;     // bf16 RMSNorm of out_bf16
-  uint16_t* f16p;   // its fp16 pair-order copy (the next GEMM's input)
+  uint16_t* f16p;   // its scaled fp16 pair-order copy (the next GEMM's input)
+  int32_t* xexp;    // the copy's row exponents
   float eps;
 };
 
@@ -431,8 +432,8 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   uint16_t* xf = at<uint16_t>(ws, lay.xf16);
   uint16_t* hf = at<uint16_t>(ws, lay.hf16);
   float* y = at<float>(ws, lay.y);
-  // the stack's normalised input comes with its fp16 copy unscaled (a = 0: rows of unit rms)
-  int32_t* xexp = x_f16_ready ? nullptr : at<int32_t>(ws, lay.xexp);
+  // (a stack's normalised input comes with its fp16 copy and row exponents already written)
+  int32_t* xexp = at<int32_t>(ws, lay.xexp);
   if (!x_f16_ready) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
@@ -444,7 +445,7 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   }));
   if (norm_next)
     MOE_TRY(launch_combine_norm(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, norm_next->eps,
-                                norm_next->xn, norm_next->f16p, s));
+                                norm_next->xn, norm_next->f16p, norm_next->xexp, s));
   else
     MOE_TRY(launch_combine(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, s));
   return MOE_OK;
@@ -747,7 +748,8 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
     } else if (!norm_in) {
       uint16_t* xn = at<uint16_t>(ws, lay.xn);
       if (f16)
-        MOE_TRY(launch_rmsnorm_bf16_f16pairs(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, at<uint16_t>(ws, lay.xf16), s));
+        MOE_TRY(launch_rmsnorm_bf16_f16pairs(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, at<uint16_t>(ws, lay.xf16),
+                                             at<int32_t>(ws, lay.xexp), s));
       else
         MOE_TRY(launch_rmsnorm_bf16(cur, T, layers[l].hidden, MOE_RMS_EPS, xn, s));
       lin = xn;
@@ -757,6 +759,7 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
     if (f16 && l + 1 < n_layers && same_shape(layers[l], layers[l + 1]) && combine_norm_ok(layers[l].hidden)) {
       nn.xn = at<uint16_t>(ws, lay.xn);
       nn.f16p = at<uint16_t>(ws, lay.xf16);
+      nn.xexp = at<int32_t>(ws, lay.xexp);
       nn.eps = MOE_RMS_EPS;
       next = &nn;
     }

@@ -187,20 +187,20 @@ __device__ __forceinline__ float block_sum_fixed(float v, float* part, int nw) {
   return tot;
 }
 
-// Rows of H = 64 G columns (G <= 64): one block per row, wave w takes the
-// 64-column groups w, w + W, ... (lane = column); group sums and the scale by
-// rms_group_sum / rms_inv_from_groups (device.h), the definition the fused
-// stack path uses; output rounded to bf16 (nearest even).
-// f16p (may be NULL): also the fp16 copy of the output in pair order (u32 j of
-// each 16-column group = columns j and j + 8, the grouped GEMM's A layout).
-// RMSNorm of one bf16 row (value of column c: get(c)) with the 64-column group
-// sums (rms_group_sum, lane = column, one wave per group) and their total
-// (rms_inv_from_groups, lane = group): out_row = bf16(x * inv); with f16p, also
-// the fp16 pair-order copy (columns c, c + 8 of each 16-column group in one word)
-// of row `row`.  Every thread of the block calls it; part holds G <= 64 floats.
+// RMSNorm of one bf16 row (value of column c: get(c)) of H = 64 G columns
+// (G <= 64) with the 64-column group sums (rms_group_sum, lane = column, one wave
+// per group) and their total (rms_inv_from_groups, lane = group): out_row =
+// bf16(x * inv), rounded to nearest even; the definition the fused stack path
+// uses too.  With f16p, also the grouped GEMMs' fp16 copy of the output row
+// scaled by its row exponent a (bf16_row_exponent of the output's largest
+// magnitude; a written to xexp[row]) in pair order (u32 j of each 16-column
+// group = columns j and j + 8), the same bits k_x_to_f16_rows makes from the
+// bf16 row.  Every thread of the block calls it; part holds G <= 64 floats,
+// wmax 16 words.
 template <class Get>
-__device__ __forceinline__ void rms_norm_row_g64(Get get, int H, float eps, float* part, uint16_t* __restrict__ out_row,
-                                                 uint32_t* __restrict__ f16p, size_t row) {
+__device__ __forceinline__ void rms_norm_row_g64(Get get, int H, float eps, float* part, uint32_t* wmax,
+                                                 uint16_t* __restrict__ out_row, uint32_t* __restrict__ f16p,
+                                                 int32_t* __restrict__ xexp, size_t row) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int G = H / 64;
@@ -210,24 +210,36 @@ __device__ __forceinline__ void rms_norm_row_g64(Get get, int H, float eps, floa
   }
   __syncthreads();
   const float inv = rms_inv_from_groups(lane < G ? part[lane] : 0.0f, H, eps);
+  uint32_t m = 0;
+  for (int g = w; g < G; g += nw) {
+    const uint16_t o = __builtin_bit_cast(uint16_t, (__bf16)(get(64 * g + lane) * inv));
+    out_row[64 * g + lane] = o;
+    m = max(m, (uint32_t)(o & 0x7FFFu));
+  }
+  if (!f16p) return;
+  m = wave_max_u32(m);
+  if (lane == 0) wmax[w] = m;
+  __syncthreads();
+  for (int i = 0; i < nw; ++i) m = max(m, wmax[i]);
+  const int a = bf16_row_exponent(m);
+  if (threadIdx.x == 0) xexp[row] = a;
   for (int g = w; g < G; g += nw) {
     const __bf16 o = (__bf16)(get(64 * g + lane) * inv);
-    out_row[64 * g + lane] = __builtin_bit_cast(uint16_t, o);
-    if (f16p) {
-      // column + 8 of the same 16-column group: rotate the 16-lane row by 8
-      const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)(float)o);
-      const uint32_t h8 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x128, 0xF, 0xF, true);
-      if ((lane & 15) < 8) f16p[(row * H + 64 * g + lane) / 16 * 8 + (lane & 7)] = h | (h8 << 16);
-    }
+    // column + 8 of the same 16-column group: rotate the 16-lane row by 8
+    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)ldexpf((float)o, a));
+    const uint32_t h8 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x128, 0xF, 0xF, true);
+    if ((lane & 15) < 8) f16p[(row * H + 64 * g + lane) / 16 * 8 + (lane & 7)] = h | (h8 << 16);
   }
 }
 
 __global__ __launch_bounds__(1024) void k_rmsnorm_bf16_g64(const uint16_t* __restrict__ x, int H, float eps,
-                                                           uint16_t* __restrict__ out, uint32_t* __restrict__ f16p) {
+                                                           uint16_t* __restrict__ out, uint32_t* __restrict__ f16p,
+                                                           int32_t* __restrict__ xexp) {
   __shared__ float part[64];
+  __shared__ uint32_t wmax[16];
   const int row = blockIdx.x;
   const uint16_t* __restrict__ xr = x + (size_t)row * H;
-  rms_norm_row_g64([&](int c) { return bf16_to_f32(xr[c]); }, H, eps, part, out + (size_t)row * H, f16p,
+  rms_norm_row_g64([&](int c) { return bf16_to_f32(xr[c]); }, H, eps, part, wmax, out + (size_t)row * H, f16p, xexp,
                    (size_t)row);
 }
 
@@ -239,9 +251,11 @@ __global__ __launch_bounds__(1024) void k_combine_norm(const float* __restrict__
                                                       const float* __restrict__ gates, int T, int k, int H,
                                                       int with_shared, const uint16_t* __restrict__ residual,
                                                       float* __restrict__ out, uint16_t* __restrict__ out_bf16,
-                                                      float eps, uint16_t* __restrict__ xn, uint32_t* __restrict__ f16p) {
+                                                      float eps, uint16_t* __restrict__ xn, uint32_t* __restrict__ f16p,
+                                                      int32_t* __restrict__ xexp) {
   __shared__ float xs[4096];
   __shared__ float part[64];
+  __shared__ uint32_t wmax[16];
   const int t = blockIdx.x, q = threadIdx.x;
   const float4 acc = combine4(y_sorted, row_to_sorted, gates, T, k, H, with_shared, residual, t, q);
   if (out) reinterpret_cast<float4*>(out)[(size_t)t * (H / 4) + q] = acc;
@@ -251,7 +265,7 @@ __global__ __launch_bounds__(1024) void k_combine_norm(const float* __restrict__
   *reinterpret_cast<float4*>(xs + 4 * q) = make_float4(bf16_to_f32(b0), bf16_to_f32(b1), bf16_to_f32(b2),
                                                        bf16_to_f32(b3));
   __syncthreads();
-  rms_norm_row_g64([&](int c) { return xs[c]; }, H, eps, part, xn + (size_t)t * H, f16p, (size_t)t);
+  rms_norm_row_g64([&](int c) { return xs[c]; }, H, eps, part, wmax, xn + (size_t)t * H, f16p, xexp, (size_t)t);
 }
 
 __global__ __launch_bounds__(1024) void k_rmsnorm_bf16_v8(const uint16_t* __restrict__ x, int H, float eps,
@@ -300,7 +314,7 @@ hipError_t launch_rmsnorm_bf16(const uint16_t* x, int T, int H, float eps, uint1
   if (H % 64 == 0 && H / 64 <= 64) {
     const int G = H / 64;
     MOE_LAUNCH(k_rmsnorm_bf16_g64, dim3(T), dim3(64 * (G < 16 ? G : 16)), 0, s, x, H, eps, out,
-               (uint32_t*)nullptr);
+               (uint32_t*)nullptr, (int32_t*)nullptr);
   } else if (H % 8 == 0 && H <= 8192) {
     const int threads = ((H / 8 + 63) / 64) * 64;
     MOE_LAUNCH(k_rmsnorm_bf16_v8, dim3(T), dim3(threads), 0, s, x, H, eps, out);
@@ -316,21 +330,21 @@ bool combine_norm_ok(int H) { return H % 256 == 0 && H <= 4096; }
 
 hipError_t launch_combine_norm(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
                                int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
-                               float eps, uint16_t* xn, uint16_t* f16p, hipStream_t s) {
+                               float eps, uint16_t* xn, uint16_t* f16p, int32_t* xexp, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (!combine_norm_ok(H) || !out_bf16 || !xn) return hipErrorInvalidValue;
+  if (!combine_norm_ok(H) || !out_bf16 || !xn || (f16p && !xexp)) return hipErrorInvalidValue;
   MOE_LAUNCH(k_combine_norm, dim3(T), dim3(H / 4), 0, s, y_sorted, row_to_sorted, gates, T, k, H, with_shared,
-             residual, out, out_bf16, eps, xn, reinterpret_cast<uint32_t*>(f16p));
+             residual, out, out_bf16, eps, xn, reinterpret_cast<uint32_t*>(f16p), xexp);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_bf16_f16pairs(const uint16_t* x, int T, int H, float eps, uint16_t* out, uint16_t* f16p,
-                                        hipStream_t s) {
+                                        int32_t* xexp, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (!rmsnorm_f16_pairs_ok(H)) return hipErrorInvalidValue;
+  if (!rmsnorm_f16_pairs_ok(H) || !xexp) return hipErrorInvalidValue;
   const int G = H / 64;
   MOE_LAUNCH(k_rmsnorm_bf16_g64, dim3(T), dim3(64 * (G < 16 ? G : 16)), 0, s, x, H, eps, out,
-             reinterpret_cast<uint32_t*>(f16p));
+             reinterpret_cast<uint32_t*>(f16p), xexp);
   return hipGetLastError();
 }
 

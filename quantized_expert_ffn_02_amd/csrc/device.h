@@ -110,6 +110,24 @@ __device__ __forceinline__ float row_inv_rms(const float* __restrict__ sq, int t
   return rms_inv_from_groups(g, H, eps);
 }
 
+// Row exponent of the grouped GEMMs' fp16 activation copy: a = -floor(log2 m)
+// for the largest magnitude m of a bf16 row, given as the largest low 15 bits of
+// its bit patterns (|x| orders as those bits for finite bf16); the row is
+// stored as x 2^a, its largest magnitude in [1, 2).  Zero, inf or NaN maxima
+// give 0.
+__device__ __forceinline__ int bf16_row_exponent(uint32_t maxbits15) {
+  if (maxbits15 == 0u || maxbits15 >= 0x7F80u) return 0;
+  const int be = (int)(maxbits15 >> 7);
+  const int e2 = be ? be - 127 : (31 - __builtin_clz(maxbits15 & 0x7Fu)) - 133;   // floor(log2 m)
+  return -e2;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, MOE_WAVE));
+  return m;
+}
+
 typedef __bf16 moe_bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two bf16 values (one u32) times s, rounded to bf16 (nearest even).

@@ -168,10 +168,11 @@ hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);
 // ---- launchers (return hipGetLastError()) ----
 hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t s);
 // RMSNorm that also writes the fp16 pair-order copy of its output (the grouped
-// GEMM's activation layout), for H = 64 G, G <= 64
+// GEMM's activation layout, each row scaled by its exponent, written to xexp[T]),
+// for H = 64 G, G <= 64
 bool rmsnorm_f16_pairs_ok(int H);
 hipError_t launch_rmsnorm_bf16_f16pairs(const uint16_t* x, int T, int H, float eps, uint16_t* out, uint16_t* f16p,
-                                        hipStream_t s);
+                                        int32_t* xexp, hipStream_t s);
 
 hipError_t launch_router_gemv(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s);
@@ -259,12 +260,13 @@ struct PackWords {
 hipError_t launch_pack_words(const PackWords& p, uint32_t* dst, hipStream_t s);
 
 // The combine (as launch_combine, out may be NULL, out_bf16 required) followed by
-// the RMSNorm of its bf16 result into xn (and, if f16p, the fp16 pair-order copy),
-// bit for bit as launch_rmsnorm_bf16_f16pairs on out_bf16.  combine_norm_ok(H).
+// the RMSNorm of its bf16 result into xn (and, if f16p, the scaled fp16 pair-order
+// copy and its row exponents xexp), bit for bit as launch_rmsnorm_bf16_f16pairs on
+// out_bf16.  combine_norm_ok(H).
 bool combine_norm_ok(int H);
 hipError_t launch_combine_norm(const float* y_sorted, const int32_t* row_to_sorted, const float* gates, int T, int k,
                                int H, int with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
-                               float eps, uint16_t* xn, uint16_t* f16p, hipStream_t s);
+                               float eps, uint16_t* xn, uint16_t* f16p, int32_t* xexp, hipStream_t s);
 
 // out[i] += y[i], i < n (both 16-byte aligned)
 hipError_t launch_add_f32(float* out, const float* y, size_t n, hipStream_t s);

@@ -130,9 +130,11 @@ static constexpr int GCOLS = 256;            // weight rows per block (4 waves x
 // 16-byte pieces instead of 2-byte scatters.
 // h' = h 4^a from the accumulators g' = g 2^a, u' = u 2^a of a row scaled by 2^a:
 // SiLU(g) u 4^a = g' u' sigma(g), with g = g' 2^-a formed only inside sigma
-// (which saturates), so h' stays finite whatever the scale of x.
+// (which saturates), so h' stays finite whatever the scale of x.  sigma takes the
+// hardware exponential and reciprocal (a few ulp of fp32, against the 2^-11 of the
+// fp16 that h is rounded to next) instead of an IEEE division sequence.
 __device__ __forceinline__ float swiglu_scaled(float gv, float uv, int a) {
-  return gv * uv / (1.0f + expf(-ldexpf(gv, -a)));
+  return gv * uv * __builtin_amdgcn_rcpf(1.0f + __expf(-ldexpf(gv, -a)));
 }
 
 template <bool TR>

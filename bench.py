@@ -244,10 +244,19 @@ def bench_stack(steps):
         torch.cuda.synchronize()
         ms_g = t0.elapsed_time(t1) / steps
         best = min(ms, ms_g)
+        # algorithmic FLOPs per step: router 2*T*H*E and 6*H*I per (token, expert) incl. the shared one, per layer
+        step_flops = wl.layers * (2.0 * T * H * E + T * (k + 1) * 6.0 * H * I)
+        # the binding roofline: bytes at 8 TB/s against FLOPs at 2.5 PF (ridge about 315 flop/B)
+        bound = "mfma" if step_flops / step_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        tflops = step_flops / (best * 1e-3) / 1e12
         res[f"T{T}"] = {"step_ms_eager": ms, "step_ms_graph": ms_g, "tokens_per_s": T / (best * 1e-3),
                         "avg_unique_experts_per_layer": float(np.mean(uniq)), "algorithmic_GB_per_step":
                         step_bytes / 1e9, "sustained_GBps": step_bytes / (best * 1e-3) / 1e9,
-                        "hbm_frac": step_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                        "hbm_frac": step_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "algorithmic_GFLOP_per_step": step_flops / 1e9, "TFLOPs": tflops,
+                        "mfma_frac_of_fp16_peak": tflops / MFMA_BF16_PEAK_TFLOPS, "bound": bound,
+                        "roofline_frac": (tflops / MFMA_BF16_PEAK_TFLOPS) if bound == "mfma" else
+                        step_bytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del g
     del layers
     torch.cuda.empty_cache()

@@ -134,6 +134,50 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
   if (P.tiles) plan_groups(P, g, g < G ? off : 0, g < G ? tot : 0);
 }
 
+// The same scan with the whole count matrix staged in LDS as 16-bit values (a
+// chunk counts at most kChunk = 1,024 entries of a group): the block loads it
+// in one cooperative pass, every load of a thread in flight at once, so it
+// waits for memory about once instead of once per batch of chunks and pass.  For count
+// matrices of up to kScanLdsCounts values (88 chunks x 513 groups at 8,192
+// tokens is 45,144).
+static constexpr int kScanLdsCounts = 49152;   // 96 KB of LDS
+
+__global__ __launch_bounds__(1024) void k_perm_scan_lds(const int32_t* __restrict__ counts, int n_chunks, int E,
+                                                        int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+                                                        PlanOut P) {
+  __shared__ uint16_t cs[kScanLdsCounts];
+  const int G = E + 1, N = n_chunks * G;
+  constexpr int PER = kScanLdsCounts / 1024;   // values per thread, all loads issued before the first store
+  int v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * 1024;
+    v[j] = i < N ? counts[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * 1024;
+    if (i < N) cs[i] = (uint16_t)v[j];
+  }
+  __syncthreads();
+  const int g = threadIdx.x;
+  int tot = 0;
+  if (g < G)
+    for (int c = 0; c < n_chunks; ++c) tot += cs[c * G + g];
+  int n_all = 0;
+  const int off = block_exclusive_scan_1024(g < G ? tot : 0, &n_all);
+  if (g < G) {
+    offsets[g] = off;
+    int run = off;
+    for (int c = 0; c < n_chunks; ++c) {
+      base[(size_t)c * G + g] = run;
+      run += cs[c * G + g];
+    }
+  }
+  if (g == 0) offsets[G] = n_all;
+  if (P.tiles) plan_groups(P, g, g < G ? off : 0, g < G ? tot : 0);
+}
+
 // One wave per chunk: entries in ascending r, 64 at a time; the rank of an
 // entry among equal-group entries of its batch comes from ballots over the
 // group's bits, and a per-group running count in LDS carries across batches.
@@ -184,7 +228,10 @@ static hipError_t permute_multi(const int32_t* ids, int T, int k, int E, int wit
   const int n = Tk + (with_shared ? T : 0);
   const int nc = permute_chunks(n);
   MOE_LAUNCH(k_perm_hist, dim3(nc), dim3(256), 0, s, ids, Tk, n, E, counts);
-  MOE_LAUNCH(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets, plan);
+  if ((size_t)nc * (E + 1) <= (size_t)kScanLdsCounts)
+    MOE_LAUNCH(k_perm_scan_lds, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets, plan);
+  else
+    MOE_LAUNCH(k_perm_scan, dim3(1), dim3(1024), 0, s, counts, nc, E, base, offsets, plan);
   MOE_LAUNCH(k_perm_scatter, dim3(nc), dim3(64), 0, s, ids, Tk, n, E, base, sorted_rows, row_to_sorted);
   return hipGetLastError();
 }

@@ -182,8 +182,16 @@ int items_per_for(int T);
 bool use_gemm_path(int n_entries);
 int mfma_min_rows(int T);
 
+// x_f16 (optional): when the top-k runs as its own launch (T > 16) it also writes
+// the grouped GEMMs' scaled fp16 copy of x and its row exponents into the
+// workspace; *x_f16 says whether it did.
 int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float* gates, float* margin, void* ws,
-             const Layout& lay, hipStream_t s) {
+             const Layout& lay, hipStream_t s, bool* x_f16 = nullptr) {
+  const bool fuse = x_f16 && T > 16 && L->routed.fmt != MOE_FMT_BF16 && topk_row_f16_ok(L->hidden);
+  const uint16_t* fx = fuse ? x : nullptr;
+  uint16_t* fxf = fuse ? at<uint16_t>(ws, lay.xf16) : nullptr;
+  int32_t* fxe = fuse ? at<int32_t>(ws, lay.xexp) : nullptr;
+  if (x_f16) *x_f16 = fuse;
   float* logits = at<float>(ws, lay.logits);
   // split-K router partial planes (16 < T < 1024)
   const int parts = T > 16 && T < 1024 ? router_parts(T, L->n_experts, L->hidden) : 1;
@@ -198,9 +206,11 @@ int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float
     return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
   }));
   if (parts > 1)
-    MOE_TRY(launch_topk(rparts, T, L->n_experts, L->top_k, ids, gates, margin, s, parts, L->router_bias));
+    MOE_TRY(launch_topk(rparts, T, L->n_experts, L->top_k, ids, gates, margin, s, parts, L->router_bias, fx,
+                        L->hidden, fxf, fxe));
   else
-    MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s));
+    MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s, 1, nullptr, fx, L->hidden, fxf,
+                        fxe));
   return MOE_OK;
 }
 
@@ -210,7 +220,7 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
                   float* y_sorted, void* ws, const Layout& lay, hipStream_t s, bool x_table_ready = false,
                   const int32_t* gemm_tiles = nullptr, const int32_t* n_gemm_tiles = nullptr,
                   const moe_bank_t* routed_override = nullptr, const float* gates = nullptr,
-                  uint16_t* y16 = nullptr) {
+                  uint16_t* y16 = nullptr, bool x_f16_ready = false) {
   const moe_bank_t& rb = routed_override ? *routed_override : L->routed;
   const int H = L->hidden, I = L->inter, E = L->n_experts;
   // upper bound on GEMV work items: every entry, or, when the MFMA GEMM takes
@@ -248,7 +258,7 @@ int do_expert_ffn(const moe_layer_t* L, const uint16_t* x, int T, const PermRef&
   int32_t* xexp = at<int32_t>(ws, lay.xexp);
   if (gemm) {
     uint16_t* xf = at<uint16_t>(ws, lay.xf16);
-    MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
+    if (!x_f16_ready) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
     MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
       return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, gemm_tiles, n_gemm_tiles, max_tiles,
                             perm.sorted_rows, T, perm.k, xf, hf, s, nullptr, nullptr, gemm_tile_rows(), false,
@@ -417,7 +427,8 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   int32_t* offsets = at<int32_t>(ws, lay.offsets);
   int32_t* srt = at<int32_t>(ws, lay.sorted_rows);
   int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
-  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
+  bool xw = false;   // the top-k launch wrote the fp16 copy of x
+  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s, x_f16_ready ? nullptr : &xw);
   if (rc) return rc;
   if (after_route && (rc = (*after_route)())) return rc;
   int32_t* chunks = at<int32_t>(ws, lay.tiles);
@@ -434,7 +445,7 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   float* y = at<float>(ws, lay.y);
   // (a stack's normalised input comes with its fp16 copy and row exponents already written)
   int32_t* xexp = at<int32_t>(ws, lay.xexp);
-  if (!x_f16_ready) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
+  if (!x_f16_ready && !xw) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
                           nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp);
@@ -488,7 +499,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   int32_t* items = at<int32_t>(ws, lay.items);
   int32_t* n_items = at<int32_t>(ws, lay.n_items);
   const bool quant = L->routed.fmt != MOE_FMT_BF16;
-  bool x_table_ready = false, gemm = false;
+  bool x_table_ready = false, gemm = false, xw = false;   // xw: the top-k launch wrote the fp16 copy of x
   if (n <= kSmallRouteMaxEntries && quant && decode_direct_ok(T, k, with_shared, L->hidden, L->inter)) {
     // decode / MTP-verify batch, entries addressed directly: router front end,
     // gate/up with the top-k inside, down, combine
@@ -618,9 +629,9 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
     MOE_TRY(timed(MOE_KERNEL_ROUTER, s, [&] { return launch_route_small(a, s); }));
     x_table_ready = quant;
   } else {
-    int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s);
-    if (rc) return rc;
     gemm = L->routed.fmt == MOE_FMT_Q2 && gemm_shape_ok(L->hidden, L->inter);
+    int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s, gemm ? &xw : nullptr);
+    if (rc) return rc;
     MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
                                 at<int32_t>(ws, lay.base), gemm ? mfma_min_rows(T) : 0x7FFFFFFF, items_per_for(T),
                                 gemm_tile_rows(), at<int32_t>(ws, lay.tiles), at<int32_t>(ws, lay.n_tiles), items,
@@ -638,7 +649,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
   // a prompt-sized chunk puts every group on the GEMM: gate-scaled fp16 rows
   uint16_t* y16 = gemm && mfma_min_rows(T) == 1 ? at<uint16_t>(ws, lay.y) : nullptr;
   int rc = do_expert_ffn(L, x, T, perm, n, y, ws, lay, s, x_table_ready, gemm ? at<int32_t>(ws, lay.tiles) : nullptr,
-                         gemm ? at<int32_t>(ws, lay.n_tiles) : nullptr, nullptr, gates, y16);
+                         gemm ? at<int32_t>(ws, lay.n_tiles) : nullptr, nullptr, gates, y16, xw);
   if (rc) return rc;
   if (y16)
     MOE_TRY(launch_combine16(y16, inv, T, k, L->hidden, with_shared, residual, out, out_bf16,

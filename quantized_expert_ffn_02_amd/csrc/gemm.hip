@@ -51,13 +51,6 @@ static constexpr int LDS_STRIDE = BK + 8;   // halves per LDS row (padding again
 // patterns (|x| orders as the low 15 bits of a finite bf16), then the scaled
 // conversion (the second read hits the cache).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int bf16_row_exponent(uint32_t maxbits15) {
-  if (maxbits15 == 0u || maxbits15 >= 0x7F80u) return 0;      // zero row, or inf / NaN
-  const int be = (int)(maxbits15 >> 7);
-  const int e2 = be ? be - 127 : (31 - __builtin_clz(maxbits15 & 0x7Fu)) - 133;   // floor(log2 max)
-  return -e2;
-}
-
 __global__ __launch_bounds__(256) void k_x_to_f16_rows(const uint16_t* __restrict__ x, int H,
                                                        uint16_t* __restrict__ out, int32_t* __restrict__ xexp) {
   __shared__ uint32_t wmax[4];

@@ -182,9 +182,14 @@ hipError_t launch_route_small(const SmallRouteArgs& a, hipStream_t s);
 // router logits + activation table only (the first launch of launch_route_small)
 hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s);
 // parts > 1: ``logits`` holds ``parts`` partial planes [T][E] to be added in
-// plane order, then ``bias`` (launch_router_split with parts > 1)
+// plane order, then ``bias`` (launch_router_split with parts > 1).  With x set,
+// the same launch also writes the grouped GEMMs' activation copy of x (as
+// launch_x_to_f16_pairs: xf16 [T][H] and xexp [T]); topk_row_f16_ok(H).
+static constexpr int kRowF16MaxH = 3072;
+bool topk_row_f16_ok(int H);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
-                       hipStream_t s, int parts = 1, const float* bias = nullptr);
+                       hipStream_t s, int parts = 1, const float* bias = nullptr, const uint16_t* x = nullptr,
+                       int H = 0, uint16_t* xf16 = nullptr, int32_t* xexp = nullptr);
 
 // permutation: counts/base are [n_chunks][E + 2] int32 scratch
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,

@@ -381,6 +381,24 @@ def test_gemm_path_medium_full_compare():
     assert err <= OUT_TOL
 
 
+@pytest.mark.parametrize("T", [16, 17, 1023])
+def test_path_boundaries_full_compare(T):
+    # The batch sizes at the edges of the paths, on the real 2-bit layer with Zipf
+    # routing: 16 tokens (the largest decode batch: entries addressed directly, the
+    # fp8 x fp4 kernels), 17 (the smallest verify batch: split router, the top-k that
+    # also writes the fp16 copy of x, single-block permutation, 32-row GEMM) and
+    # 1,023 (the largest verify batch, 11,253 entries), each against the oracle over
+    # the whole [T, H] output.
+    hl, x, ref, ids_r, gates_r = prompt_case(T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    assert_route_matches(ids, gates, hl.logits(x), hl.shape.top_k, f"boundary T={T}")
+    err = OL.rel_max_err(out, ref)
+    print(f"boundary T={T}: max|err|/rms = {err:.3e} over the whole [T, H] output")
+    assert err <= OUT_TOL
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
 @pytest.mark.parametrize("T", [1024, 3000, 8192])
 def test_prompt_chunk_full_compare(T):
     # Prompt-sized chunks (T >= 1,024: every group on the 128-row grouped GEMM, the

@@ -203,6 +203,35 @@ __device__ __forceinline__ void wave_step(const uint16_t* __restrict__ As, const
   }
 }
 
+// Half-width 32-row tiles (3-bit): the wave's one 32-column B fragment for a
+// 64-K step -- its codes, high bits and scales -- as two exact fragments and two
+// MFMAs into one accumulator per 16 K.
+struct BRegsH3 {
+  u32x4 c0;
+  uint32_t s0;
+  uint2 h0;
+};
+__device__ __forceinline__ void pin_b(BRegsH3& R) {
+  asm volatile("" : "+v"(R.c0), "+v"(R.s0), "+v"(R.h0.x), "+v"(R.h0.y));
+}
+
+__device__ __forceinline__ void wave_step_half3(const uint16_t* __restrict__ As, const BRegsH3& R, int shift,
+                                                int hshift, const BConst& bc, const BConstHi& bch, f16x_t& acc) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, kh = (lane >> 5) * 8;
+  const uint32_t cw[4] = {R.c0.x, R.c0.y, R.c0.z, R.c0.w};
+  const h2_t m2 = h2_t{(_Float16)-2.0f, (_Float16)-2.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const h2_t s2 = scale_pair(R.s0, s >= 2);
+    const h8_t b = b_frag(cw[s] >> shift, s2, bc);
+    const h8_t bh = b_frag_hi((s < 2 ? R.h0.x : R.h0.y) >> (hshift + 8 * (s & 1)), s2, s2 * m2, bch, bc.magic);
+    const h8_t a = *reinterpret_cast<const h8_t*>(As + r * A_STRIDE + s * 16 + kh);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bh, acc, 0, 0, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Grouped GEMM tiles: (group, first sorted position, rows <= GBM) per M-tile.
 // ---------------------------------------------------------------------------
@@ -267,9 +296,14 @@ struct GemmArgs {
 // rows); NMI <= MAXNMI the fragments this tile's rows need.  As holds three LDS
 // buffers of the A tile.  128-row tiles run with the transposed accumulator
 // (TR, see mfma_op).
-template <bool GATEUP, int NMI, int MAXNMI, int DEPTH, bool Q3>
+// HALF (3-bit 32-row tiles): each wave takes one 32-column B fragment instead of
+// two -- 16 gate + 16 up columns (gate/up) or 32 output columns (down) -- so a
+// launch has twice the blocks, each with half the work and fewer registers
+// (three blocks per compute unit instead of two).
+template <bool GATEUP, int NMI, int MAXNMI, int DEPTH, bool Q3, bool HALF = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, uint16_t* As) {
-  typedef typename std::conditional<Q3, BRegs3, BRegs>::type BRegs;
+  static_assert(!HALF || (MAXNMI == 1 && Q3), "half-width tiles: 32 rows, 3-bit");
+  typedef typename std::conditional<Q3, typename std::conditional<HALF, BRegsH3, BRegs3>::type, BRegs>::type BRegs;
   constexpr bool TR = MAXNMI == 4;
   constexpr int BMX = 32 * MAXNMI;          // tile rows
   constexpr int NV = BMX / 32;              // 16-byte A chunks per thread and step
@@ -307,7 +341,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   // column 8 + j inside each 16-group), so accumulator rows come out in pair
   // order and h is stored as it is laid out.
   int n0, n1;
-  if (GATEUP) {
+  if (HALF) {
+    // lane m < 16 of each half-wave: gate column j; lane m + 16: up column j
+    const int m = lane & 31;
+    n0 = GATEUP ? (m < 16 ? 0 : g.I) + t.n * 64 + wv * 16 + (m & 15) : t.n * 128 + wv * 32 + m;
+    n1 = n0;
+  } else if (GATEUP) {
     const int m = lane & 31, j = m & 15;
     n0 = t.n * 128 + wv * 32 + (TR ? ((m & 16) | ((j & 1) ? 8 + (j >> 1) : (j >> 1))) : m);
     n1 = g.I + n0;
@@ -324,9 +363,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   const __amdgpu_buffer_rsrc_t s_rsrc = buffer_rsrc(g.scales, g.scale_bytes);
   const uint32_t c_voff = (uint32_t)((((n0 >> 6) * (K / 64)) * 64 + (n0 & 63)) * 16);
   const uint32_t s_voff = (uint32_t)((((n0 >> 6) * (K / 128)) * 64 + (n0 & 63)) * 8);
-  const uint32_t c_d1 = __builtin_amdgcn_readfirstlane(
+  const uint32_t c_d1 = HALF ? 0u : __builtin_amdgcn_readfirstlane(
       (uint32_t)((((n1 >> 6) * (K / 64)) * 64 + (n1 & 63)) * 16) - c_voff);
-  const uint32_t s_d1 = __builtin_amdgcn_readfirstlane(
+  const uint32_t s_d1 = HALF ? 0u : __builtin_amdgcn_readfirstlane(
       (uint32_t)((((n1 >> 6) * (K / 128)) * 64 + (n1 & 63)) * 8) - s_voff);
   const int shift = (lane >> 5) * 8, hshift = (lane >> 5) * 4;
   const BConst bc = bconst();
@@ -357,7 +396,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
   };
   auto load_bc = [&](int kc, BRegs& R) {
     kc = kc < nch ? kc : nch - 1;
-    if constexpr (Q3) {
+    if constexpr (HALF) {
+      // one column: as load_b for B0
+      R.c0 = B0.codes[(size_t)kc * 64];
+      R.s0 = B0.scales[(size_t)(kc >> 1) * 128 + (kc & 1)];
+      R.h0 = B0.hi[(size_t)kc * 64];
+    } else if constexpr (Q3) {
       load_b(B0, B1, kc, R);
     } else {
       // codes: 1024 bytes per step; scales: blocks 2 kc, 2 kc + 1 at dword
@@ -368,6 +412,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
       R.c1 = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, c_voff, kc * 1024 + c_d1, 0);
       R.s1 = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_voff, so + s_d1, 0);
     }
+  };
+
+  auto compute = [&](const uint16_t* Ab, const BRegs& Bc) {
+    if constexpr (HALF)
+      wave_step_half3(Ab, Bc, shift, hshift, bc, bch, acc[0][0]);
+    else
+      wave_step<NMI, MAXNMI, Q3, TR>(Ab, Bc, shift, hshift, bc, bch, acc);
   };
 
   if constexpr (DEPTH == 2) {
@@ -392,7 +443,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     load_bc(kc + J + 2, BNEW);                                       \
     __builtin_amdgcn_sched_barrier(0);                               \
     pin_b(BCUR);                                                     \
-    wave_step<NMI, MAXNMI, Q3, TR>(As + J * ABUF, BCUR, shift, hshift, bc, bch, acc); \
+    compute(As + J * ABUF, BCUR);                                    \
     __syncthreads();                                                 \
   }
     // whole groups of three steps with no branch inside (exact wait counts),
@@ -431,7 +482,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     load_bc(kc + J + DEPTH, Br[(J + DEPTH) % R]);                              \
     __builtin_amdgcn_sched_barrier(0);                                         \
     pin_b(Br[J % R]);                                                          \
-    wave_step<NMI, MAXNMI, Q3, TR>(As + (J % 3) * ABUF, Br[J % R], shift, hshift, bc, bch, acc); \
+    compute(As + (J % 3) * ABUF, Br[J % R]);                                   \
     __syncthreads();                                                           \
   }
   // whole groups of U steps with no branch inside (exact wait counts), then
@@ -533,6 +584,34 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const GemmTile& t, 
     }
     return;
   }
+  if (HALF && GATEUP) {
+    // lanes m < 16 of each half-wave hold gate column j, lanes m + 16 the up
+    // column j of the same rows: one exchange, then the gate lanes store h
+    const int m = lane & 31;
+    const int col = t.n * 64 + wv * 16 + (m & 15);
+    const int pcol = (col & ~15) + pair_pos(col & 15);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float mine = acc[0][0][r];
+      const float other = __shfl_xor(mine, 16, 64);
+      const int row = acc_row(r, lane);
+      if (m < 16 && row < t.rows) {
+        const float hv = swiglu_scaled(mine, other, g.row_exp ? g.row_exp[row] : 0);
+        g.h_out[(size_t)(t.m0 + row) * g.I + pcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+      }
+    }
+    return;
+  }
+  if (HALF) {
+    // down: fp32 column n0 of each row (y16 is not used with 3-bit weights)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = acc_row(r, lane);
+      if (row < t.rows)
+        g.y_out[(size_t)(t.m0 + row) * g.H + n0] = ldexpf(acc[0][0][r], g.row_exp ? -2 * g.row_exp[row] : 0);
+    }
+    return;
+  }
   if (GATEUP) {
     // h = SiLU(gate) * up, fp16, stored at the pair-order position of its column
     const int col = t.n * 128 + wv * 32 + (lane & 31);
@@ -591,11 +670,13 @@ struct GemmKArgs {
 
 // One kernel per projection, tile height and format: MAXNMI = 4 (128-row
 // tiles, 2-bit, for prompt chunks) or 1 (32-row tiles, for verify batches of
-// many sequences, whose experts have a few to a few dozen rows; 2- or 3-bit).
+// many sequences, whose experts have a few to a few dozen rows; 2-bit, or 3-bit
+// with half-width tiles).
 // In expert-cache mode a tile whose group has no slot computes nothing: the
 // down projection writes zero rows, so the combine adds nothing for it.
-template <bool GATEUP, int MAXNMI, bool Q3>
-__global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(GemmKArgs a) {
+template <bool GATEUP, int MAXNMI, bool Q3, bool HALF = false>
+__global__ __launch_bounds__(256, (MAXNMI == 4 || (Q3 && !HALF)) ? 2 : 3) void k_gemm_q2(GemmKArgs a) {
+  constexpr int BCOLS = HALF ? 128 : GCOLS;   // output columns of a down block
   __shared__ __attribute__((aligned(16))) uint16_t As[3 * 32 * MAXNMI * A_STRIDE];
   __shared__ float row_gate[32 * MAXNMI];
   __shared__ int32_t row_exp[32 * MAXNMI];
@@ -607,8 +688,8 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(Ge
     slot = a.slot_map[t.g];
     if (slot < 0) {
       if (!GATEUP) {
-        for (int i = threadIdx.x; i < t.rows * GCOLS; i += blockDim.x)
-          a.y_out[(size_t)(t.m0 + i / GCOLS) * a.H + t.n * GCOLS + i % GCOLS] = 0.0f;
+        for (int i = threadIdx.x; i < t.rows * BCOLS; i += blockDim.x)
+          a.y_out[(size_t)(t.m0 + i / BCOLS) * a.H + t.n * BCOLS + i % BCOLS] = 0.0f;
       }
       return;
     }
@@ -655,7 +736,7 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(Ge
   constexpr int D = MAXNMI == 4 ? 2 : (Q3 ? 3 : 5);
   const int nmi = __builtin_amdgcn_readfirstlane((t.rows + 31) >> 5);
   if (MAXNMI == 1 || nmi == 1) {
-    gemm_tile<GATEUP, 1, MAXNMI, D, Q3>(g, t, As);
+    gemm_tile<GATEUP, 1, MAXNMI, D, Q3, HALF>(g, t, As);
   } else if (MAXNMI == 2 || nmi == 2) {
     gemm_tile<GATEUP, (MAXNMI >= 2 ? 2 : 1), MAXNMI, D, Q3>(g, t, As);
   } else if (nmi == 3) {
@@ -665,14 +746,15 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || Q3) ? 2 : 3) void k_gemm_q2(Ge
   }
 }
 
-template <int MAXNMI, bool Q3>
+template <int MAXNMI, bool Q3, bool HALF = false>
 static hipError_t launch_gemm_q2_t(GemvKind kind, GemmKArgs a, int max_tiles, void* out, hipStream_t s) {
   if (kind == GemvKind::GateUp) {
     a.h_out = (uint16_t*)out;
-    MOE_LAUNCH((k_gemm_q2<true, MAXNMI, Q3>), dim3(max_tiles, a.I / 128), dim3(256), 0, s, a);
+    MOE_LAUNCH((k_gemm_q2<true, MAXNMI, Q3, HALF>), dim3(max_tiles, a.I / (HALF ? 64 : 128)), dim3(256), 0, s, a);
   } else {
     a.y_out = a.y16 ? nullptr : (float*)out;
-    MOE_LAUNCH((k_gemm_q2<false, MAXNMI, Q3>), dim3(max_tiles, a.H / GCOLS), dim3(256), 0, s, a);
+    MOE_LAUNCH((k_gemm_q2<false, MAXNMI, Q3, HALF>), dim3(max_tiles, a.H / (HALF ? 128 : GCOLS)), dim3(256), 0, s,
+               a);
   }
   return hipGetLastError();
 }
@@ -705,9 +787,9 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
   a.xexp = xexp;
   if (q3) {
     // 3-bit weights run on 32-row tiles only (the 128-row kernel's registers
-    // have no room for the high-bit planes); y16 is not used with them
+    // have no room for the high-bit planes), half-width; y16 is not used with them
     if (tile_rows != 32 || y16) return hipErrorInvalidValue;
-    return launch_gemm_q2_t<1, true>(kind, a, max_tiles, out, s);
+    return launch_gemm_q2_t<1, true, true>(kind, a, max_tiles, out, s);
   }
   if (tile_rows == 32) return launch_gemm_q2_t<1, false>(kind, a, max_tiles, out, s);
   return launch_gemm_q2_t<GBM / 32, false>(kind, a, max_tiles, out, s);

@@ -506,11 +506,15 @@ def test_layer_forced_tie(T):
     np.testing.assert_allclose(gates[:, :3], g_r[:, :3], rtol=0, atol=GATE_TOL)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("workload,T", [("decode", 4), ("prefill", 64), ("prefill", 1024), ("cache", 64)])
+def test_graph_replay_matches_eager(workload, T):
     # the whole layer call captured into one HIP graph; every replay (with other
-    # eager work between them) must equal the eager result bit for bit
-    hl = W.host_layer("decode")
-    T = 4
+    # eager work between them) must equal the eager result bit for bit.  The
+    # cases take the decode path, the 32-row grouped GEMM (split router, the top-k
+    # that writes the fp16 copy of x, single-block permutation), the prompt path
+    # (MFMA router, multi-block permutation, 128-row GEMMs, fp16 combine) and the
+    # 3-bit half-width GEMM.
+    hl = W.host_layer(workload)
     x, _ = W.activations_with_margin(hl, T)
     x2 = synth.activations(31, 0, T, hl.H)
     d = W.upload(hl)

@@ -94,3 +94,31 @@ def test_stack_48_layers(stack, T):
         got = host(ids)
         for t in np.flatnonzero(ok):
             assert set(got[t].tolist()) == set(ref_ids[t].tolist()), f"layer {l} token {t}"
+
+
+@pytest.mark.parametrize("T", [1, 128])
+def test_stack_graph_replay_matches_eager(stack, T):
+    # the 48-layer stack captured into one HIP graph: every replay, with eager work
+    # on the same workspace between replays, equals the eager result bit for bit
+    hls, devs = stack
+    H = synth.CONFIGS["stack"].shape.hidden
+    structs = [d.struct for d in devs]
+    x0, _ = W.activations_with_margin(hls[0], T)
+    x1 = synth.activations(77, 0, T, H)
+    ws = devs[0].workspace(T)
+    xd, x1d = W.upload_rows(x0), W.upload_rows(x1)
+    x_out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    other = torch.empty_like(x_out)
+    B.stack_forward(structs, xd, T, x_out, ws)
+    torch.cuda.synchronize()
+    eager = host(x_out).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.stack_forward(structs, xd, T, x_out, ws)
+    for rep in range(3):
+        x_out.zero_()
+        B.stack_forward(structs, x1d, T, other, ws)      # eager work on the same workspace in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(x_out), eager, err_msg=f"replay {rep}")

@@ -717,6 +717,17 @@ def main():
     ms1, _, uniq1 = run(1, max(args.steps // 2, 1), args.warmup, False)
     ms1_step = ms1 / max(args.steps // 2, 1)
     step_bytes1 = E * H * 2 + (float(uniq1.mean()) + 1) * eb + H * 2 + H * 4
+    # an MTP verify batch of 32 sequences x (1 + 3 drafts): 128 independent tokens on the
+    # same layers (the 32-row grouped GEMM path)
+    TV, sv = 128, max(args.steps // 10, 1)
+    msv, _, uniqv = run(TV, sv, max(args.warmup // 10, 5), False)
+    msv_step = msv / sv
+    dv = float(uniqv.mean())
+    bytes_v = E * H * 2 + (dv + 1) * eb + TV * H * 2 + TV * H * 4
+    flops_v = 2.0 * TV * H * E + TV * (k + 1) * 6.0 * H * I
+    gbps_v = bytes_v / (msv_step * 1e-3) / 1e9
+    tflops_v = flops_v / (msv_step * 1e-3) / 1e12
+    hbm_bound_v = flops_v / bytes_v < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
     result = {
         "metric": "MoE-layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak",
@@ -752,6 +763,21 @@ def main():
                           "down_gemv": kms[B.KERNEL_DOWN_GEMV] * 1e3},
             "T1": {"tokens_per_s": 1 / (ms1_step * 1e-3), "layer_us": ms1_step * 1e3,
                    "layer_GBps": step_bytes1 / (ms1_step * 1e-3) / 1e9},
+        },
+        "verify": {
+            "workload": f"verify: one real-shape 2-bit layer, T={TV} independent tokens (32 sequences x (1 + 3 MTP "
+                        f"drafts)), the decode layers and router, {R} distinct layers rotated",
+            "layer_us": msv_step * 1e3,
+            "tokens_per_s": TV / (msv_step * 1e-3),
+            "unique_experts_per_step": dv,
+            "algorithmic_MB_per_step": bytes_v / 1e6,
+            "GBps": gbps_v,
+            "hbm_frac": gbps_v / HBM_PEAK_GBS,
+            "algorithmic_GFLOP_per_step": flops_v / 1e9,
+            "TFLOPs": tflops_v,
+            "mfma_frac_of_fp16_peak": tflops_v / MFMA_BF16_PEAK_TFLOPS,
+            "bound": "hbm" if hbm_bound_v else "mfma",
+            "roofline_frac": gbps_v / HBM_PEAK_GBS if hbm_bound_v else tflops_v / MFMA_BF16_PEAK_TFLOPS,
         },
         "roofline": {
             "kernel": "k_decode_gateup_mx (top-k, gate/up + SwiGLU on the fp8 x fp4 matrix cores, down-table epilogue)",

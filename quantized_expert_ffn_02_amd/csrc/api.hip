@@ -66,6 +66,7 @@ struct Layout {
   size_t xtab_pairs, xtab_init, xf32, xf16, xexp, hf16, tiles, n_tiles;
   size_t h, htab_pairs, htab_init, y;
   size_t xmx_data, xmx_exps, hmx_data, hmx_exps;   // fp8-piece tables (mx.h)
+  int64_t mx_tokens;                                // tokens those tables hold (entries: k + 1 each)
   size_t norm_sq;                                   // partial sums of squares of a stack layer's output
   size_t out_f32, xa, xb, xn;     // stack ping-pong buffers and the normalised layer input
   size_t miss_flag;
@@ -105,15 +106,20 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xexp = take(dense ? 0 : T * 4);   // row exponents of the fp16 copy
   o.hf16 = take(dense ? 0 : n * I * 2);
   o.tiles = take((n / kSmallTileRows + E + 2) * 3 * 4);   // GEMM tiles (128 or 32 rows)
-  o.n_tiles = take(4);
+  o.n_tiles = take(8);                                      // all tiles, fp16 tiles
   o.h = take(n * I * 4);
   o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
   o.htab_init = take(dense ? 0 : n * (I / 32) * 4);
   o.y = take(n * H * 4);
-  // fp8-piece tables of the 2-bit decode batch (up to kDecodeDirectMaxTokens tokens)
-  const bool mx = decode_mx_ok((int)H, (int)I, L->routed.fmt == MOE_FMT_Q3 ? 1 : 0) && !dense;
-  const int64_t Tm = mx ? (T < kDecodeDirectMaxTokens ? T : kDecodeDirectMaxTokens) : 0;
+  // fp8-piece tables of the 2-bit decode batch (up to kDecodeDirectMaxTokens tokens),
+  // and of the fp8 x fp4 tiles of a 2-bit batch on the 32-row GEMM path (any T below a
+  // prompt chunk: x per token, h per entry)
+  const bool q2 = L->routed.fmt == MOE_FMT_Q2;
+  const bool mx = decode_mx_ok((int)H, (int)I, q2 ? 0 : 1) && !dense;
+  const bool mxt = q2 && T > kDecodeDirectMaxTokens && T < 1024 && mx_tiles_ok((int)H, (int)I);
+  const int64_t Tm = mxt ? T : mx ? (T < kDecodeDirectMaxTokens ? T : kDecodeDirectMaxTokens) : 0;
   const int64_t nm = Tm * k + Tm;
+  o.mx_tokens = Tm;
   o.xmx_data = take(Tm * mx_data_bytes((int)H));
   o.xmx_exps = take(Tm * mx_exps_bytes((int)H));
   o.hmx_data = take(nm * mx_data_bytes((int)I));
@@ -185,8 +191,10 @@ int mfma_min_rows(int T);
 // x_f16 (optional): when the top-k runs as its own launch (T > 16) it also writes
 // the grouped GEMMs' scaled fp16 copy of x and its row exponents into the
 // workspace; *x_f16 says whether it did.
+// mx_table: the top-k launch of a verify batch also writes x's fp8-piece table (the
+// fp8 x fp4 tiles of the 32-row GEMM path)
 int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float* gates, float* margin, void* ws,
-             const Layout& lay, hipStream_t s, bool* x_f16 = nullptr) {
+             const Layout& lay, hipStream_t s, bool* x_f16 = nullptr, bool mx_table = false) {
   const bool fuse = x_f16 && T > 16 && L->routed.fmt != MOE_FMT_BF16 && topk_row_f16_ok(L->hidden);
   const uint16_t* fx = fuse ? x : nullptr;
   uint16_t* fxf = fuse ? at<uint16_t>(ws, lay.xf16) : nullptr;
@@ -205,12 +213,14 @@ int do_route(const moe_layer_t* L, const uint16_t* x, int T, int32_t* ids, float
                                  parts > 1 ? rparts : logits, parts, s);
     return launch_router_gemv(x, T, L->w_router, L->router_bias, L->n_experts, L->hidden, logits, s);
   }));
+  uint8_t* tabd = mx_table ? at<uint8_t>(ws, lay.xmx_data) : nullptr;
+  uint8_t* tabe = mx_table ? at<uint8_t>(ws, lay.xmx_exps) : nullptr;
   if (parts > 1)
     MOE_TRY(launch_topk(rparts, T, L->n_experts, L->top_k, ids, gates, margin, s, parts, L->router_bias, fx,
-                        L->hidden, fxf, fxe));
+                        L->hidden, fxf, fxe, x, tabd, tabe));
   else
     MOE_TRY(launch_topk(logits, T, L->n_experts, L->top_k, ids, gates, margin, s, 1, nullptr, fx, L->hidden, fxf,
-                        fxe));
+                        fxe, x, tabd, tabe));
   return MOE_OK;
 }
 
@@ -428,16 +438,24 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   int32_t* srt = at<int32_t>(ws, lay.sorted_rows);
   int32_t* inv = at<int32_t>(ws, lay.row_to_sorted);
   bool xw = false;   // the top-k launch wrote the fp16 copy of x
-  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s, x_f16_ready ? nullptr : &xw);
+  const bool q3 = routed.fmt == MOE_FMT_Q3;
+  // groups of up to kMxTileRows entries on the fp8 x fp4 matrix cores (2-bit)
+  const bool mxt = !q3 && T < 1024 && mx_tiles_ok(H, I) && lay.mx_tokens >= T;
+  int rc = do_route(L, x, T, ids, gates, margin, ws, lay, s, x_f16_ready ? nullptr : &xw, mxt);
   if (rc) return rc;
   if (after_route && (rc = (*after_route)())) return rc;
   int32_t* chunks = at<int32_t>(ws, lay.tiles);
   int32_t* n_chunks = at<int32_t>(ws, lay.n_tiles);
   MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
                               at<int32_t>(ws, lay.base), 1, 1, kSmallTileRows, chunks, n_chunks,
-                              at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items), s));
+                              at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items), s,
+                              mxt ? kMxTileRows : 0));
   const int max_chunks = n / kSmallTileRows + std::min(E + 1, n) + 1;
-  const bool q3 = routed.fmt == MOE_FMT_Q3;
+  MxTables mxtab;
+  mxtab.x_data = at<uint8_t>(ws, lay.xmx_data);
+  mxtab.x_exps = at<uint8_t>(ws, lay.xmx_exps);
+  mxtab.h_data = at<uint8_t>(ws, lay.hmx_data);
+  mxtab.h_exps = at<uint8_t>(ws, lay.hmx_exps);
   const MatRef r13 = mat_w13(routed), r2 = mat_w2(routed);
   const MatRef s13 = with_shared ? mat_w13(L->shared) : MatRef(), s2 = with_shared ? mat_w2(L->shared) : MatRef();
   uint16_t* xf = at<uint16_t>(ws, lay.xf16);
@@ -448,11 +466,11 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   if (!x_f16_ready && !xw) MOE_TRY(launch_x_to_f16_pairs(x, T, H, xf, xexp, s));
   MOE_TRY(timed(MOE_KERNEL_GATEUP_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::GateUp, r13, s13, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, xf, hf, s,
-                          nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp);
+                          nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp, mxt ? &mxtab : nullptr);
   }));
   MOE_TRY(timed(MOE_KERNEL_DOWN_GEMM, s, [&] {
     return launch_gemm_q2(GemvKind::Down, r2, s2, H, I, E, chunks, n_chunks, max_chunks, srt, T, k, hf, y, s,
-                          nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp);
+                          nullptr, nullptr, kSmallTileRows, q3, slot_map, xexp, mxt ? &mxtab : nullptr);
   }));
   if (norm_next)
     MOE_TRY(launch_combine_norm(y, inv, gates, T, k, H, with_shared, residual, out, out_bf16, norm_next->eps,

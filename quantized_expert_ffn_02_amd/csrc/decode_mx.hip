@@ -59,11 +59,6 @@ __device__ __forceinline__ mx_v8i mx_act_operand(const MxAct& A) {
   return a;
 }
 
-// y + s * (sum of the four pieces' outputs) for this lane's (weight row, block).
-__device__ __forceinline__ float mx_accumulate(const mx_v4f& o, uint32_t scale16, float y) {
-  return fmaf(fp16_to_f32(scale16), (o[0] + o[1]) + (o[2] + o[3]), y);
-}
-
 // Gate/up in the 256-column form: per 256 columns and 16-row subgroup, lane
 // (n, q) = (lane % 16, lane / 16) loads the 16 code bytes of row n, 64-column
 // chunk q (blocks 2 q and 2 q + 1) and their two fp16 scales; the first MFMA

@@ -31,6 +31,7 @@
 #include "device.h"
 #include "internal.h"
 #include "mfma.h"
+#include "mx_group.h"
 
 namespace moe {
 
@@ -237,13 +238,16 @@ __device__ __forceinline__ void wave_step_half3(const uint16_t* __restrict__ As,
 // ---------------------------------------------------------------------------
 struct GemmTile {
   int g, m0, rows, n;   // n = column-tile index
+  bool mx;              // a small group on the fp8 x fp4 matrix cores (mx_group.h)
 };
 
 // Workgroups are placed on the 8 XCDs round-robin by linear id.  Only the
 // first n_valid = tiles x column-tiles linear ids carry work (the grid is a host
 // bound); re-number those so that XCD x runs a contiguous range of logical
 // tiles, column-tile fastest: the column tiles of one row tile then share its
-// activation rows in one L2, and every XCD still gets 1/8 of the work.
+// activation rows in one L2, and every XCD still gets 1/8 of the work.  The
+// fp16 tiles, listed first by the plan, are numbered apart from the fp8 x fp4
+// tiles after them, so that every XCD starts with its share of the longer ones.
 __device__ __forceinline__ int xcd_logical_id(int lin, int n_valid) {
   const int per = (n_valid + 7) / 8;
   const int xcd = lin & 7, slot = lin >> 3;
@@ -256,12 +260,15 @@ __device__ __forceinline__ bool load_tile(const int32_t* __restrict__ tiles, con
   const int lin = blockIdx.y * gridDim.x + blockIdx.x;
   const int n_valid = n_tiles[0] * (int)gridDim.y;
   if (lin >= n_valid) return false;
-  const int id = xcd_logical_id(lin, n_valid);
+  const int n_f16 = n_tiles[1] * (int)gridDim.y;
+  const int id = lin < n_f16 ? xcd_logical_id(lin, n_f16) : n_f16 + xcd_logical_id(lin - n_f16, n_valid - n_f16);
   const int mt = id / gridDim.y;
   t.n = id % gridDim.y;
   t.g = tiles[3 * mt];
   t.m0 = tiles[3 * mt + 1];
-  t.rows = tiles[3 * mt + 2];
+  const int rw = tiles[3 * mt + 2];
+  t.rows = rw & (kTileMx - 1);
+  t.mx = (rw & kTileMx) != 0;
   return true;
 }
 
@@ -666,7 +673,61 @@ struct GemmKArgs {
   uint16_t* y16;
   const int32_t* slot_map;   // expert-cache mode: pool slot of routed group g, or -1 (a miss)
   const int32_t* xexp;       // row exponent of each token (x' = x 2^a), or NULL (a = 0)
+  MxTables mx;               // fp8-piece tables of the fp8 x fp4 tiles
 };
+
+static constexpr int kMxTileMaxI = 768;
+#ifndef MOE_MX_DEPTH
+#define MOE_MX_DEPTH 2
+#endif
+static constexpr int kMxDepth = MOE_MX_DEPTH;   // 256-column code chunks in flight per wave (gate/up)
+bool mx_tiles_ok(int H, int I) {
+  return H % 256 == 0 && H <= kMxTileMaxH && (I == 512 || I == 640 || I == 768);
+}
+
+// An fp8 x fp4 tile (mx_group.h) on the block's 4 waves: the rows' tables into
+// LDS, then each wave's columns.
+template <bool GATEUP>
+__device__ __forceinline__ void gemm_tile_mx(const GemmKArgs& a, const GemmTile& t, const MatRef& M, size_t eidx,
+                                             uint8_t* lds) {
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(M.codes + eidx * M.code_stride, (uint32_t)M.code_stride);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(M.scales + eidx * M.scale_stride, (uint32_t)(M.scale_stride * 2));
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // source rows of the tables: the token of each entry (x), or the sorted
+  // position itself (h); rows past the tile repeat its last row (never read)
+  int src[kMxTileRows];
+#pragma unroll
+  for (int j = 0; j < kMxTileRows; ++j) {
+    const int p = t.m0 + (j < t.rows ? j : t.rows - 1);
+    if (GATEUP) {
+      const int r = a.sorted_rows[p], Tk = a.T * a.k;
+      src[j] = r < Tk ? r / a.k : r - Tk;
+    } else {
+      src[j] = p;
+    }
+  }
+  // each wave issues its first code loads, then the block stages the tables
+  if (GATEUP) {
+    auto stage = [&] {
+      mx_stage<kMxTileMaxH>(lds, a.mx.x_data, a.mx.x_exps, a.H, t.rows, src);
+      __syncthreads();
+    };
+    mx_tile_gateup<kMxDepth>(lds, t.rows, a.H, a.I, t.n * 128 + 32 * wv, rc, rs, t.m0, a.mx.h_data, a.mx.h_exps,
+                             stage);
+  } else {
+    auto stage = [&] {
+      mx_stage<kMxTileMaxI>(lds, a.mx.h_data, a.mx.h_exps, a.I, t.rows, src);
+      __syncthreads();
+    };
+    const int o0 = t.n * GCOLS + 64 * wv;
+    if (a.I == 512)
+      mx_tile_down<2, 0>(lds, t.rows, a.H, o0, rc, rs, t.m0, a.y_out, stage);
+    else if (a.I == 640)
+      mx_tile_down<2, 1>(lds, t.rows, a.H, o0, rc, rs, t.m0, a.y_out, stage);
+    else
+      mx_tile_down<3, 0>(lds, t.rows, a.H, o0, rc, rs, t.m0, a.y_out, stage);
+  }
+}
 
 // One kernel per projection, tile height and format: MAXNMI = 4 (128-row
 // tiles, 2-bit, for prompt chunks) or 1 (32-row tiles, for verify batches of
@@ -674,10 +735,16 @@ struct GemmKArgs {
 // with half-width tiles).
 // In expert-cache mode a tile whose group has no slot computes nothing: the
 // down projection writes zero rows, so the combine adds nothing for it.
+// The 2-bit 32-row kernels also run the fp8 x fp4 tiles of small groups (MX);
+// their LDS holds either the three A buffers or the staged tables.
 template <bool GATEUP, int MAXNMI, bool Q3, bool HALF = false>
 __global__ __launch_bounds__(256, (MAXNMI == 4 || (Q3 && !HALF)) ? 2 : 3) void k_gemm_q2(GemmKArgs a) {
   constexpr int BCOLS = HALF ? 128 : GCOLS;   // output columns of a down block
-  __shared__ __attribute__((aligned(16))) uint16_t As[3 * 32 * MAXNMI * A_STRIDE];
+  constexpr bool MX = MAXNMI == 1 && !Q3;
+  constexpr int AS_BYTES = 3 * 32 * MAXNMI * A_STRIDE * 2;
+  constexpr int MX_BYTES = MX ? mx_stage_bytes(GATEUP ? kMxTileMaxH : kMxTileMaxI) : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[AS_BYTES > MX_BYTES ? AS_BYTES : MX_BYTES];
+  uint16_t* As = reinterpret_cast<uint16_t*>(lds);
   __shared__ float row_gate[32 * MAXNMI];
   __shared__ int32_t row_exp[32 * MAXNMI];
   GemmTile t;
@@ -691,6 +758,12 @@ __global__ __launch_bounds__(256, (MAXNMI == 4 || (Q3 && !HALF)) ? 2 : 3) void k
         for (int i = threadIdx.x; i < t.rows * BCOLS; i += blockDim.x)
           a.y_out[(size_t)(t.m0 + i / BCOLS) * a.H + t.n * BCOLS + i % BCOLS] = 0.0f;
       }
+      return;
+    }
+  }
+  if constexpr (MX) {
+    if (t.mx) {
+      gemm_tile_mx<GATEUP>(a, t, sh ? a.shared : a.routed, sh ? 0 : (size_t)slot, lds);
       return;
     }
   }
@@ -762,8 +835,12 @@ static hipError_t launch_gemm_q2_t(GemvKind kind, GemmKArgs a, int max_tiles, vo
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates,
-                          uint16_t* y16, int tile_rows, bool q3, const int32_t* slot_map, const int32_t* xexp) {
+                          uint16_t* y16, int tile_rows, bool q3, const int32_t* slot_map, const int32_t* xexp,
+                          const MxTables* mx) {
   if (max_tiles <= 0) return hipSuccess;
+  // fp8 x fp4 tiles: 2-bit 32-row tiles writing fp32 rows
+  if (mx && (q3 || tile_rows != 32 || y16 || !mx_tiles_ok(H, I) || !mx->x_data || !mx->h_data))
+    return hipErrorInvalidValue;
   // the kernels address activations and one expert's weights with 32-bit
   // buffer offsets
   const uint64_t a_bytes = kind == GemvKind::GateUp ? (uint64_t)T * H * 2 : (uint64_t)T * (k + 1) * I * 2;
@@ -785,6 +862,7 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
   a.y16 = y16;
   a.slot_map = slot_map;
   a.xexp = xexp;
+  if (mx) a.mx = *mx;
   if (q3) {
     // 3-bit weights run on 32-row tiles only (the 128-row kernel's registers
     // have no room for the high-bit planes), half-width; y16 is not used with them
@@ -987,7 +1065,8 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ offse
     items[3 * (pi + i) + 2] = min(items_per, cnt - i * items_per);
   }
   if (g == 0) {
-    *n_tiles = tot_t;
+    n_tiles[0] = tot_t;
+    n_tiles[1] = tot_t;   // all fp16 tiles
     *n_items = tot_i;
   }
 }

@@ -184,12 +184,15 @@ hipError_t launch_route_front(const SmallRouteArgs& a, hipStream_t s);
 // parts > 1: ``logits`` holds ``parts`` partial planes [T][E] to be added in
 // plane order, then ``bias`` (launch_router_split with parts > 1).  With x set,
 // the same launch also writes the grouped GEMMs' activation copy of x (as
-// launch_x_to_f16_pairs: xf16 [T][H] and xexp [T]); topk_row_f16_ok(H).
+// launch_x_to_f16_pairs: xf16 [T][H] and xexp [T]); topk_row_f16_ok(H).  With xmx_data
+// set, extra blocks of the same launch write the fp8-piece table of xt (bf16 [T][H],
+// H % 256 == 0; mx.h, 256-column form) for the fp8 x fp4 tiles of the grouped GEMM.
 static constexpr int kRowF16MaxH = 3072;
 bool topk_row_f16_ok(int H);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
                        hipStream_t s, int parts = 1, const float* bias = nullptr, const uint16_t* x = nullptr,
-                       int H = 0, uint16_t* xf16 = nullptr, int32_t* xexp = nullptr);
+                       int H = 0, uint16_t* xf16 = nullptr, int32_t* xexp = nullptr, const uint16_t* xt = nullptr,
+                       uint8_t* xmx_data = nullptr, uint8_t* xmx_exps = nullptr);
 
 // permutation: counts/base are [n_chunks][E + 2] int32 scratch
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
@@ -198,10 +201,13 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shar
 int permute_chunks(int n_entries);
 // permutation followed by the plan (launch_plan); batches of up to 16,384 entries
 // in one single-block launch
+// mx_rows > 0: every group of 1 .. mx_rows entries becomes one tile of the fp8 x fp4
+// form (rows | kTileMx), listed after all the fp16 tiles; n_tiles[0] counts all
+// tiles, n_tiles[1] the fp16 ones
 hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
                                int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
                                int min_rows, int items_per, int tile_rows, int32_t* tiles, int32_t* n_tiles,
-                               int32_t* items, int32_t* n_items, hipStream_t s);
+                               int32_t* items, int32_t* n_items, hipStream_t s, int mx_rows = 0);
 // work items of a permutation (see PermRef), from its offsets
 hipError_t launch_items_from_offsets(const int32_t* offsets, int E, int items_per, int32_t* items,
                                      int32_t* n_items, hipStream_t s);
@@ -226,13 +232,31 @@ hipError_t launch_gemv_dense(GemvKind kind, const MatRef& routed, const MatRef& 
 // MFMA path (gemm.hip)
 // x' = x 2^a per row (a = -floor(log2 max|x_row|), written to xexp[T]) as fp16 in pair order
 hipError_t launch_x_to_f16_pairs(const uint16_t* x, int T, int H, uint16_t* out, int32_t* xexp, hipStream_t s);
+// The fp8-piece tables of the fp8 x fp4 tiles (2-bit, 32-row tiles): x [T] rows in the
+// 256-column form (read), h [sorted position] rows in the mixed form (written by
+// gate/up, read by down).
+struct MxTables {
+  const uint8_t* x_data = nullptr;
+  const uint8_t* x_exps = nullptr;
+  uint8_t* h_data = nullptr;
+  uint8_t* h_exps = nullptr;
+};
 hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& shared, int H, int I, int E,
                           const int32_t* tiles, const int32_t* n_tiles, int max_tiles, const int32_t* sorted_rows,
                           int T, int k, const uint16_t* a_f16, void* out, hipStream_t s, const float* gates = nullptr,
                           uint16_t* y16 = nullptr, int tile_rows = 128, bool q3 = false,
-                          const int32_t* slot_map = nullptr, const int32_t* xexp = nullptr);
+                          const int32_t* slot_map = nullptr, const int32_t* xexp = nullptr,
+                          const MxTables* mx = nullptr);
 // rows per tile of the grouped GEMM for batches beyond a decode step and below a prompt chunk
 static constexpr int kSmallTileRows = 32;
+// Tiles of an expert group of at most kMxTileRows entries on the 32-row 2-bit path
+// run on the block-scaled fp8 x fp4 matrix cores (the decode form, one product per
+// row over codes loaded once) instead of dequantising the expert into fp16; the plan
+// marks them with kTileMx in the rows field.  Shapes: mx_tiles_ok.
+static constexpr int kMxTileRows = 4;
+static constexpr int kTileMx = 1 << 16;
+static constexpr int kMxTileMaxH = 3072;
+bool mx_tiles_ok(int H, int I);
 // router of such batches (router_split.hip): 32 tokens x 64 experts per unit, K split over
 // ``parts`` blocks (router_parts) and over the 4 waves of each; parts == 1 writes logits (with
 // the bias), parts > 1 writes partial planes [parts][T][E] (without it) for launch_topk

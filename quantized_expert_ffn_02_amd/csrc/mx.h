@@ -73,24 +73,6 @@ __device__ __forceinline__ int mx_weight_at(int p) {
   return (p & 16) | (i < 8 ? 2 * i : 2 * (i - 8) + 1);
 }
 
-// fp32 -> OCP e4m3 byte, round to nearest even, for |f| < 448 (the pieces
-// are below 256 by construction).  Below 2^-6 the format steps by 2^-9
-// (subnormals; 8 steps is the smallest normal, whose byte is also 8).
-__device__ __forceinline__ uint32_t e4m3_rne(float f) {
-  const uint32_t s = (__float_as_uint(f) >> 24) & 0x80u;
-  const float a = fabsf(f);
-  if (a < 0.015625f) return s | (uint32_t)__builtin_rintf(a * 512.0f);
-  const uint32_t au = __float_as_uint(a);
-  const uint32_t r = au + 0x7FFFFu + ((au >> 20) & 1u);   // significand rounded to 3 bits
-  return s | (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t ef = (b >> 3) & 15u, m = b & 7u;
-  const float mag = ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  return (b & 0x80u) ? -mag : mag;
-}
-
 // Largest |v| over each 32-lane half of the wave, in every lane of that half:
 // DPP steps inside each 16-lane row (magnitudes as unsigned words order like
 // the floats; moves from outside the row read 0), then the four row results.
@@ -110,20 +92,34 @@ __device__ __forceinline__ float half_wave_max_abs(float v) {
 
 // Pieces of the value v held by this lane; the 32 lanes of each half wave form
 // one block (all 64 lanes must call).  p[j]: e4m3 bytes; sb[j]: E8M0 scale
-// bytes (127 + e_j + 1).
+// bytes (127 + e_j + 1).  Piece j is k_j * 16 * 2^e_j with k_j = rint(r / u_j),
+// u_j = 2^(e_j + 4) its unit (u_j and 1 / u_j normal floats for every e here, so
+// both products are exact), r = fma(-k_j, u_j, r) the exact remainder; 16 k_j
+// (|k_j| <= 16) is an e4m3 value exactly, converted two at a time by the
+// hardware (no rounding happens).
 __device__ __forceinline__ void mx_pieces(float v, uint32_t (&p)[kMxPieces], uint32_t (&sb)[kMxPieces]) {
   const float m = half_wave_max_abs(v);
   int e = (int)((__float_as_uint(m) >> 23) & 255u) - 134;   // floor(log2 m) - 7
   e = m > 0.0f ? (e < -113 ? -113 : e) : 0;                  // e - 15 stays a valid scale
-  float r = v;
+  float u = __uint_as_float((uint32_t)(e + 4 + 127) << 23);         // 2^(e_0 + 4)
+  float ui = __uint_as_float((uint32_t)(127 - (e + 4)) << 23);      // 2^-(e_0 + 4)
+  float r = v, k16[kMxPieces];
 #pragma unroll
   for (int j = 0; j < kMxPieces; ++j) {
-    const int ej = e - 5 * j;
-    const float k16 = 16.0f * __builtin_rintf(ldexpf(r, -ej) * 0.0625f);   // |k16| <= 256
-    p[j] = e4m3_rne(k16);
-    r -= ldexpf(k16, ej);
-    sb[j] = (uint32_t)(128 + ej);
+    const float k = __builtin_rintf(r * ui);
+    r = fmaf(-k, u, r);
+    k16[j] = 16.0f * k;
+    sb[j] = (uint32_t)(128 + e - 5 * j);
+    u *= 0.03125f;
+    ui *= 32.0f;
   }
+  static_assert(kMxPieces == 4, "two packed conversions");
+  const uint32_t b01 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(k16[0], k16[1], 0, false);
+  const uint32_t b23 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(k16[2], k16[3], 0, false);
+  p[0] = b01 & 0xFFu;
+  p[1] = (b01 >> 8) & 0xFFu;
+  p[2] = b23 & 0xFFu;
+  p[3] = (b23 >> 8) & 0xFFu;
 }
 
 // fp4 operand of a 32-weight block from its two code words.
@@ -149,6 +145,12 @@ __device__ __forceinline__ mx_v8i mx_minus_one() {
 // 16 weight rows (fp4, unit scales), plus c.
 __device__ __forceinline__ mx_v4f mx_mfma(const mx_v8i& a, const mx_v8i& b, int sa, const mx_v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
+}
+
+// y + s * (sum of the four pieces' outputs) for this lane's (weight row, block);
+// s is the block's fp16 weight scale.
+__device__ __forceinline__ float mx_accumulate(const mx_v4f& o, uint32_t scale16, float y) {
+  return fmaf(fp16_to_f32(scale16), (o[0] + o[1]) + (o[2] + o[3]), y);
 }
 
 // Per-lane constants for reading a row's activation operand of one chunk
@@ -197,6 +199,44 @@ __device__ __forceinline__ void mx_emit(float v, int row, int slot, int p, int K
   if (p == 0)
     reinterpret_cast<uint32_t*>(exps + (size_t)row * mx_exps_bytes(K))[slot] =
         sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+}
+
+// Table of T rows of bf16 x (256-column form) built by blocks blk of nblk
+// (256 threads each): element it = (row, column) in the table's column order
+// (the thread of block position p reads the weight index at p).  A pass gives
+// each thread kMxTablePer elements, 256 apart, whose loads are all issued
+// before the first piece is made.  T H is a multiple of 64, so the waves are
+// whole and all 64 lanes of each take part in the block maxima.
+static constexpr int kMxTablePer = 4;
+
+__host__ __device__ constexpr int mx_table_blocks(int T, int H, int cap) {
+  return (T * H + 256 * kMxTablePer - 1) / (256 * kMxTablePer) < cap ? (T * H + 256 * kMxTablePer - 1) / (256 * kMxTablePer)
+                                                                    : cap;
+}
+
+__device__ __forceinline__ void mx_table_pass(const uint16_t* __restrict__ x, int T, int H, uint8_t* __restrict__ data,
+                                              uint8_t* __restrict__ exps, int blk, int nblk) {
+  const int items = T * H;
+  for (int base = blk * 256 * kMxTablePer; base < items; base += nblk * 256 * kMxTablePer) {
+    float v[kMxTablePer];
+#pragma unroll
+    for (int u = 0; u < kMxTablePer; ++u) {
+      const int it = base + u * 256 + (int)threadIdx.x;
+      v[u] = 0.0f;
+      if (it < items) {
+        const int row = it / H, col = it - row * H;
+        v[u] = bf16_to_f32(x[(size_t)row * H + (col & ~31) + mx_weight_at(col & 31)]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMxTablePer; ++u) {
+      const int it = base + u * 256 + (int)threadIdx.x;
+      if (it < items) {
+        const int row = it / H, col = it - row * H;
+        mx_emit(v[u], row, mx_slot256(col >> 5), col & 31, H, data, exps);
+      }
+    }
+  }
 }
 
 }  // namespace moe

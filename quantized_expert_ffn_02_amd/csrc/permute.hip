@@ -69,22 +69,38 @@ static constexpr int kScanBatch = 16;
 
 struct PlanOut {
   int min_rows = 0, items_per = 1, tile_rows = 1;
+  int mx_rows = 0;   // groups of 1 .. mx_rows entries: one fp8 x fp4 tile each
   int32_t *tiles = nullptr, *n_tiles = nullptr, *items = nullptr, *n_items = nullptr;
 };
 
 // Plan of the groups (as k_plan computes it) from thread g's group start and
-// count; every thread of the block calls it.
+// count; every thread of the block calls it.  The fp8 x fp4 tiles of small
+// groups (rows | kTileMx) follow all the fp16 tiles, so the longer fp16 tiles
+// are dispatched first; n_tiles[1] counts the fp16 tiles.
 __device__ void plan_groups(const PlanOut& P, int g, int start, int cnt) {
   const bool big = cnt >= P.min_rows;
-  const int nt = big ? (cnt + P.tile_rows - 1) / P.tile_rows : 0;
+  const bool mx = big && cnt > 0 && cnt <= P.mx_rows;
+  const int nt = big && !mx ? (cnt + P.tile_rows - 1) / P.tile_rows : 0;
   const int ni = big ? 0 : (cnt + P.items_per - 1) / P.items_per;
-  int tot_t = 0, tot_i = 0;
-  const int pt = block_exclusive_scan_1024(nt, &tot_t);
+  // with fp8 x fp4 tiles (batches below a prompt chunk: fewer than 2^20 fp16 tiles,
+  // at most 1,024 groups) one scan counts both kinds: fp16 tiles in the low 20
+  // bits, fp8 x fp4 tiles above them
+  int tot_tm = 0, tot_i = 0;
+  const int ptm = P.mx_rows > 0 ? block_exclusive_scan_1024(nt | (mx ? 1 << 20 : 0), &tot_tm)
+                                : block_exclusive_scan_1024(nt, &tot_tm);
   const int pi = block_exclusive_scan_1024(ni, &tot_i);
+  const int low = P.mx_rows > 0 ? (1 << 20) - 1 : -1;
+  const int pt = ptm & low, pm = P.mx_rows > 0 ? ptm >> 20 : 0;
+  const int tot_t = tot_tm & low, tot_m = P.mx_rows > 0 ? tot_tm >> 20 : 0;
   for (int i = 0; i < nt; ++i) {
     P.tiles[3 * (pt + i)] = g;
     P.tiles[3 * (pt + i) + 1] = start + i * P.tile_rows;
     P.tiles[3 * (pt + i) + 2] = min(P.tile_rows, cnt - i * P.tile_rows);
+  }
+  if (mx) {
+    P.tiles[3 * (tot_t + pm)] = g;
+    P.tiles[3 * (tot_t + pm) + 1] = start;
+    P.tiles[3 * (tot_t + pm) + 2] = cnt | kTileMx;
   }
   for (int i = 0; i < ni; ++i) {
     P.items[3 * (pi + i)] = g;
@@ -92,7 +108,8 @@ __device__ void plan_groups(const PlanOut& P, int g, int start, int cnt) {
     P.items[3 * (pi + i) + 2] = min(P.items_per, cnt - i * P.items_per);
   }
   if (g == 0) {
-    *P.n_tiles = tot_t;
+    P.n_tiles[0] = tot_t + tot_m;
+    P.n_tiles[1] = tot_t;
     *P.n_items = tot_i;
   }
 }
@@ -261,7 +278,7 @@ __global__ __launch_bounds__(1024) void k_perm_plan_small(const int32_t* __restr
                                                           int32_t* __restrict__ row_to_sorted, int min_rows,
                                                           int items_per, int tile_rows, int32_t* __restrict__ tiles,
                                                           int32_t* __restrict__ n_tiles, int32_t* __restrict__ items,
-                                                          int32_t* __restrict__ n_items) {
+                                                          int32_t* __restrict__ n_items, int mx_rows) {
   __shared__ int hw[16][1024];
   __shared__ int s_off[1025];
   const int G = E + 1;
@@ -324,6 +341,7 @@ __global__ __launch_bounds__(1024) void k_perm_plan_small(const int32_t* __restr
   P.min_rows = min_rows;
   P.items_per = items_per;
   P.tile_rows = tile_rows;
+  P.mx_rows = mx_rows;
   P.tiles = tiles;
   P.n_tiles = n_tiles;
   P.items = items;
@@ -335,18 +353,19 @@ __global__ __launch_bounds__(1024) void k_perm_plan_small(const int32_t* __restr
 hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
                                int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
                                int min_rows, int items_per, int tile_rows, int32_t* tiles, int32_t* n_tiles,
-                               int32_t* items, int32_t* n_items, hipStream_t s) {
+                               int32_t* items, int32_t* n_items, hipStream_t s, int mx_rows) {
   const int Tk = T * k;
   const int n = Tk + (with_shared ? T : 0);
   if (n <= kPermSmallMax && E + 1 <= 1024) {
     MOE_LAUNCH(k_perm_plan_small, dim3(1), dim3(1024), 0, s, ids, Tk, n, E, offsets, sorted_rows, row_to_sorted,
-               min_rows, items_per, tile_rows, tiles, n_tiles, items, n_items);
+               min_rows, items_per, tile_rows, tiles, n_tiles, items, n_items, mx_rows);
     return hipGetLastError();
   }
   PlanOut P;
   P.min_rows = min_rows;
   P.items_per = items_per;
   P.tile_rows = tile_rows;
+  P.mx_rows = mx_rows;
   P.tiles = tiles;
   P.n_tiles = n_tiles;
   P.items = items;

@@ -10,6 +10,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "mx.h"
 #include "topk.h"
 
 namespace moe {
@@ -77,11 +78,26 @@ __device__ __forceinline__ void wave_row_to_f16(const uint16_t* __restrict__ xr,
   }
 }
 
+// With tab.data set, blocks past the top-k's build x's fp8-piece table (mx.h,
+// 256-column form) for the grouped GEMM's fp8 x fp4 tiles, on the compute units
+// that the one-wave-per-token top-k leaves idle.
+struct MxTab {
+  const uint16_t* x = nullptr;   // bf16 [T][H], H % 256 == 0
+  int H = 0;
+  uint8_t* data = nullptr;
+  uint8_t* exps = nullptr;
+};
+
 template <int VPL, bool PARTS>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ gates,
                                               float* __restrict__ margin, int parts, const float* __restrict__ bias,
-                                              RowF16 f16) {
+                                              RowF16 f16, MxTab tab) {
+  const int kb = (T + 3) / 4;   // top-k blocks
+  if ((int)blockIdx.x >= kb) {
+    mx_table_pass(tab.x, T, tab.H, tab.data, tab.exps, (int)blockIdx.x - kb, (int)gridDim.x - kb);
+    return;
+  }
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   if (f16.x) wave_row_to_f16(f16.x + (size_t)t * f16.H, f16.H, f16.out + (size_t)t * f16.H, f16.xexp + t);
@@ -91,18 +107,18 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 
 template <bool PARTS>
 static hipError_t launch_topk_t(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
-                                int parts, const float* bias, const RowF16& f, hipStream_t s) {
-  dim3 grid((T + 3) / 4);
+                                int parts, const float* bias, const RowF16& f, const MxTab& mt, hipStream_t s) {
+  dim3 grid((T + 3) / 4 + (mt.data ? mx_table_blocks(T, mt.H, 512) : 0));
   if (E <= 64)
-    MOE_LAUNCH((k_topk<1, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f);
+    MOE_LAUNCH((k_topk<1, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f, mt);
   else if (E <= 128)
-    MOE_LAUNCH((k_topk<2, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f);
+    MOE_LAUNCH((k_topk<2, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f, mt);
   else if (E <= 256)
-    MOE_LAUNCH((k_topk<4, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f);
+    MOE_LAUNCH((k_topk<4, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f, mt);
   else if (E <= 512)
-    MOE_LAUNCH((k_topk<8, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f);
+    MOE_LAUNCH((k_topk<8, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f, mt);
   else
-    MOE_LAUNCH((k_topk<16, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f);
+    MOE_LAUNCH((k_topk<16, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f, mt);
   return hipGetLastError();
 }
 
@@ -110,7 +126,7 @@ bool topk_row_f16_ok(int H) { return H % 16 == 0 && H <= kRowF16MaxH; }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
                        hipStream_t s, int parts, const float* bias, const uint16_t* x, int H, uint16_t* xf16,
-                       int32_t* xexp) {
+                       int32_t* xexp, const uint16_t* xt, uint8_t* xmx_data, uint8_t* xmx_exps) {
   RowF16 f;
   if (x) {
     if (!topk_row_f16_ok(H) || !xf16 || !xexp) return hipErrorInvalidValue;
@@ -119,8 +135,16 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
     f.out = xf16;
     f.xexp = xexp;
   }
-  if (parts > 1) return launch_topk_t<true>(logits, T, E, k, ids, gates, margin, parts, bias, f, s);
-  return launch_topk_t<false>(logits, T, E, k, ids, gates, margin, 1, nullptr, f, s);
+  MxTab mt;
+  if (xmx_data) {
+    if (!xt || !xmx_exps || H % 256) return hipErrorInvalidValue;
+    mt.x = xt;
+    mt.H = H;
+    mt.data = xmx_data;
+    mt.exps = xmx_exps;
+  }
+  if (parts > 1) return launch_topk_t<true>(logits, T, E, k, ids, gates, margin, parts, bias, f, mt, s);
+  return launch_topk_t<false>(logits, T, E, k, ids, gates, margin, 1, nullptr, f, mt, s);
 }
 
 }  // namespace moe

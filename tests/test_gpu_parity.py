@@ -381,6 +381,49 @@ def test_gemm_path_medium_full_compare():
     assert err <= OUT_TOL
 
 
+@pytest.mark.parametrize("T", [17, 128, 300])
+def test_verify_batch_fp8_tiles(T):
+    # Independent tokens on the uniform-router layers: a verify batch of many
+    # sequences, whose experts mostly have one to four entries.  Those groups run as
+    # fp8 x fp4 tiles (codes loaded once, one product per row), the larger ones and
+    # the shared expert (T rows) as 32-row fp16 tiles, in the same launches.  The
+    # whole [T, H] output against the oracle, then rows rescaled over bf16's range
+    # (their experts are almost all small groups) one by one.  The rescalings are
+    # powers of two (2^17, 2^40, 2^-20, 2^-40: exact in bf16), so the uniform router
+    # ranks every rescaled row's experts as it ranked the row.
+    hl = shared_host_layer("decode")
+    x0, _ = W.activations_with_margin(hl, T)
+    rows = list(range(3, 3 + 4))
+    from oracle import formats
+    xf = formats.bf16_to_f64(x0[rows]).astype(np.float32)
+    for j, e in enumerate((17, 40, -20, -40)):
+        xf[j] *= np.float32(2.0 ** e)
+    x = x0.copy()
+    x[rows] = synth.f32_to_bf16_bits(xf)
+    logits = hl.logits(x)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    assert np.isfinite(out).all()
+    assert_route_matches(ids, gates, logits, hl.shape.top_k, f"verify T={T}")
+    counts = np.bincount(ids.reshape(-1), minlength=hl.shape.n_experts)
+    small = ((counts >= 1) & (counts <= 4)).sum()
+    # (about 2.7 entries per expert at 128 tokens, 5.9 at 300)
+    assert small >= 0.25 * (counts > 0).sum(), f"groups of 1..4 entries: {small} of {(counts > 0).sum()}"
+    ref, *_ = hl.oracle_forward(x)
+    err = OL.rel_max_err(out[np.setdiff1d(np.arange(T), rows)], ref[np.setdiff1d(np.arange(T), rows)])
+    print(f"verify T={T}: {small} of {(counts > 0).sum()} groups with 1..4 entries; "
+          f"max|err|/rms = {err:.3e} over the other rows")
+    assert err <= OUT_TOL
+    for t in rows:
+        e = OL.rel_max_err(out[t], ref[t])
+        print(f"verify T={T} rescaled row {t}: max|err|/rms = {e:.3e}")
+        assert e <= OUT_TOL
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+    # re-run: the same bits
+    out2, *_ = run_layer(d, x, T)
+    np.testing.assert_array_equal(out2, out)
+
+
 @pytest.mark.parametrize("T", [16, 17, 1023])
 def test_path_boundaries_full_compare(T):
     # The batch sizes at the edges of the paths, on the real 2-bit layer with Zipf

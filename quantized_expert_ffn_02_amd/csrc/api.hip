@@ -105,7 +105,7 @@ Layout make_layout(const moe_layer_t* L, int64_t T) {
   o.xf16 = take(dense ? 0 : T * H * 2);
   o.xexp = take(dense ? 0 : T * 4);   // row exponents of the fp16 copy
   o.hf16 = take(dense ? 0 : n * I * 2);
-  o.tiles = take((n / kSmallTileRows + E + 2) * 3 * 4);   // GEMM tiles (128 or 32 rows)
+  o.tiles = take((n / kSmallTileRows + 2 * E + 3) * 3 * 4);   // GEMM tiles (128, 32 or 1 .. 4 rows)
   o.n_tiles = take(8);                                      // all tiles, fp16 tiles
   o.h = take(n * I * 4);
   o.htab_pairs = take(dense ? 0 : n * (I / 32) * planes * 2 * 16 * 4);
@@ -449,8 +449,12 @@ static int medium_path(const moe_layer_t* L, const moe_bank_t& routed, const int
   MOE_TRY(launch_permute_plan(ids, T, k, E, with_shared, offsets, srt, inv, at<int32_t>(ws, lay.counts),
                               at<int32_t>(ws, lay.base), 1, 1, kSmallTileRows, chunks, n_chunks,
                               at<int32_t>(ws, lay.items), at<int32_t>(ws, lay.n_items), s,
-                              mxt ? kMxTileRows : 0));
-  const int max_chunks = n / kSmallTileRows + std::min(E + 1, n) + 1;
+                              mxt ? kMxGroupRows : 0));
+  // tiles: at most n / 32 + groups, and with fp8 x fp4 tiles one more for each group
+  // of more than kMxTileRows entries (up to kMxGroupRows <= 2 kMxTileRows: two tiles)
+  static_assert(kMxGroupRows <= 2 * kMxTileRows, "at most two fp8 x fp4 tiles per group");
+  const int max_chunks = n / kSmallTileRows + std::min(E + 1, n) +
+                         (mxt && kMxGroupRows > kMxTileRows ? std::min(n / (kMxTileRows + 1), E + 1) : 0) + 1;
   MxTables mxtab;
   mxtab.x_data = at<uint8_t>(ws, lay.xmx_data);
   mxtab.x_exps = at<uint8_t>(ws, lay.xmx_exps);

@@ -201,9 +201,9 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int with_shar
 int permute_chunks(int n_entries);
 // permutation followed by the plan (launch_plan); batches of up to 16,384 entries
 // in one single-block launch
-// mx_rows > 0: every group of 1 .. mx_rows entries becomes one tile of the fp8 x fp4
-// form (rows | kTileMx), listed after all the fp16 tiles; n_tiles[0] counts all
-// tiles, n_tiles[1] the fp16 ones
+// mx_rows > 0: every group of 1 .. mx_rows entries becomes ceil(entries / kMxTileRows)
+// tiles of the fp8 x fp4 form (rows | kTileMx), listed after all the fp16 tiles;
+// n_tiles[0] counts all tiles, n_tiles[1] the fp16 ones
 hipError_t launch_permute_plan(const int32_t* ids, int T, int k, int E, int with_shared, int32_t* offsets,
                                int32_t* sorted_rows, int32_t* row_to_sorted, int32_t* counts, int32_t* base,
                                int min_rows, int items_per, int tile_rows, int32_t* tiles, int32_t* n_tiles,
@@ -249,11 +249,15 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
                           const MxTables* mx = nullptr);
 // rows per tile of the grouped GEMM for batches beyond a decode step and below a prompt chunk
 static constexpr int kSmallTileRows = 32;
-// Tiles of an expert group of at most kMxTileRows entries on the 32-row 2-bit path
-// run on the block-scaled fp8 x fp4 matrix cores (the decode form, one product per
-// row over codes loaded once) instead of dequantising the expert into fp16; the plan
-// marks them with kTileMx in the rows field.  Shapes: mx_tiles_ok.
+// An expert group of at most kMxGroupRows entries on the 32-row 2-bit path runs on
+// the block-scaled fp8 x fp4 matrix cores (the decode form, one product per row over
+// codes loaded once) instead of dequantising the expert into fp16, in tiles of at
+// most kMxTileRows rows; the plan marks them with kTileMx in the rows field.
+// Shapes: mx_tiles_ok.  (Groups of 5 to 8 entries as two such tiles, each reading
+// the expert's codes, were slower than one 32-row fp16 tile: 312 against 279 us for
+// a 300-token verify batch.)
 static constexpr int kMxTileRows = 4;
+static constexpr int kMxGroupRows = 4;
 static constexpr int kTileMx = 1 << 16;
 static constexpr int kMxTileMaxH = 3072;
 bool mx_tiles_ok(int H, int I);

@@ -161,12 +161,13 @@ __device__ __forceinline__ void mx_tile_gateup(const uint8_t* __restrict__ lds, 
   // refilled with chunk c + D, then every row's products
   auto chunk = [&](MxChunk& B, int c) {
     mx_v8i W[2][4];
-    uint32_t sc[4];
+    float sc[2][4];   // the fp16 block scales of this lane's (row, even / odd block)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       W[0][g] = mx_weights(B.c[g].x, B.c[g].y);
       W[1][g] = mx_weights(B.c[g].z, B.c[g].w);
-      sc[g] = B.s[g];
+      sc[0][g] = fp16_to_f32(B.s[g] & 0xFFFFu);
+      sc[1][g] = fp16_to_f32(B.s[g] >> 16);
     }
     load(c + D, B);
 #pragma unroll
@@ -180,7 +181,7 @@ __device__ __forceinline__ void mx_tile_gateup(const uint8_t* __restrict__ lds, 
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const mx_v4f o = mx_mfma(A, W[pi][g], sa, off);
-            y[j][g] = mx_accumulate(o, pi ? sc[g] >> 16 : sc[g] & 0xFFFFu, y[j][g]);
+            y[j][g] = fmaf(sc[pi][g], (o[0] + o[1]) + (o[2] + o[3]), y[j][g]);
           }
         }
       }
@@ -263,8 +264,12 @@ __device__ __forceinline__ void mx_tile_down(const uint8_t* __restrict__ lds, in
   for (int v = 0; v < NV; ++v) {
     const int c = v >> 1, pi = v & 1;   // the tail chunk (v = 2 NS) reads words 0, 1 of its own loads
     mx_v8i W[4];
+    float s[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) W[g] = pi ? mx_weights(cw[c][g].z, cw[c][g].w) : mx_weights(cw[c][g].x, cw[c][g].y);
+    for (int g = 0; g < 4; ++g) {
+      W[g] = pi ? mx_weights(cw[c][g].z, cw[c][g].w) : mx_weights(cw[c][g].x, cw[c][g].y);
+      s[g] = fp16_to_f32(pi ? sc[c][g] >> 16 : sc[c][g] & 0xFFFFu);
+    }
 #pragma unroll
     for (int j = 0; j < kMxTileRows; ++j) {
       if (j < rows) {
@@ -274,7 +279,7 @@ __device__ __forceinline__ void mx_tile_down(const uint8_t* __restrict__ lds, in
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const mx_v4f o = mx_mfma(A, W[g], sa, off);
-          y[j][g] = mx_accumulate(o, pi ? sc[c][g] >> 16 : sc[c][g] & 0xFFFFu, y[j][g]);
+          y[j][g] = fmaf(s[g], (o[0] + o[1]) + (o[2] + o[3]), y[j][g]);
         }
       }
     }

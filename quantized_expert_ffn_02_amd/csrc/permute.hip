@@ -69,24 +69,26 @@ static constexpr int kScanBatch = 16;
 
 struct PlanOut {
   int min_rows = 0, items_per = 1, tile_rows = 1;
-  int mx_rows = 0;   // groups of 1 .. mx_rows entries: one fp8 x fp4 tile each
+  int mx_rows = 0;   // groups of 1 .. mx_rows entries: fp8 x fp4 tiles of at most kMxTileRows rows
   int32_t *tiles = nullptr, *n_tiles = nullptr, *items = nullptr, *n_items = nullptr;
 };
 
 // Plan of the groups (as k_plan computes it) from thread g's group start and
-// count; every thread of the block calls it.  The fp8 x fp4 tiles of small
-// groups (rows | kTileMx) follow all the fp16 tiles, so the longer fp16 tiles
-// are dispatched first; n_tiles[1] counts the fp16 tiles.
+// count; every thread of the block calls it.  A small group is cut into
+// ceil(cnt / kMxTileRows) fp8 x fp4 tiles of (nearly) equal rows (rows |
+// kTileMx), which follow all the fp16 tiles, so the longer fp16 tiles are
+// dispatched first; n_tiles[1] counts the fp16 tiles.
 __device__ void plan_groups(const PlanOut& P, int g, int start, int cnt) {
   const bool big = cnt >= P.min_rows;
   const bool mx = big && cnt > 0 && cnt <= P.mx_rows;
+  const int nmx = mx ? (cnt + kMxTileRows - 1) / kMxTileRows : 0;
   const int nt = big && !mx ? (cnt + P.tile_rows - 1) / P.tile_rows : 0;
   const int ni = big ? 0 : (cnt + P.items_per - 1) / P.items_per;
   // with fp8 x fp4 tiles (batches below a prompt chunk: fewer than 2^20 fp16 tiles,
-  // at most 1,024 groups) one scan counts both kinds: fp16 tiles in the low 20
-  // bits, fp8 x fp4 tiles above them
+  // fewer than 2^11 fp8 x fp4 tiles) one scan counts both kinds: fp16 tiles in the
+  // low 20 bits, fp8 x fp4 tiles above them
   int tot_tm = 0, tot_i = 0;
-  const int ptm = P.mx_rows > 0 ? block_exclusive_scan_1024(nt | (mx ? 1 << 20 : 0), &tot_tm)
+  const int ptm = P.mx_rows > 0 ? block_exclusive_scan_1024(nt | (nmx << 20), &tot_tm)
                                 : block_exclusive_scan_1024(nt, &tot_tm);
   const int pi = block_exclusive_scan_1024(ni, &tot_i);
   const int low = P.mx_rows > 0 ? (1 << 20) - 1 : -1;
@@ -97,10 +99,11 @@ __device__ void plan_groups(const PlanOut& P, int g, int start, int cnt) {
     P.tiles[3 * (pt + i) + 1] = start + i * P.tile_rows;
     P.tiles[3 * (pt + i) + 2] = min(P.tile_rows, cnt - i * P.tile_rows);
   }
-  if (mx) {
-    P.tiles[3 * (tot_t + pm)] = g;
-    P.tiles[3 * (tot_t + pm) + 1] = start;
-    P.tiles[3 * (tot_t + pm) + 2] = cnt | kTileMx;
+  for (int i = 0; i < nmx; ++i) {
+    const int r0 = i * cnt / nmx, r1 = (i + 1) * cnt / nmx;
+    P.tiles[3 * (tot_t + pm + i)] = g;
+    P.tiles[3 * (tot_t + pm + i) + 1] = start + r0;
+    P.tiles[3 * (tot_t + pm + i) + 2] = (r1 - r0) | kTileMx;
   }
   for (int i = 0; i < ni; ++i) {
     P.items[3 * (pi + i)] = g;

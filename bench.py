@@ -36,8 +36,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # Reported only while the kernel's sources are the ones that were counted.
 GATEUP_TRAFFIC = {
     "sources": ["decode_mx.hip", "mx.h", "mfma.h", "device.h", "topk.h"],
-    "sha256": "6756d5983efc038c2726fa544dc3e568c329e4791b31abadaf96f4357822178a",
-    "fetch_kib": 22239.0, "fetch_scale": 262144.0 / 131084.5,
+    "sha256": "d38f707b77f3d03ffdf50589e8c9dcbbd9c2ac127d3355c6860e13a15c3ab421",
+    "fetch_kib": 22235.5, "fetch_scale": 262144.0 / 131084.5,
     "write_kib": 118.8, "write_scale": 1.0,
     "tokens": 4,
 }
@@ -622,6 +622,7 @@ def main():
     ap.add_argument("--coder-steps", type=int, default=2000)
     ap.add_argument("--no-coder", action="store_true")
     ap.add_argument("--no-adaptive", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run 10 plain device copies of BYTES bytes (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -719,15 +720,32 @@ def main():
     step_bytes1 = E * H * 2 + (float(uniq1.mean()) + 1) * eb + H * 2 + H * 4
     # an MTP verify batch of 32 sequences x (1 + 3 drafts): 128 independent tokens on the
     # same layers (the 32-row grouped GEMM path)
-    TV, sv = 128, max(args.steps // 10, 1)
-    msv, _, uniqv = run(TV, sv, max(args.warmup // 10, 5), False)
-    msv_step = msv / sv
-    dv = float(uniqv.mean())
-    bytes_v = E * H * 2 + (dv + 1) * eb + TV * H * 2 + TV * H * 4
-    flops_v = 2.0 * TV * H * E + TV * (k + 1) * 6.0 * H * I
-    gbps_v = bytes_v / (msv_step * 1e-3) / 1e9
-    tflops_v = flops_v / (msv_step * 1e-3) / 1e12
-    hbm_bound_v = flops_v / bytes_v < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    verify = None
+    if not args.no_verify:
+        TV, sv = 128, max(args.steps // 10, 1)
+        msv, _, uniqv = run(TV, sv, max(args.warmup // 10, 5), False)
+        msv_step = msv / sv
+        dv = float(uniqv.mean())
+        bytes_v = E * H * 2 + (dv + 1) * eb + TV * H * 2 + TV * H * 4
+        flops_v = 2.0 * TV * H * E + TV * (k + 1) * 6.0 * H * I
+        gbps_v = bytes_v / (msv_step * 1e-3) / 1e9
+        tflops_v = flops_v / (msv_step * 1e-3) / 1e12
+        hbm_bound_v = flops_v / bytes_v < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+        verify = {
+            "workload": f"verify: one real-shape 2-bit layer, T={TV} independent tokens (32 sequences x (1 + 3 MTP "
+                        f"drafts)), the decode layers and router, {R} distinct layers rotated",
+            "layer_us": msv_step * 1e3,
+            "tokens_per_s": TV / (msv_step * 1e-3),
+            "unique_experts_per_step": dv,
+            "algorithmic_MB_per_step": bytes_v / 1e6,
+            "GBps": gbps_v,
+            "hbm_frac": gbps_v / HBM_PEAK_GBS,
+            "algorithmic_GFLOP_per_step": flops_v / 1e9,
+            "TFLOPs": tflops_v,
+            "mfma_frac_of_fp16_peak": tflops_v / MFMA_BF16_PEAK_TFLOPS,
+            "bound": "hbm" if hbm_bound_v else "mfma",
+            "roofline_frac": gbps_v / HBM_PEAK_GBS if hbm_bound_v else tflops_v / MFMA_BF16_PEAK_TFLOPS,
+        }
 
     result = {
         "metric": "MoE-layer tokens/s at 1 MI355X; decode HBM GB/s and prefill MFMA % of peak",
@@ -764,21 +782,6 @@ def main():
             "T1": {"tokens_per_s": 1 / (ms1_step * 1e-3), "layer_us": ms1_step * 1e3,
                    "layer_GBps": step_bytes1 / (ms1_step * 1e-3) / 1e9},
         },
-        "verify": {
-            "workload": f"verify: one real-shape 2-bit layer, T={TV} independent tokens (32 sequences x (1 + 3 MTP "
-                        f"drafts)), the decode layers and router, {R} distinct layers rotated",
-            "layer_us": msv_step * 1e3,
-            "tokens_per_s": TV / (msv_step * 1e-3),
-            "unique_experts_per_step": dv,
-            "algorithmic_MB_per_step": bytes_v / 1e6,
-            "GBps": gbps_v,
-            "hbm_frac": gbps_v / HBM_PEAK_GBS,
-            "algorithmic_GFLOP_per_step": flops_v / 1e9,
-            "TFLOPs": tflops_v,
-            "mfma_frac_of_fp16_peak": tflops_v / MFMA_BF16_PEAK_TFLOPS,
-            "bound": "hbm" if hbm_bound_v else "mfma",
-            "roofline_frac": gbps_v / HBM_PEAK_GBS if hbm_bound_v else tflops_v / MFMA_BF16_PEAK_TFLOPS,
-        },
         "roofline": {
             "kernel": "k_decode_gateup_mx (top-k, gate/up + SwiGLU on the fp8 x fp4 matrix cores, down-table epilogue)",
             "bound": "hbm",
@@ -792,6 +795,8 @@ def main():
             "avg_launch_us": gu_ms * 1e3,
         },
     }
+    if verify is not None:
+        result["verify"] = verify
     del layers, pool
     torch.cuda.empty_cache()
     if not args.no_prefill:

@@ -291,6 +291,44 @@ def test_cache_adapts(fmt):
     assert hits[0] == 0 and hits[-1] > hits[0]
 
 
+def test_cached_q2_pool_fp8_tiles():
+    # A real-shape 2-bit layer (uniform router) in expert-cache mode with a 48-slot pool
+    # holding experts 0..47: at 64 tokens its hit groups have one to four entries, so they
+    # run as fp8 x fp4 tiles under the slot map, and the missed groups' tiles write
+    # nothing but zero rows.  Route, miss list and output against the oracle's cached layer.
+    hl = W.host_layer("decode")
+    s = hl.shape
+    H, I, E, k, T, n_slots = s.hidden, s.inter, s.n_experts, s.top_k, 64, 48
+    per = {n: len(v) // E for n, v in hl.routed.items()}
+    dpool = DeviceBank(s.fmt, n_slots, H, I, {n: np.ascontiguousarray(v[:per[n] * n_slots]) for n, v in hl.routed.items()})
+    dl = DeviceLayer(H, E, k, I, hl.wr, hl.bias, dpool, DeviceBank(s.fmt, 1, H, I, hl.shared))
+    slot_row = np.full(E, -1, dtype=np.int32)
+    slot_row[:n_slots] = np.arange(n_slots, dtype=np.int32)
+    x, _ = W.activations_with_margin(hl, T)
+    ws = dl.workspace(T)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    miss = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    n_miss = torch.zeros(1, dtype=torch.int32, device="cuda")
+    B.layer_forward_cached(dl.struct, 0, 1, to_device(slot_row[None, :]), dpool.struct, to_device(x), T, out, ids,
+                           gates, miss, n_miss, ws)
+    torch.cuda.synchronize()
+    smat = OF.expert_matrices(s.fmt, hl.shared, H, I)
+    slot_fn = lambda sl: OF.expert_matrices(s.fmt, hl.routed, H, I, sl)   # slot sl holds expert sl
+    ref, ids_r, gates_r, misses_r, _ = OL.cached_layer_forward(x, hl.wr, k, slot_row, slot_fn, lambda: smat,
+                                                                bias=hl.bias)
+    assert_route_matches(host(ids), host(gates), hl.logits(x), k, "cached q2 pool")
+    counts = np.bincount(host(ids).reshape(-1), minlength=E)[:n_slots]
+    assert ((counts >= 1) & (counts <= 4)).sum() >= 20, counts
+    nm = int(host(n_miss)[0])
+    assert nm == len(misses_r) and nm < T * k
+    np.testing.assert_array_equal(host(miss)[:nm], misses_r)
+    err = OL.rel_max_err(host(out), ref)
+    print(f"cached q2 pool: hits {T * k - nm}/{T * k} in {(counts > 0).sum()} groups, max|err|/rms = {err:.3e}")
+    assert err <= OUT_TOL
+
+
 @pytest.mark.parametrize("T", [8, 32])
 def test_tiered_layer_q2_small(T):
     # 2-bit weights end to end through the tiered layer: a small layer (H = 512, I = 256,

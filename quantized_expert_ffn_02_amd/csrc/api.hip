@@ -508,7 +508,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
                               float* out, uint16_t* out_bf16, int32_t* topk_ids, float* topk_gates, float* margin,
                               void* ws, const Layout& lay, hipStream_t s, const float* norm_sq_in = nullptr,
                               float* norm_sq_out = nullptr, bool x_f16_ready = false,
-                              const NormNext* norm_next = nullptr) {
+                              const NormNext* norm_next = nullptr, const Prefetch* prefetch = nullptr) {
   if (norm_next && !medium_path_taken(L, T)) return MOE_EINVAL;   // only the 32-row GEMM path's combine writes it
   const int k = L->top_k, E = L->n_experts;
   int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, lay.ids);
@@ -571,7 +571,7 @@ static int layer_forward_impl(const moe_layer_t* L, const uint16_t* x, int32_t T
       if (decode_down_combine_mx_ok(L->inter, k, with_shared)) {
         // down projection and combine in one launch (a block per token and 64 rows)
         MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s,
-                      [&] { return launch_decode_down_combine_mx(m, residual, out, out_bf16, norm_sq_out, s); }));
+                      [&] { return launch_decode_down_combine_mx(m, residual, out, out_bf16, norm_sq_out, s, prefetch); }));
         return MOE_OK;
       }
       MOE_TRY(timed(MOE_KERNEL_DOWN_GEMV, s, [&] { return launch_decode_down_mx(m, s); }));
@@ -796,8 +796,27 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
       nn.eps = MOE_RMS_EPS;
       next = &nn;
     }
+    // on the fused-norm decode path the layer's last launch also reads the next
+    // layer's router rows and shared expert into the memory-side cache
+    Prefetch pf;
+    if (fused && l + 1 < n_layers) {
+      const moe_layer_t& Ln = layers[l + 1];
+      pf.ptr[0] = Ln.w_router;
+      pf.bytes[0] = (uint32_t)((size_t)Ln.n_experts * Ln.hidden * 2);
+      if (has_shared(&Ln)) {
+        const MatRef s13 = mat_w13(Ln.shared), s2 = mat_w2(Ln.shared);
+        pf.ptr[1] = s13.codes;
+        pf.bytes[1] = (uint32_t)s13.code_stride;
+        pf.ptr[2] = s13.scales;
+        pf.bytes[2] = (uint32_t)(s13.scale_stride * 2);
+        pf.ptr[3] = s2.codes;
+        pf.bytes[3] = (uint32_t)s2.code_stride;
+        pf.ptr[4] = s2.scales;
+        pf.bytes[4] = (uint32_t)(s2.scale_stride * 2);
+      }
+    }
     rc = layer_forward_impl(&layers[l], lin, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s,
-                            norm_in ? sq : nullptr, norm_out ? sq : nullptr, f16, next);
+                            norm_in ? sq : nullptr, norm_out ? sq : nullptr, f16, next, pf.max_bytes() ? &pf : nullptr);
     if (rc) return rc;
     norm_done = next != nullptr;
     have_sq = norm_out;

@@ -19,6 +19,8 @@
 // The combine is k_decode_combine (decode_ffn.hip).
 #include <math.h>
 
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 #include "mfma.h"
@@ -291,6 +293,30 @@ __global__ __launch_bounds__((NS + TAIL) * 64) void k_decode_down_mx(MxFfnArgs a
   }
 }
 
+// The prefetch role of a block: block b of n reads its share of the ranges in
+// 16-byte pieces, consecutive lanes at consecutive addresses (a wave instruction
+// covers 1 KB), every load of the thread issued before the first is used (offsets
+// past a range read nothing: buffer loads); the loaded words only feed an empty
+// asm statement, so the loads stay.
+__device__ __forceinline__ void prefetch_lines(const Prefetch& pf, int b, int n) {
+  const uint32_t step = (uint32_t)n * blockDim.x * 16u;
+  const uint32_t base = ((uint32_t)b * blockDim.x + threadIdx.x) * 16u;
+  u32x4 w[Prefetch::kMax][Prefetch::kPerThread];
+#pragma unroll
+  for (int r = 0; r < Prefetch::kMax; ++r) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(pf.ptr[r], pf.bytes[r]);
+#pragma unroll
+    for (int i = 0; i < Prefetch::kPerThread; ++i)
+      w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + i * step, 0, 0);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int r = 0; r < Prefetch::kMax; ++r)
+#pragma unroll
+    for (int i = 0; i < Prefetch::kPerThread; ++i) acc ^= w[r][i].x ^ w[r][i].y ^ w[r][i].z ^ w[r][i].w;
+  asm volatile("" : : "v"(acc));
+}
+
 // Down projection and combine of token t and RB (64 or 32) output rows: wave
 // i < k takes routed entry t k + i, wave k the shared expert, each over all
 // K = I columns (256-column chunks, then the 128-column tail, in order); waves
@@ -303,11 +329,16 @@ template <int W, int NS, int TAIL, int RB>
 __global__ __launch_bounds__(W * 64) void k_decode_down_combine_mx(MxFfnArgs a, const uint16_t* __restrict__ residual,
                                                                   float* __restrict__ out,
                                                                   uint16_t* __restrict__ out_bf16,
-                                                                  float* __restrict__ sq_out) {
+                                                                  float* __restrict__ sq_out, Prefetch pf) {
   constexpr int NV = 2 * NS + TAIL;   // activation chunks of K
   constexpr int S = RB / 16;          // 16-row MFMA groups of the block
   static_assert(RB == 64 || RB == 32, "64- or 32-row blocks");
   __shared__ __attribute__((aligned(16))) float red[W][S][64];
+  const int nrg = a.H / RB;   // the launch's own rows of blocks; the ones after them prefetch
+  if ((int)blockIdx.y >= nrg) {
+    prefetch_lines(pf, (blockIdx.y - nrg) * gridDim.x + blockIdx.x, (gridDim.y - nrg) * gridDim.x);
+    return;
+  }
   const int tok = blockIdx.x, rg = blockIdx.y;
   // 64-row weight tile of the block, and the block's first row inside it
   const int tile = RB == 64 ? rg : rg >> 1, r0 = RB == 64 ? 0 : (rg & 1) * 32;
@@ -436,22 +467,28 @@ hipError_t launch_decode_gateup_mx(const MxFfnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
-                                         float* sq_out, hipStream_t s) {
+                                         float* sq_out, hipStream_t s, const Prefetch* pf) {
   const int n_ent = a.k + (a.with_shared ? 1 : 0);
   // 32-row blocks when 64-row ones would be very few (one token: 40 blocks at
   // H = 2560; measured 18.1 against 19.5 us a layer, while at four tokens 320
   // 32-row blocks were slower than 160 64-row ones)
   const bool rows32 = a.T * (a.H / 64) <= 64;
-  dim3 grid(a.T, a.H / (rows32 ? 32 : 64));
+  const Prefetch p = pf ? *pf : Prefetch();
+  // prefetch rows: about 160 blocks (on the compute units the launch's own blocks
+  // leave free), enough for kPerThread 16-byte pieces per thread of the largest range
+  const int waves = n_ent <= 11 ? 11 : 16;
+  const uint32_t pieces = (p.max_bytes() + 15) / 16, per_row = (uint32_t)a.T * waves * 64 * Prefetch::kPerThread;
+  const int prow = p.max_bytes() ? std::max((int)((pieces + per_row - 1) / per_row), (160 + a.T - 1) / a.T) : 0;
+  dim3 grid(a.T, a.H / (rows32 ? 32 : 64) + prow);
   if (!decode_down_combine_mx_ok(a.I, a.k, a.with_shared)) return hipErrorInvalidValue;
 #define MOE_DC_MX(W, NS, TL)                                                                                  \
   do {                                                                                                        \
     if (rows32)                                                                                               \
       MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL, 32>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16, \
-                 sq_out);                                                                                     \
+                 sq_out, p);                                                                                  \
     else                                                                                                      \
       MOE_LAUNCH((k_decode_down_combine_mx<W, NS, TL, 64>), grid, dim3(W * 64), 0, s, a, residual, out, out_bf16, \
-                 sq_out);                                                                                     \
+                 sq_out, p);                                                                                  \
   } while (0)
   const bool small = n_ent <= 11;
   switch (a.I) {

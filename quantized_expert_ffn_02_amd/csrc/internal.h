@@ -157,10 +157,25 @@ hipError_t launch_decode_down_mx(const MxFfnArgs& a, hipStream_t s);
 // down projection and combine in one launch: a block per token and 64 output
 // rows, a wave per entry (I in {512, 640, 768}, k + 1 <= 16 entries per token)
 bool decode_down_combine_mx_ok(int I, int k, int with_shared);
+// Byte ranges that a launch reads into the memory-side cache for a later launch (the
+// next layer's weights that do not depend on its input: router rows, shared expert),
+// in blocks after the launch's own.
+struct Prefetch {
+  static constexpr int kMax = 5;
+  static constexpr int kPerThread = 2;   // 16-byte pieces per thread and range, all loads issued at once
+  const void* ptr[kMax] = {};
+  uint32_t bytes[kMax] = {};             // 0: unused range
+  uint32_t max_bytes() const {
+    uint32_t m = 0;
+    for (int i = 0; i < kMax; ++i) m = bytes[i] > m ? bytes[i] : m;
+    return m;
+  }
+};
 // sq_out (may be NULL): partial sums of squares of the bf16 output per token and
-// 64 rows ([T][H / 64]), the next layer's RMSNorm input
+// 64 rows ([T][H / 64]), the next layer's RMSNorm input; pf (may be NULL): ranges
+// read by extra rows of blocks of the same launch, dispatched after its own
 hipError_t launch_decode_down_combine_mx(const MxFfnArgs& a, const uint16_t* residual, float* out, uint16_t* out_bf16,
-                                         float* sq_out, hipStream_t s);
+                                         float* sq_out, hipStream_t s, const Prefetch* pf = nullptr);
 hipError_t launch_decode_gateup(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeFfnArgs& a, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeFfnArgs& a, hipStream_t s);

@@ -41,6 +41,7 @@ __host__ __device__ constexpr int mx_stage_bytes(int K) {
 template <int MAXK>
 __device__ __forceinline__ void mx_stage(uint8_t* __restrict__ lds, const uint8_t* __restrict__ data,
                                          const uint8_t* __restrict__ exps, int K, int rows, const int (&src)[kMxTileRows]) {
+  static_assert(kMxTileRows == 4, "the source row is picked from four");
   constexpr int IT = (mx_stage_bytes(MAXK) / 16 + 255) / 256;
   const int db = (int)mx_data_bytes(K), eb = (int)mx_exps_bytes(K);
   const int per = (db + eb) / 16;

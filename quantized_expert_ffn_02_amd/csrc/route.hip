@@ -20,8 +20,9 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // parts > 1: the logits are `parts` partial planes of [T][E] plus bias (the
 // K-split router of router_split.hip), added here in plane order.
-// With f16.x set, the token's wave also writes the grouped GEMMs' activation
-// copy of its row (wave_row_to_f16), which then needs no launch of its own.
+// With f16.x set, blocks of the same launch write the grouped GEMMs' activation
+// copy of the rows (wave_row_to_f16, one wave per token, beside the token's
+// selection), which then needs no launch of its own.
 struct RowF16 {
   const uint16_t* x = nullptr;   // bf16 [T][H]
   int H = 0;                     // H % 16 == 0, H <= kRowF16MaxH
@@ -93,14 +94,19 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
                                               int32_t* __restrict__ ids, float* __restrict__ gates,
                                               float* __restrict__ margin, int parts, const float* __restrict__ bias,
                                               RowF16 f16, MxTab tab) {
-  const int kb = (T + 3) / 4;   // top-k blocks
-  if ((int)blockIdx.x >= kb) {
-    mx_table_pass(tab.x, T, tab.H, tab.data, tab.exps, (int)blockIdx.x - kb, (int)gridDim.x - kb);
+  const int kb = (T + 3) / 4;                       // top-k blocks, then as many conversion blocks
+  const int cb = f16.x ? 2 * kb : kb;
+  const int b = blockIdx.x;
+  if (b >= cb) {
+    mx_table_pass(tab.x, T, tab.H, tab.data, tab.exps, b - cb, (int)gridDim.x - cb);
     return;
   }
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = (b < kb ? b : b - kb) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  if (f16.x) wave_row_to_f16(f16.x + (size_t)t * f16.H, f16.H, f16.out + (size_t)t * f16.H, f16.xexp + t);
+  if (b >= kb) {
+    wave_row_to_f16(f16.x + (size_t)t * f16.H, f16.H, f16.out + (size_t)t * f16.H, f16.xexp + t);
+    return;
+  }
   wave_topk_row<VPL, PARTS>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, gates + (size_t)t * k,
                             margin ? margin + t : nullptr, nullptr, parts, (size_t)T * E, bias);
 }
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 template <bool PARTS>
 static hipError_t launch_topk_t(const float* logits, int T, int E, int k, int32_t* ids, float* gates, float* margin,
                                 int parts, const float* bias, const RowF16& f, const MxTab& mt, hipStream_t s) {
-  dim3 grid((T + 3) / 4 + (mt.data ? mx_table_blocks(T, mt.H, 512) : 0));
+  dim3 grid((T + 3) / 4 * (f.x ? 2 : 1) + (mt.data ? mx_table_blocks(T, mt.H, 512) : 0));
   if (E <= 64)
     MOE_LAUNCH((k_topk<1, PARTS>), grid, dim3(256), 0, s, logits, T, E, k, ids, gates, margin, parts, bias, f, mt);
   else if (E <= 128)

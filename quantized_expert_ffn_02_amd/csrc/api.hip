@@ -815,7 +815,9 @@ int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_
         pf.bytes[4] = (uint32_t)(s2.scale_stride * 2);
       }
     }
-    rc = layer_forward_impl(&layers[l], lin, T, cur, of, nxt, nullptr, nullptr, nullptr, ws, lay, s,
+    // a layer whose combine writes the next layer's normalised input leaves no fp32
+    // output (only the last layer's is returned)
+    rc = layer_forward_impl(&layers[l], lin, T, cur, next ? nullptr : of, nxt, nullptr, nullptr, nullptr, ws, lay, s,
                             norm_in ? sq : nullptr, norm_out ? sq : nullptr, f16, next, pf.max_bytes() ? &pf : nullptr);
     if (rc) return rc;
     norm_done = next != nullptr;

@@ -90,7 +90,8 @@ __device__ void plan_groups(const PlanOut& P, int g, int start, int cnt) {
   int tot_tm = 0, tot_i = 0;
   const int ptm = P.mx_rows > 0 ? block_exclusive_scan_1024(nt | (nmx << 20), &tot_tm)
                                 : block_exclusive_scan_1024(nt, &tot_tm);
-  const int pi = block_exclusive_scan_1024(ni, &tot_i);
+  // with min_rows <= 1 every non-empty group takes tiles: no work items, no scan for them
+  const int pi = P.min_rows > 1 ? block_exclusive_scan_1024(ni, &tot_i) : 0;
   const int low = P.mx_rows > 0 ? (1 << 20) - 1 : -1;
   const int pt = ptm & low, pm = P.mx_rows > 0 ? ptm >> 20 : 0;
   const int tot_t = tot_tm & low, tot_m = P.mx_rows > 0 ? tot_tm >> 20 : 0;

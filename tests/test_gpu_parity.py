@@ -7,6 +7,8 @@ Bars (written per check):
   * gates: |gpu - oracle| <= 1e-5 (fp32 softmax over fp32 logits);
   * layer output: max |gpu - oracle| / rms(oracle) <= 1e-2 (fp32 output).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -225,6 +227,57 @@ def test_coder_shape(T):
     err = OL.rel_max_err(out, ref)
     print(f"coder T={T}: max|err|/rms = {err:.3e}")
     assert err <= (1e-4 if T <= 16 else 1e-2)
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
+def degenerate_host_layer(shape):
+    """Host layer of a degenerate shape; the real shape without a shared expert
+    reuses the decode layer's routed experts (same seed and layer)."""
+    if shape not in _LAYERS:
+        base = shared_host_layer("decode")
+        if dataclasses.replace(shape, shared=True) == base.shape:
+            _LAYERS[shape] = dataclasses.replace(base, shape=shape, shared=None,
+                                                 _fn={k: v for k, v in base._fn.items() if k == "e"})
+        else:
+            _LAYERS[shape] = W.host_layer("decode", shape=shape)
+    return _LAYERS[shape]
+
+
+@pytest.mark.parametrize("shape,T", [
+    # every expert selected (k = E): the gates are the softmax over all logits
+    # and the margin below the last selected logit is +inf
+    (synth.LayerShape(512, 8, 8, 256, True, "q2", None), 1),
+    (synth.LayerShape(512, 8, 8, 256, True, "q2", None), 4),
+    (synth.LayerShape(512, 8, 8, 256, True, "q2", None), 17),
+    (synth.LayerShape(512, 8, 8, 256, True, "q2", None), 64),
+    # one expert, no shared expert: every gate is 1 and each row is that
+    # expert's FFN
+    (synth.LayerShape(512, 1, 1, 256, False, "q2", None), 1),
+    (synth.LayerShape(512, 1, 1, 256, False, "q2", None), 64),
+    # the real layer shape without a shared expert: the decode kernels and the
+    # grouped GEMMs' fp8 x fp4 tiles with no shared entry
+    (synth.LayerShape(2560, 512, 10, 640, False, "q2", None), 1),
+    (synth.LayerShape(2560, 512, 10, 640, False, "q2", None), 4),
+    (synth.LayerShape(2560, 512, 10, 640, False, "q2", None), 64),
+], ids=lambda v: f"T{v}" if isinstance(v, int) else f"E{v.n_experts}k{v.top_k}{'s' if v.shared else ''}")
+def test_degenerate_layers(shape, T):
+    hl = degenerate_host_layer(shape)
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+    tag = f"E={shape.n_experts} k={shape.top_k} shared={shape.shared} T={T}"
+    assert_route_matches(ids, gates, hl.logits(x), shape.top_k, tag)
+    if shape.top_k == shape.n_experts:
+        assert np.all(np.isposinf(margin)), tag
+        np.testing.assert_allclose(gates.sum(axis=1), 1.0, rtol=0, atol=1e-5)
+    else:
+        np.testing.assert_allclose(margin, m_r, rtol=0, atol=1e-5)
+    if shape.n_experts == 1:
+        assert np.all(ids == 0) and np.all(gates == 1.0), tag
+    err = OL.rel_max_err(out, ref)
+    print(f"{tag}: max|err|/rms = {err:.3e}")
+    assert err <= (1e-4 if T <= 16 else OUT_TOL)
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
 
 

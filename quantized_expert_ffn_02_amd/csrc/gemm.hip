@@ -993,6 +993,14 @@ __global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restri
       __syncthreads();
     }
   }
+  // The bias is added before any store, and the stores take no branch (an
+  // element outside [T) x [E) gets an offset past the buffer's end, which the
+  // store drops): a store behind a branch that needs a bias load made the
+  // compiler wait for every store in flight before it.
+  float bv[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) bv[ni] = bias ? bias[min(n0 + b0 + 32 * ni + r32, E - 1)] : 0.0f;
+  const __amdgpu_buffer_rsrc_t lr = buffer_rsrc(logits, (uint32_t)T * (uint32_t)E * 4u);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -1001,13 +1009,16 @@ __global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restri
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + a0 + 32 * mi + acc_row(r, lane);
         const int col = n0 + b0 + 32 * ni + r32;
-        if (row < T && col < E) logits[(size_t)row * E + col] = acc[mi][ni][r] + (bias ? bias[col] : 0.0f);
+        const uint32_t off = row < T && col < E ? ((uint32_t)row * (uint32_t)E + (uint32_t)col) * 4u : 0xFFFFFFF0u;
+        const float v = acc[mi][ni][r] + bv[ni];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), lr, off, 0, 0);
       }
 }
 
 hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, const float* bias, int E, int H,
                               float* logits, hipStream_t s) {
-  if ((uint64_t)T * H * 2 > 0x7FFFFFFFu || (uint64_t)E * H * 2 > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  if ((uint64_t)T * H * 2 > 0x7FFFFFFFu || (uint64_t)E * H * 2 > 0x7FFFFFFFu || (uint64_t)T * E * 4 > 0x7FFFFFFFu)
+    return hipErrorInvalidValue;
   const int tiles = ((T + BM - 1) / BM) * ((E + BN - 1) / BN);
   MOE_LAUNCH(k_router_mfma, dim3(tiles), dim3(256), 0, s, x, T, wr, bias, E, H, logits);
   return hipGetLastError();

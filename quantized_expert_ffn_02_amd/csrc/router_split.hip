@@ -72,16 +72,27 @@ __global__ __launch_bounds__(256) void k_router_split(RouterArgs a, int reps) {
   }
   __syncthreads();
   // 2 x 16 x 64 outputs over 256 threads: 8 each, summed over the waves in order
+  // The bias (KS = 1) is loaded before any store, and the stores take no
+  // branch (an element outside the chunk's rows or past E gets an offset past
+  // the plane's end, which the store drops): a store behind a branch that needs
+  // a bias load made the compiler wait for every store in flight before it.
   const size_t plane = (size_t)a.T * a.E;
   float* __restrict__ dst = a.out + (a.KS > 1 ? (size_t)ks * plane : 0);
+  const __amdgpu_buffer_rsrc_t dr = buffer_rsrc(dst, (uint32_t)plane * 4u);
+  float bv[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+    bv[f] = a.KS == 1 && a.bias ? a.bias[min(64 * j + 32 * f + (lane & 31), a.E - 1)] : 0.0f;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int o = q * 256 + (int)threadIdx.x;   // o = f * 1024 + r * 64 + l
+    const int o = q * 256 + (int)threadIdx.x;   // o = f * 1024 + r * 64 + l, l = lane
     const int f = o >> 10, r = (o >> 6) & 15, l = o & 63;
     const float sum = ((red[0][f][r][l] + red[1][f][r][l]) + red[2][f][r][l]) + red[3][f][r][l];
     const int row = acc_row(r, l), col = 64 * j + 32 * f + (l & 31);
-    if (row < rows && col < a.E)
-      dst[(size_t)(m0 + row) * a.E + col] = a.KS > 1 ? sum : sum + (a.bias ? a.bias[col] : 0.0f);
+    const uint32_t off =
+        row < rows && col < a.E ? ((uint32_t)(m0 + row) * (uint32_t)a.E + (uint32_t)col) * 4u : 0xFFFFFFF0u;
+    const float v = a.KS > 1 ? sum : sum + bv[f];
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), dr, off, 0, 0);
   }
 }
 

@@ -87,9 +87,13 @@ def assert_route_matches(ids_g, gates_g, logits_ref, k, tag=""):
 
 # ------------------------------------------------------------------ route
 
-@pytest.mark.parametrize("T", [1, 4, 64, 1000])
-def test_route_decode_shape(T):
-    hl = W.host_layer("decode")
+@pytest.mark.parametrize("workload,T", [("decode", 1), ("decode", 4), ("decode", 64), ("decode", 1000),
+                                        ("decode", 1024), ("decode", 1500), ("tiny", 1100), ("coder", 2100)])
+def test_route_decode_shape(workload, T):
+    # T >= 1,024 runs the 128 x 128-tile MFMA router: 1,500 and 2,100 tokens end
+    # in a partial token tile, and the 16-expert layer fills 16 of a tile's 128
+    # expert columns
+    hl = shared_host_layer(workload)
     x, _ = W.activations_with_margin(hl, T)
     d = W.upload(hl)
     k, E = hl.shape.top_k, hl.shape.n_experts

@@ -878,28 +878,40 @@ hipError_t launch_gemm_q2(GemvKind kind, const MatRef& routed, const MatRef& sha
 // Both operands are bf16 in natural column order; products are exact in fp32.
 //
 // A prompt chunk has few tiles (8,192 tokens x 512 experts is one tile per
-// compute unit), so a block cannot count on a second block to hide memory
-// latency: it runs alone (launch bound 1) and keeps RDEPTH K-steps of both
-// operands in flight in registers.  Step m: write step m + 1 (loaded RDEPTH - 1
-// steps earlier) into the other LDS buffer, issue the loads of step m + RDEPTH
-// into the register set just freed, then 4 x 4 MFMAs per wave from LDS.  The
+// compute unit), so one block per compute unit must hide its own latencies.
+// The block has 8 waves, two per SIMD: waves 0-3 take the first half of K and
+// waves 4-7 the second (H is a multiple of 128, so each half is a whole number
+// of 64-column steps), each half with its own two LDS buffers of the A and B
+// tiles, so that one half's LDS traffic and barriers overlap the other's MFMAs.
+// At the end the second half's accumulators go through LDS and the first half
+// adds them (first half + second half) and stores.  Each wave computes 64
+// tokens x 64 experts.
+// A half keeps RDEPTH K-steps of both operands in flight in registers.  Step m:
+// write step m + 1 (loaded RDEPTH - 1 steps earlier) into the other LDS buffer,
+// issue the loads of step m + RDEPTH into the register set just freed, then
+// 4 x 4 MFMAs per wave from LDS (fragments read one 16-K sub-step ahead).  The
 // loop is unrolled by RDEPTH so that every register set has a static name.
 // Tile (m, n) is block n + 4 m of a linear order whose neighbours share one
 // XCD, so the expert tiles of a token tile read its rows from one L2.
 // ---------------------------------------------------------------------------
-static constexpr int RDEPTH = 6;
+static constexpr int RDEPTH = 4;
 
 __device__ __forceinline__ b8_t lds_frag_b(const uint16_t* base, int row, int k) {
   return *reinterpret_cast<const b8_t*>(base + row * LDS_STRIDE + k);
 }
 
-__global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restrict__ x, int T,
-                                                        const uint16_t* __restrict__ wr,
-                                                        const float* __restrict__ bias, int E, int H,
-                                                        float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
+static constexpr int KH = 2;   // K halves
+
+__global__ __launch_bounds__(256 * KH, 1) void k_router_mfma(const uint16_t* __restrict__ x, int T,
+                                                             const uint16_t* __restrict__ wr,
+                                                             const float* __restrict__ bias, int E, int H,
+                                                             float* __restrict__ logits) {
+  constexpr int TILE = BM * LDS_STRIDE;   // halves per LDS tile buffer
+  // [half][buffer] A tiles, then [half][buffer] B tiles; the second half's
+  // accumulators reuse the space at the end (4 x 2 x 2 x 16 x 64 floats)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[KH * 4 * TILE > 32768 ? KH * 4 * TILE : 32768];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int half = wv >> 2, wq = wv & 3, t = tid & 255;
   const int ntn = (E + BN - 1) / BN, ntm = (T + BM - 1) / BM;
   const int n_valid = ntm * ntn;
   const int lin = blockIdx.x;
@@ -908,20 +920,23 @@ __global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restri
   const int full = n_valid - 8 * (per - 1);
   const int id = xcd < full ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
   const int m0 = (id / ntn) * BM, n0 = (id % ntn) * BN;
-  // staging: chunk q * 256 + tid of a step is row 32 q + tid / 8, 16-byte chunk
-  // tid % 8 (whole 128-byte row segments per load instruction); rows past T or
+  uint16_t* As = lds + (size_t)half * 2 * TILE;
+  uint16_t* Bs = lds + (size_t)(KH + half) * 2 * TILE;
+  // staging: chunk q * 256 + t of a step is row 32 q + t / 8, 16-byte chunk
+  // t % 8 (whole 128-byte row segments per load instruction); rows past T or
   // E load the last row and are never stored
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)T * (uint32_t)H * 2u);
   const __amdgpu_buffer_rsrc_t wrr = buffer_rsrc(wr, (uint32_t)E * (uint32_t)H * 2u);
+  const int nch = H / BK / KH;           // K steps of this half
+  const int kbase = half * nch * 128;    // byte offset of the half's K range in a row
   uint32_t xo[4], wo[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int rr = 32 * q + (tid >> 3);
-    xo[q] = ((uint32_t)min(m0 + rr, T - 1) * (uint32_t)H + (uint32_t)(tid & 7) * 8u) * 2u;
-    wo[q] = ((uint32_t)min(n0 + rr, E - 1) * (uint32_t)H + (uint32_t)(tid & 7) * 8u) * 2u;
+    const int rr = 32 * q + (t >> 3);
+    xo[q] = ((uint32_t)min(m0 + rr, T - 1) * (uint32_t)H + (uint32_t)(t & 7) * 8u) * 2u + kbase;
+    wo[q] = ((uint32_t)min(n0 + rr, E - 1) * (uint32_t)H + (uint32_t)(t & 7) * 8u) * 2u + kbase;
   }
-  const int st_off = (tid >> 3) * LDS_STRIDE + (tid & 7) * 8;
-  const int nch = H / BK;
+  const int st_off = (t >> 3) * LDS_STRIDE + (t & 7) * 8;
   struct Stage {
     u32x4 a[4], b[4];
   };
@@ -936,8 +951,8 @@ __global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restri
   auto store = [&](const Stage& S, int buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<u32x4*>(&As[buf][st_off + 32 * q * LDS_STRIDE]) = S.a[q];
-      *reinterpret_cast<u32x4*>(&Bs[buf][st_off + 32 * q * LDS_STRIDE]) = S.b[q];
+      *reinterpret_cast<u32x4*>(&As[buf * TILE + st_off + 32 * q * LDS_STRIDE]) = S.a[q];
+      *reinterpret_cast<u32x4*>(&Bs[buf * TILE + st_off + 32 * q * LDS_STRIDE]) = S.b[q];
     }
   };
   f16x_t acc[2][2];
@@ -947,27 +962,28 @@ __global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restri
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const int a0 = (wv >> 1) * 64, b0 = (wv & 1) * 64;
+  const int a0 = (wq >> 1) * 64, b0 = (wq & 1) * 64;
   const int r32 = lane & 31, kh = (lane >> 5) * 8;
-  // all 16 fragments of the step are read before the first MFMA: one LDS
-  // round trip per step instead of one per 16 K
   auto compute = [&](int buf) {
-    b8_t fa[4][2], fb[4][2];
+    const uint16_t* Ab = As + buf * TILE;
+    const uint16_t* Bb = Bs + buf * TILE;
+    b8_t fa[2][2], fb[2][2];
+    auto frags = [&](int k, int u) {
+      fa[u][0] = lds_frag_b(Ab, a0 + r32, 16 * k + kh);
+      fa[u][1] = lds_frag_b(Ab, a0 + 32 + r32, 16 * k + kh);
+      fb[u][0] = lds_frag_b(Bb, b0 + r32, 16 * k + kh);
+      fb[u][1] = lds_frag_b(Bb, b0 + 32 + r32, 16 * k + kh);
+    };
+    frags(0, 0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      fa[k][0] = lds_frag_b(As[buf], a0 + r32, 16 * k + kh);
-      fa[k][1] = lds_frag_b(As[buf], a0 + 32 + r32, 16 * k + kh);
-      fb[k][0] = lds_frag_b(Bs[buf], b0 + r32, 16 * k + kh);
-      fb[k][1] = lds_frag_b(Bs[buf], b0 + 32 + r32, 16 * k + kh);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
+      if (k + 1 < 4) frags(k + 1, (k + 1) & 1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k][i], fb[k][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k & 1][i], fb[k & 1][j], acc[i][j], 0, 0, 0);
+    }
   };
   Stage S[RDEPTH];
 #pragma unroll
@@ -992,6 +1008,27 @@ __global__ __launch_bounds__(256, 1) void k_router_mfma(const uint16_t* __restri
       compute((kc + J) & 1);
       __syncthreads();
     }
+  }
+  {
+    // every wave is past its last LDS read (the loop's last barrier): the
+    // second half's accumulators go to LDS, the first half adds them
+    float* red = reinterpret_cast<float*>(lds);   // [wq][i][j][r][lane]
+    if (half == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((((wq * 2 + i) * 2 + j) * 16) + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (half == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((((wq * 2 + i) * 2 + j) * 16) + r) * 64 + lane];
   }
   // The bias is added before any store, and the stores take no branch (an
   // element outside [T) x [E) gets an offset past the buffer's end, which the
@@ -1019,8 +1056,9 @@ hipError_t launch_router_mfma(const uint16_t* x, int T, const uint16_t* wr, cons
                               float* logits, hipStream_t s) {
   if ((uint64_t)T * H * 2 > 0x7FFFFFFFu || (uint64_t)E * H * 2 > 0x7FFFFFFFu || (uint64_t)T * E * 4 > 0x7FFFFFFFu)
     return hipErrorInvalidValue;
+  if (H % (BK * KH)) return hipErrorInvalidValue;
   const int tiles = ((T + BM - 1) / BM) * ((E + BN - 1) / BN);
-  MOE_LAUNCH(k_router_mfma, dim3(tiles), dim3(256), 0, s, x, T, wr, bias, E, H, logits);
+  MOE_LAUNCH(k_router_mfma, dim3(tiles), dim3(256 * KH), 0, s, x, T, wr, bias, E, H, logits);
   return hipGetLastError();
 }
 

@@ -119,8 +119,12 @@ def permute(ids, E, with_shared):
 # ---------------------------------------------------------------- expert FFN
 
 def silu(a):
-    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a))."""
-    return a / (1.0 + np.exp(-a))
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a)).
+
+    For a below about -709, exp(-a) overflows to inf and the quotient is -0.0,
+    the exact limit of SiLU; the overflow is expected there and not reported."""
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
 
 
 def expert_ffn(x, w_gate, w_up, w_down):

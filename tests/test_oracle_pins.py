@@ -404,6 +404,14 @@ def test_silu_closed_forms():
     assert abs(L.silu(np.array(-ln3)) + 0.25 * ln3) <= 4e-16         # sigmoid(-ln 3) = 1/4
     a = np.random.default_rng(1).standard_normal(1000) * 5
     np.testing.assert_allclose(L.silu(a), a * scipy.special.expit(a), rtol=1e-15, atol=1e-300)
+    # saturated tails: SiLU(a) -> 0 as a -> -inf and SiLU(a) = a for large a, with no
+    # warning (exp(-a) overflowing to inf is the expected route to the limit)
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("error")
+        tails = L.silu(np.array([-1e4, -800.0, 800.0, 1e4]))
+    assert tails[0] == 0.0 and tails[1] == 0.0
+    assert tails[2] == 800.0 and tails[3] == 1e4
 
 
 def test_expert_ffn_closed_form():

@@ -603,6 +603,11 @@ def _cpu_model():
     return None
 
 
+def progress(section):
+    """One line on stderr per finished section (stdout carries only the JSON line)."""
+    print(f"bench: {section} done", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -666,6 +671,7 @@ def main():
             host0 = (wl.seed, s, wr, routed, shared)
         del routed
     pool = [to_device(synth.activations(wl.seed + 5000, j, T, H)) for j in range(args.pool)]
+    progress("decode layer setup")
 
     def run(T_, steps, warm, time_kernels):
         """Headline loop (no events inside), then, if asked, a second loop with one-shot
@@ -799,19 +805,26 @@ def main():
         result["verify"] = verify
     del layers, pool
     torch.cuda.empty_cache()
+    progress("decode and verify")
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args.prefill_steps)
+        progress("prefill")
     if not args.no_stack:
         result["stack"] = bench_stack(args.stack_steps)
+        progress("stack")
     if not args.no_cache:
         result["cache"] = bench_cache(args.cache_steps)
+        progress("cache")
     if not args.no_coder:
         result["coder"] = bench_coder(args.coder_steps)
+        progress("coder")
     if not args.no_adaptive:
         result["adaptive"] = bench_adaptive()
+        progress("adaptive")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host0, T, args.cpu_seconds)
         result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]
+        progress("cpu baseline")
     print(json.dumps(result))
 
 

@@ -43,6 +43,11 @@
  *     leaves them zero again.  Calls that share a workspace must not overlap.
  *   - Results are deterministic: no floating-point atomics; every sum has a
  *     fixed order, so re-running a call gives bit-identical outputs.
+ *   - Batch size: every call that takes a token count T accepts 1 <= T <=
+ *     MOE_MAX_TOKENS, the largest prompt chunk the pages read in one pass (second
+ *     page cited above, chunked prompt reading); a longer prompt is fed as several
+ *     calls.  Outside that range the call returns MOE_EINVAL (moe_workspace_bytes
+ *     and moe_tiered_host_bytes return 0).
  *
  * Weight layouts (this library's own definition; the pages give none).
  * A matrix W has N rows (outputs) and K columns (inputs), N % 64 == 0 and
@@ -85,6 +90,9 @@ enum { MOE_FMT_NONE = -1, MOE_FMT_BF16 = 0, MOE_FMT_Q2 = 1, MOE_FMT_Q3 = 2 };
 
 /* Bytes at the start of every workspace reserved for zero-initialised counters. */
 #define MOE_WS_CONTROL_BYTES 65536
+
+/* Largest token count T of one call. */
+#define MOE_MAX_TOKENS 8192
 
 /* A bank of n_experts experts in one format (device pointers, caller-owned). */
 typedef struct moe_bank {

@@ -15,6 +15,7 @@ NOALLOC_SCRATCH_BYTES = 40 << 20
 FMT_NONE, FMT_BF16, FMT_Q2, FMT_Q3 = -1, 0, 1, 2
 FMT_BY_NAME = {"bf16": FMT_BF16, "q2": FMT_Q2, "q3": FMT_Q3}
 WS_CONTROL_BYTES = 65536
+MAX_TOKENS = 8192
 KERNEL_ROUTER, KERNEL_GATEUP_GEMV, KERNEL_DOWN_GEMV, KERNEL_GATEUP_GEMM, KERNEL_DOWN_GEMM = 0, 1, 2, 3, 4
 
 # Every function the header declares, with (restype, argtypes).

@@ -59,6 +59,9 @@ int check_layer(const moe_layer_t* L) {
 
 bool has_shared(const moe_layer_t* L) { return L->shared.fmt != MOE_FMT_NONE; }
 
+// 1 <= T <= MOE_MAX_TOKENS (one prompt chunk at most)
+bool tokens_ok(int32_t T) { return T >= 1 && T <= MOE_MAX_TOKENS; }
+
 // Workspace layout of every call for a layer shape and up to T tokens.
 struct Layout {
   size_t logits, rparts, ids, gates, margin;
@@ -312,7 +315,7 @@ bool use_gemm_path(int n_entries) { return n_entries > kSmallRouteMaxEntries; }
 extern "C" {
 
 int moe_rmsnorm_bf16(const uint16_t* x, int32_t T, int32_t H, uint16_t* out, void* stream) {
-  if (!x || !out || T <= 0 || H <= 0) return MOE_EINVAL;
+  if (!x || !out || !tokens_ok(T) || H <= 0) return MOE_EINVAL;
   return hip_rc(launch_rmsnorm_bf16(x, T, H, MOE_RMS_EPS, out, (hipStream_t)stream));
 }
 
@@ -337,7 +340,7 @@ const char* moe_strerror(int code) {
 }
 
 size_t moe_workspace_bytes(const moe_layer_t* L, int32_t T) {
-  if (check_shape(L) || T <= 0) return 0;
+  if (check_shape(L) || !tokens_ok(T)) return 0;
   if (!fmt_ok(L->routed.fmt)) return 0;
   return make_layout(L, T).total;
 }
@@ -351,7 +354,7 @@ int moe_route(const moe_layer_t* L, const uint16_t* x, int32_t T, int32_t* topk_
               float* margin, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (!L->w_router || !x || !topk_ids || !topk_gates || T <= 0) return MOE_EINVAL;
+  if (!L->w_router || !x || !topk_ids || !topk_gates || !tokens_ok(T)) return MOE_EINVAL;
   if (!fmt_ok(L->routed.fmt)) return MOE_EUNSUPPORTED;
   const Layout lay = make_layout(L, T);
   if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
@@ -361,7 +364,7 @@ int moe_route(const moe_layer_t* L, const uint16_t* x, int32_t T, int32_t* topk_
 int moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t with_shared, int32_t* offsets,
                 int32_t* sorted_rows, int32_t* row_to_sorted, void* ws, size_t ws_bytes, void* stream) {
   if (!topk_ids || !offsets || !sorted_rows || !row_to_sorted) return MOE_EINVAL;
-  if (T <= 0 || E < 1 || E > 1023 || k < 1 || k > E) return MOE_EINVAL;
+  if (!tokens_ok(T) || E < 1 || E > 1023 || k < 1 || k > E) return MOE_EINVAL;
   if ((int64_t)T * (k + 1) > (int64_t)1 << 30) return MOE_EINVAL;
   const int n = T * k + (with_shared ? T : 0);
   const int nc = permute_chunks(n);
@@ -379,7 +382,7 @@ int moe_expert_ffn_q2(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
                       const int32_t* sorted_rows, float* y_sorted, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if (!x || !offsets || !sorted_rows || !y_sorted || T <= 0) return MOE_EINVAL;
+  if (!x || !offsets || !sorted_rows || !y_sorted || !tokens_ok(T)) return MOE_EINVAL;
   const Layout lay = make_layout(L, T);
   if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
   hipStream_t s = (hipStream_t)stream;
@@ -405,7 +408,7 @@ int moe_combine(const float* y_sorted, const int32_t* row_to_sorted, const float
                 int32_t H, int32_t with_shared, const uint16_t* residual, float* out, uint16_t* out_bf16,
                 void* stream) {
   if (!y_sorted || !row_to_sorted || !topk_gates || !out) return MOE_EINVAL;
-  if (T <= 0 || k < 1 || H <= 0 || H % 4) return MOE_EINVAL;
+  if (!tokens_ok(T) || k < 1 || H <= 0 || H % 4) return MOE_EINVAL;
   return hip_rc(launch_combine(y_sorted, row_to_sorted, topk_gates, T, k, H, with_shared ? 1 : 0, residual, out,
                                out_bf16, (hipStream_t)stream));
 }
@@ -686,7 +689,7 @@ int moe_layer_forward(const moe_layer_t* L, const uint16_t* x, int32_t T, const 
                       size_t ws_bytes, void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if (!x || !out || T <= 0) return MOE_EINVAL;
+  if (!x || !out || !tokens_ok(T)) return MOE_EINVAL;
   const Layout lay = make_layout(L, T);
   if ((rc = check_ws(ws, ws_bytes, lay))) return rc;
   return layer_forward_impl(L, x, T, residual, out, out_bf16, topk_ids, topk_gates, margin, ws, lay,
@@ -729,7 +732,7 @@ int moe_layer_forward_noalloc(const moe_layer_t* L, const uint16_t* x, int32_t T
                               void* stream) {
   int rc = check_layer(L);
   if (rc) return rc;
-  if (!x || !out || T <= 0) return MOE_EINVAL;
+  if (!x || !out || !tokens_ok(T)) return MOE_EINVAL;
   const Layout lay = make_layout(L, T);
   if (lay.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ESCRATCH;
   void* ws = nullptr;
@@ -740,7 +743,7 @@ int moe_layer_forward_noalloc(const moe_layer_t* L, const uint16_t* x, int32_t T
 
 int moe_stack_forward(const moe_layer_t* layers, int32_t n_layers, const uint16_t* x0, int32_t T, uint16_t* x_out,
                       float* out_last, void* ws, size_t ws_bytes, void* stream) {
-  if (!layers || n_layers < 1 || !x0 || !x_out || T <= 0) return MOE_EINVAL;
+  if (!layers || n_layers < 1 || !x0 || !x_out || !tokens_ok(T)) return MOE_EINVAL;
   int rc;
   size_t need = 0;
   for (int l = 0; l < n_layers; ++l) {
@@ -838,7 +841,8 @@ static int cached_layer(const moe_layer_t* L, int32_t layer_idx, int32_t n_layer
                         const float** gates_out = nullptr) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (!L->w_router || !slot_of || !slot_pool || !x || !out || !miss_rows || !n_miss || T <= 0) return MOE_EINVAL;
+  if (!L->w_router || !slot_of || !slot_pool || !x || !out || !miss_rows || !n_miss || !tokens_ok(T))
+    return MOE_EINVAL;
   if (n_layers < 1 || layer_idx < 0 || layer_idx >= n_layers) return MOE_EINVAL;
   if ((rc = check_bank(*slot_pool, 1, L->hidden, L->inter))) return rc;
   if (slot_pool->fmt == MOE_FMT_BF16) return MOE_EUNSUPPORTED;
@@ -951,7 +955,7 @@ static HostStage host_stage(const moe_layer_t* L, int64_t T) {
 }
 
 size_t moe_tiered_host_bytes(const moe_layer_t* L, int32_t T) {
-  if (check_shape(L) || T <= 0) return 0;
+  if (check_shape(L) || !tokens_ok(T)) return 0;
   return host_stage(L, T).total;
 }
 
@@ -962,7 +966,7 @@ int moe_layer_forward_tiered(const moe_layer_t* L, int32_t layer_idx, int32_t n_
                              void* stream) {
   int rc = check_shape(L);
   if (rc) return rc;
-  if (!host_bank || !host_ws || T <= 0 || n_threads < 0) return MOE_EINVAL;
+  if (!host_bank || !host_ws || !tokens_ok(T) || n_threads < 0) return MOE_EINVAL;
   if ((uintptr_t)x & 3) return MOE_EINVAL;   // copied to the host as 4-byte words
   if (!slot_pool) return MOE_EINVAL;
   if ((rc = check_bank(*host_bank, L->n_experts, L->hidden, L->inter))) return rc;

@@ -275,7 +275,8 @@ int moe_cpu_isa(void) { return moe_host::cpu_isa(); }
 
 int moe_cpu_expert_ffn(const moe_bank_t* bank, const uint16_t* x, int32_t T, int32_t k, const int32_t* ids,
                        const float* gates, const int32_t* rows, int32_t n_rows, float* y, int32_t n_threads) {
-  if (!bank || !x || !ids || !gates || !y || T <= 0 || k <= 0 || n_rows < 0 || n_threads < 0) return MOE_EINVAL;
+  if (!bank || !x || !ids || !gates || !y || T <= 0 || T > MOE_MAX_TOKENS || k <= 0 || n_rows < 0 || n_threads < 0)
+    return MOE_EINVAL;
   if (n_rows > 0 && !rows) return MOE_EINVAL;
   if ((int64_t)n_rows > (int64_t)T * k) return MOE_EINVAL;
   const moe_bank_t& b = *bank;

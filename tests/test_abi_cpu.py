@@ -111,6 +111,35 @@ def test_layer_forward_rejects(lib, case, code):
     assert fwd(lib, L, **kw) == code
 
 
+def test_token_count_bound(lib):
+    # 1 <= T <= MOE_MAX_TOKENS (one prompt chunk) on every call that takes T
+    text = open(HEADER).read()
+    assert re.search(r"#define MOE_MAX_TOKENS 8192\b", text) and B.MAX_TOKENS == 8192
+    L = q2_layer()
+    over = B.MAX_TOKENS + 1
+    assert B.workspace_bytes(L, B.MAX_TOKENS) > 0 and B.workspace_bytes(L, over) == 0
+    assert fwd(lib, L, T=over) == B.MOE_EINVAL
+    assert lib.moe_route(ctypes.byref(L), FAKE, over, FAKE, FAKE, None, FAKE * 64, 1 << 40, None) == B.MOE_EINVAL
+    assert lib.moe_permute(FAKE, over, 10, 512, 1, FAKE, FAKE, FAKE, FAKE * 64, 1 << 40, None) == B.MOE_EINVAL
+    assert lib.moe_expert_ffn_q2(ctypes.byref(L), FAKE, over, FAKE, FAKE, FAKE, FAKE * 64, 1 << 40, None) \
+        == B.MOE_EINVAL
+    assert lib.moe_combine(FAKE, FAKE, FAKE, over, 10, 2560, 1, None, FAKE, None, None) == B.MOE_EINVAL
+    assert lib.moe_rmsnorm_bf16(FAKE, over, 2560, FAKE, None) == B.MOE_EINVAL
+    arr = (B.Layer * 1)(L)
+    assert lib.moe_stack_forward(arr, 1, FAKE, over, FAKE, None, FAKE * 64, 1 << 40, None) == B.MOE_EINVAL
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(L), FAKE, over, None, FAKE, None, None, None, None, None) \
+        == B.MOE_EINVAL
+    pool = q2_layer(fmt="q3").routed
+    L3 = q2_layer(fmt="q3")
+    assert lib.moe_layer_forward_cached(ctypes.byref(L3), 0, 48, FAKE, ctypes.byref(pool), FAKE, over, FAKE, None,
+                                        None, FAKE, FAKE, FAKE * 64, 1 << 40, None) == B.MOE_EINVAL
+    assert lib.moe_tiered_host_bytes(ctypes.byref(L3), over) == 0
+    assert lib.moe_layer_forward_tiered(ctypes.byref(L3), 0, 48, FAKE, ctypes.byref(pool), ctypes.byref(pool), FAKE,
+                                        over, FAKE, None, None, FAKE, FAKE, FAKE * 64, 1 << 40, FAKE * 64, 1 << 40, 0,
+                                        None) == B.MOE_EINVAL
+    assert lib.moe_cpu_expert_ffn(ctypes.byref(pool), FAKE, over, 10, FAKE, FAKE, None, 0, FAKE, 0) == B.MOE_EINVAL
+
+
 def test_other_entry_points_validate(lib):
     L = q2_layer()
     vp = ctypes.c_void_p

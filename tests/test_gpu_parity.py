@@ -181,8 +181,11 @@ def run_layer(d, x, T, residual=None):
 
 # decode T = 2 and 3 cover the batch sizes where the gate/up launch switches from
 # 32-row to 64-row blocks; T = 9 an odd batch between the MTP verify size and 16
-@pytest.mark.parametrize("workload,T", [("tiny", 4), ("decode", 1), ("decode", 2), ("decode", 3), ("decode", 4),
-                                        ("decode", 9), ("decode", 16), ("decode", 64), ("decode", 100)])
+# tiny (bf16 experts) at T = 1, 4, 64 and 300: the dense GEMV work items, with the
+# small-batch routing and with the router, permutation and combine launches
+@pytest.mark.parametrize("workload,T", [("tiny", 1), ("tiny", 4), ("tiny", 64), ("tiny", 300), ("decode", 1),
+                                        ("decode", 2), ("decode", 3), ("decode", 4), ("decode", 9), ("decode", 16),
+                                        ("decode", 64), ("decode", 100)])
 def test_layer_forward_parity(workload, T):
     hl = W.host_layer(workload)
     x, _ = W.activations_with_margin(hl, T)

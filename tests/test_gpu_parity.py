@@ -239,6 +239,30 @@ def test_coder_shape(T):
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
 
 
+# The largest shapes the ABI accepts: E = 1,023 experts (16 logits per lane in the
+# top-k, 1,024 permutation groups, a partial last router tile) and top_k = 32
+# (33 entries per token: the decode down projection and combine as two launches).
+_EXTREME = {"E1023": synth.LayerShape(512, 1023, 10, 512, True, "q2", None),
+            "k32": synth.LayerShape(512, 64, 32, 512, True, "q2", None)}
+
+
+@pytest.mark.parametrize("name,T", [("E1023", 1), ("E1023", 4), ("E1023", 64), ("E1023", 1024),
+                                    ("k32", 1), ("k32", 4), ("k32", 64)])
+def test_extreme_shapes(name, T):
+    shape = _EXTREME[name]
+    hl = W.host_layer("decode", shape=shape)
+    x, _ = W.activations_with_margin(hl, T)
+    d = W.upload(hl)
+    out, out_bf, ids, gates, margin, _ = run_layer(d, x, T)
+    ref, ids_r, gates_r, m_r = hl.oracle_forward(x)
+    assert_route_matches(ids, gates, hl.logits(x), shape.top_k, f"{name} T={T}")
+    err = OL.rel_max_err(out, ref)
+    print(f"{name} T={T}: max|err|/rms = {err:.3e}")
+    assert err <= (1e-4 if T <= 16 else OUT_TOL)
+    np.testing.assert_allclose(margin, m_r, rtol=0, atol=1e-5)
+    np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
+
+
 def degenerate_host_layer(shape):
     """Host layer of a degenerate shape; the real shape without a shared expert
     reuses the decode layer's routed experts (same seed and layer)."""

@@ -242,12 +242,17 @@ def test_coder_shape(T):
 # The largest shapes the ABI accepts: E = 1,023 experts (16 logits per lane in the
 # top-k, 1,024 permutation groups, a partial last router tile) and top_k = 32
 # (33 entries per token: the decode down projection and combine as two launches).
+# The 3-bit and bf16 banks take E = 1,023 on a smaller matrix (H = 256, I = 128).
 _EXTREME = {"E1023": synth.LayerShape(512, 1023, 10, 512, True, "q2", None),
-            "k32": synth.LayerShape(512, 64, 32, 512, True, "q2", None)}
+            "k32": synth.LayerShape(512, 64, 32, 512, True, "q2", None),
+            "E1023q3": synth.LayerShape(256, 1023, 10, 128, True, "q3", None),
+            "E1023bf16": synth.LayerShape(256, 1023, 10, 128, True, "bf16", None)}
 
 
 @pytest.mark.parametrize("name,T", [("E1023", 1), ("E1023", 4), ("E1023", 64), ("E1023", 1024),
-                                    ("k32", 1), ("k32", 4), ("k32", 64)])
+                                    ("k32", 1), ("k32", 4), ("k32", 64),
+                                    ("E1023q3", 1), ("E1023q3", 4), ("E1023q3", 64),
+                                    ("E1023bf16", 1), ("E1023bf16", 4), ("E1023bf16", 64)])
 def test_extreme_shapes(name, T):
     shape = _EXTREME[name]
     hl = W.host_layer("decode", shape=shape)
@@ -258,7 +263,10 @@ def test_extreme_shapes(name, T):
     assert_route_matches(ids, gates, hl.logits(x), shape.top_k, f"{name} T={T}")
     err = OL.rel_max_err(out, ref)
     print(f"{name} T={T}: max|err|/rms = {err:.3e}")
-    assert err <= (1e-4 if T <= 16 else OUT_TOL)
+    # the 2-bit and bf16 decode paths carry x and h to about 2^-19 of a block's largest
+    # value (1e-4 leaves a wide margin); the 3-bit decode GEMV rounds h to bf16 pairs
+    # and the GEMM paths round h to fp16, so they take the layer bar
+    assert err <= (1e-4 if T <= 16 and shape.fmt != "q3" else OUT_TOL)
     np.testing.assert_allclose(margin, m_r, rtol=0, atol=1e-5)
     np.testing.assert_array_equal(out_bf, synth.f32_to_bf16_bits(out))
 

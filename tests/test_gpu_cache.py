@@ -27,11 +27,12 @@ def pool():
     return slot_of, pool, dpool
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 17, 64])
+@pytest.mark.parametrize("T", [1, 4, 16, 17, 64, 1024])
 def test_q3_layer_forward(T):
     # a plain (uncached) 3-bit layer: all 512 experts resident (T = 1: the decode
     # down projection's one-token launch shape; T = 16: the largest decode batch;
-    # T = 17: the first batch past the decode path, on the 32-row grouped GEMM)
+    # T = 17: the first batch past the decode path, on the 32-row grouped GEMM;
+    # T = 1,024: a prompt-sized batch, which 3-bit weights also run on 32-row tiles)
     hl = W.host_layer("cache")
     x, _ = W.activations_with_margin(hl, T)
     d = W.upload(hl)
